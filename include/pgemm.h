@@ -1,0 +1,137 @@
+/*
+ * pgemm.h -- C ABI of a tiled GEMM whose K loop is software-pipelined over a
+ * ring of LDS stages, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "Double Buffering: Software Pipelining the K-Loop",
+ * section "The Kernel": row-major A, B, C and the fused alpha/beta
+ * read-modify-write of C) is
+ *
+ *     C[i*ldc + j] = alpha * sum_k A[i*lda + k] * B[k*ldb + j] + beta * C[i*ldc + j]
+ *
+ * for 0 <= i < M, 0 <= j < N.  The K loop runs as a prologue, a steady state
+ * and an epilogue over `stages` LDS buffers (page "Software pipelines and
+ * asynchronous copies", sections "Prologue, steady state, and epilogue" and
+ * "Producer-consumer synchronization"): one readiness barrier per K tile, the
+ * loads of tile t+stages-1 in flight while tile t is multiplied.
+ *
+ * Conventions shared by every entry point:
+ *   - Layout: row-major A[M][K], B[K][N], C[M][N] with lda >= K, ldb >= N,
+ *     ldc >= N (elements, not bytes).
+ *   - dtype: PGEMM_F32 (A, B, C fp32), PGEMM_F16 and PGEMM_BF16 (A, B 16-bit,
+ *     C fp32, fp32 accumulation), PGEMM_I8 (A, B int8, C int32, int32
+ *     accumulation and int32 two's-complement epilogue; alpha and beta must be
+ *     integers in int32 range).
+ *   - Pointers A, B, C are device pointers owned by the caller.  The library
+ *     allocates nothing and keeps no state besides constant tables.
+ *   - beta == 0: C is written without being read (NaN/Inf in C do not
+ *     propagate).  K == 0: C = beta*C.  M == 0 or N == 0: nothing happens.
+ *   - C must not overlap A or B.
+ *   - stream: a hipStream_t (NULL = the default stream).  The call only
+ *     enqueues work and returns; completion is observed through the stream.
+ *   - Misaligned pointers or leading dimensions are not an error: they select
+ *     the element-wise producer (slower, same results).
+ *   - Return value: PGEMM_OK (0) or a negative pgemm_status.  Argument errors
+ *     are detected on the host before anything is enqueued.
+ */
+#ifndef PGEMM_H
+#define PGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pgemm_dtype {
+    PGEMM_F32 = 0,
+    PGEMM_F16 = 1,
+    PGEMM_BF16 = 2,
+    PGEMM_I8 = 3
+};
+
+enum pgemm_status {
+    PGEMM_OK = 0,
+    PGEMM_ERR_INVALID_ARG = -1,        /* negative size, ld too small, null pointer with work to do */
+    PGEMM_ERR_UNSUPPORTED_DTYPE = -2,  /* dtype not one of pgemm_dtype */
+    PGEMM_ERR_BAD_STAGES = -3,         /* stages outside 0..4 */
+    PGEMM_ERR_INFEASIBLE_PLAN = -4,    /* no compiled variant satisfies the forced options */
+    PGEMM_ERR_NONINTEGRAL_SCALAR = -5, /* int8 with alpha or beta not an int32 integer */
+    PGEMM_ERR_HIP = -6,                /* the HIP runtime rejected the launch */
+    PGEMM_ERR_TOO_LARGE = -7           /* a dimension or byte offset exceeds the 32-bit tile addressing */
+};
+
+/* Producer of a K tile (page "Double Buffering...", section "Two Stages, One
+ * Barrier"; page "GPU-Kernel pipelinen", step 2):
+ *   DIRECT   -- buffer_load ... lds: global memory straight into the LDS stage
+ *               with no register involvement (the cp.async analogue).
+ *   REGISTER -- global memory into VGPRs at the top of the iteration, written
+ *               to the LDS stage after the iteration's MFMA work.
+ *   GENERIC  -- element-wise loads through VGPRs; used for misaligned data. */
+enum pgemm_producer {
+    PGEMM_PRODUCER_AUTO = 0,
+    PGEMM_PRODUCER_DIRECT = 1,
+    PGEMM_PRODUCER_REGISTER = 2,
+    PGEMM_PRODUCER_GENERIC = 3
+};
+
+/* Optional overrides for pgemm_gemm_ex / pgemm_plan.  Zero-initialise and set
+ * only what you want to force. */
+typedef struct pgemm_opts {
+    int producer;  /* pgemm_producer; AUTO lets the planner choose */
+    int tile_m;    /* 0 = planner's choice; else force BM (with tile_n, tile_k) */
+    int tile_n;
+    int tile_k;
+    int reserved[4];
+} pgemm_opts;
+
+/* What the planner chose (pgemm_plan output). */
+typedef struct pgemm_plan_info {
+    int tile_m, tile_n, tile_k;  /* BM, BN, BK */
+    int stages;                  /* requested ring depth after auto selection */
+    int stages_eff;              /* min(stages, max(nK, 1)): buffers actually filled */
+    int num_k_tiles;             /* nK = ceil(K / BK) */
+    int producer;                /* pgemm_producer actually used */
+    int threads;                 /* workgroup size */
+    int waves_m, waves_n;        /* wave grid inside the workgroup */
+    int lds_bytes;               /* stages * (BM*BK + BK*BN) * element size */
+    int wg_per_cu;               /* resident workgroups per CU (LDS and VGPR limit) */
+    int grid;                    /* number of workgroups launched */
+    int variant;                 /* index into the library's compiled-variant table */
+    double est_uncovered_cycles; /* latency left exposed per K tile by the stage-count model */
+} pgemm_plan_info;
+
+/* C = alpha*A*B + beta*C with the planner's choices (stages = 0: auto, 1..4:
+ * ring depth).  Asynchronous on `stream`. */
+int pgemm_gemm(int64_t M, int64_t N, int64_t K, double alpha,
+               const void* A, int64_t lda, const void* B, int64_t ldb,
+               double beta, void* C, int64_t ldc,
+               int dtype, int stages, void* stream);
+
+/* As pgemm_gemm, with producer/tile overrides (opts may be NULL). */
+int pgemm_gemm_ex(int64_t M, int64_t N, int64_t K, double alpha,
+                  const void* A, int64_t lda, const void* B, int64_t ldb,
+                  double beta, void* C, int64_t ldc,
+                  int dtype, int stages, const pgemm_opts* opts, void* stream);
+
+/* Host-only: the plan pgemm_gemm_ex would use for these sizes.  `aligned`
+ * states whether A, B, lda, ldb, K, N meet the 16-byte vector-load rules
+ * (1) or not (0).  Touches no GPU state. */
+int pgemm_plan(int64_t M, int64_t N, int64_t K, int dtype, int stages,
+               int aligned, const pgemm_opts* opts, pgemm_plan_info* out);
+
+/* Static description of a pgemm_status value. */
+const char* pgemm_strerror(int status);
+
+/* Number of compiled kernel variants and their static description
+ * (host-only; for sweeps and tests). */
+int pgemm_num_variants(void);
+int pgemm_variant_info(int index, pgemm_plan_info* out, int* dtype);
+
+/* ABI version: major*10000 + minor*100 + patch. */
+int pgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PGEMM_H */

@@ -1,0 +1,252 @@
+"""Pins of the oracle against facts that do not come from the oracle itself.
+
+The oracle (oracle/oracle.c) computes C = alpha*A@B + beta*C0, the kernel
+semantics of page "Double Buffering: Software Pipelining the K-Loop", section
+"The Kernel".  The pages print no matrix results, so the oracle is pinned by:
+
+  * exhaustive decoder checks against numpy's float16 and torch's bfloat16;
+  * exact rational brute force (fractions.Fraction) on every shape in {1..8}^3
+    with values whose products and sums are exact in double, so the oracle must
+    agree bit for bit; non-square shapes with distinct values catch swapped
+    indices and transposed operands;
+  * the error bound K * 2^-52 * sum|a*b| against the exact rational result for
+    full-mantissa random fp32 inputs;
+  * closed forms: identity B gives alpha*A + beta*C0, all-ones gives
+    alpha*K + beta*C0, int8 (-128)(-128) gives 16384*K, 1*(-1) gives -K;
+  * int8 results reduced modulo 2^32 match Python's unbounded integers;
+  * beta == 0 never reads C0 (NaN poison stays out), K == 0 gives beta*C0,
+    and padding beyond K / N (NaN-filled) is never read.
+"""
+import itertools
+import math
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from software_pipelined_tiled_loop_amd import inputs
+
+
+def bits_f16(x):
+    return np.array([x], dtype=np.float16).view(np.uint16)
+
+
+def bf16_bits_of(vals):
+    return torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def f16_bits_of(vals):
+    return np.asarray(vals, dtype=np.float16).view(np.uint16)
+
+
+def encode(dtype, vals):
+    vals = np.asarray(vals, dtype=np.float64)
+    if dtype == "f32":
+        return vals.astype(np.float32)
+    if dtype == "f16":
+        return f16_bits_of(vals).reshape(vals.shape)
+    if dtype == "bf16":
+        return bf16_bits_of(vals.reshape(-1)).reshape(vals.shape)
+    return vals.astype(np.int8)
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_f16_decoder_matches_numpy_exhaustively():
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = allbits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.decode_f16(int(b)) for b in allbits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zero and a subnormal, spelled out
+    assert math.copysign(1.0, oracle.decode_f16(0x8000)) == -1.0
+    assert oracle.decode_f16(0x0001) == 2.0 ** -24
+    assert oracle.decode_f16(0x3C00) == 1.0
+
+
+def test_bf16_decoder_matches_torch_exhaustively():
+    allbits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    ref = allbits.view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.decode_bf16(int(b) & 0xFFFF) for b in allbits.tolist()])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert oracle.decode_bf16(0x3F80) == 1.0
+    assert oracle.decode_bf16(0xC000) == -2.0
+
+
+# ---------------------------------------------------------------- brute force
+
+def exact_gemm(M, N, K, alpha, A, B, beta, C0):
+    out = [[None] * N for _ in range(M)]
+    for i in range(M):
+        for j in range(N):
+            s = Fraction(0)
+            for k in range(K):
+                s += Fraction(A[i][k]) * Fraction(B[k][j])
+            v = Fraction(alpha) * s
+            if beta != 0:
+                v += Fraction(beta) * Fraction(C0[i][j])
+            out[i][j] = v
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_bruteforce_all_small_shapes_exact(dtype):
+    rng = random.Random(1234 + hash(dtype) % 97)
+    for M, N, K in itertools.product(range(1, 9), repeat=3):
+        pad = 3
+        if dtype == "i8":
+            Av = [[rng.randint(-128, 127) for _ in range(K)] for _ in range(M)]
+            Bv = [[rng.randint(-128, 127) for _ in range(N)] for _ in range(K)]
+            C0v = [[rng.randint(-1000, 1000) for _ in range(N)] for _ in range(M)]
+            alpha, beta = rng.choice([1, 2, -3]), rng.choice([0, 1, -2])
+            A = np.full((M, K + pad), 0x7F, np.int8)
+            B = np.full((K, N + pad), 0x7F, np.int8)
+            A[:, :K] = np.array(Av, np.int8)
+            B[:, :N] = np.array(Bv, np.int8)
+            C0 = np.full((M, N + pad), 0x7F7F7F7F, np.int32)
+            C0[:, :N] = np.array(C0v, np.int32)
+            got = oracle.gemm("i8", M, N, K, alpha, A, B, beta, C0)
+            ref = exact_gemm(M, N, K, alpha, Av, Bv, beta, C0v)
+            assert all(int(got[i, j]) == int(ref[i][j]) for i in range(M) for j in range(N)), (M, N, K)
+            continue
+        # dyadic values k/8, |k| <= 32: exact in every input format; products and
+        # sums of <= 8 terms are exact in double, so the oracle must be exact.
+        Av = [[rng.randint(-32, 32) / 8 for _ in range(K)] for _ in range(M)]
+        Bv = [[rng.randint(-32, 32) / 8 for _ in range(N)] for _ in range(K)]
+        C0v = [[rng.randint(-64, 64) / 16 for _ in range(N)] for _ in range(M)]
+        alpha, beta = rng.choice([1.0, 0.5, -2.0]), rng.choice([0.0, 1.0, -0.25])
+        in_dt = np.float32 if dtype == "f32" else np.uint16
+        nan_bits = encode(dtype, [float("nan")])[0]
+        A = np.full((M, K + pad), nan_bits, in_dt)
+        B = np.full((K, N + pad), nan_bits, in_dt)
+        A[:, :K] = encode(dtype, Av)
+        B[:, :N] = encode(dtype, Bv)
+        C0 = np.full((M, N + pad), np.nan, np.float32)
+        C0[:, :N] = np.array(C0v, np.float32)
+        got = oracle.gemm(dtype, M, N, K, alpha, A, B, beta, C0)
+        ref = exact_gemm(M, N, K, alpha, Av, Bv, beta, C0v)
+        for i in range(M):
+            for j in range(N):
+                assert Fraction(float(got[i, j])) == ref[i][j], (dtype, M, N, K, i, j)
+
+
+def test_random_fp32_within_double_rounding_bound():
+    rng = np.random.default_rng(77)
+    for (M, N, K) in [(3, 5, 7), (8, 2, 64), (5, 9, 200)]:
+        A = (rng.random((M, K), dtype=np.float32) * 2 - 1).astype(np.float32)
+        B = (rng.random((K, N), dtype=np.float32) * 2 - 1).astype(np.float32)
+        got = oracle.gemm("f32", M, N, K, 1.0, A, B)
+        for i in range(M):
+            for j in range(N):
+                exact = sum(Fraction(float(A[i, k])) * Fraction(float(B[k, j])) for k in range(K))
+                mag = sum(abs(float(A[i, k]) * float(B[k, j])) for k in range(K))
+                assert abs(Fraction(float(got[i, j])) - exact) <= Fraction(K * mag) / 2 ** 52
+
+
+def test_matches_numpy_float64_matmul_library():
+    op = inputs.make_operands("f32", 97, 83, 129, seed=5, alpha=1.5, beta=-0.5)
+    A, B, C = op.numpy_views()
+    got = oracle.gemm("f32", 97, 83, 129, 1.5, A, B, -0.5, C)
+    ref = 1.5 * (A.astype(np.float64) @ B.astype(np.float64)) - 0.5 * C.astype(np.float64)
+    bound = 129 * 2.0 ** -52 * (np.abs(A.astype(np.float64)) @ np.abs(B.astype(np.float64))) * 1.5 + 1e-300
+    assert np.all(np.abs(got - ref) <= bound + 2.0 ** -52 * np.abs(ref))
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_identity_B_gives_alpha_A_plus_beta_C0(dtype):
+    M, K = 37, 48
+    op = inputs.make_operands(dtype, M, K, K, seed=11, alpha=2.0, beta=0.5, lda=K + 5, ldc=K + 2)
+    A, _, C0 = op.numpy_views()
+    eye = encode(dtype, np.eye(K))
+    got = oracle.gemm(dtype, M, K, K, 2.0, A, eye, 0.5, C0)
+    Ad = A[:, :K].astype(np.float64) if dtype == "f32" else torch.from_numpy(A[:, :K].view(np.int16)).view(
+        inputs.TORCH_IN[dtype]).to(torch.float64).numpy()
+    ref = 2.0 * Ad + 0.5 * C0[:, :K].astype(np.float64)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("K", [0, 1, 2, 3, 17, 640])
+def test_all_ones_gives_alpha_K_plus_beta_C0(dtype, K):
+    M, N = 9, 13
+    ones_a = encode(dtype, np.ones((M, max(K, 1))))
+    ones_b = encode(dtype, np.ones((max(K, 1), N)))
+    C0 = np.arange(M * N, dtype=np.float32).reshape(M, N) / 4
+    got = oracle.gemm(dtype, M, N, K, 3.0, ones_a, ones_b, -1.0, C0)
+    assert np.array_equal(got, 3.0 * K - C0.astype(np.float64))
+
+
+def test_int8_closed_forms():
+    M, N, K = 6, 7, 4096
+    a = np.full((M, K), -128, np.int8)
+    b = np.full((K, N), -128, np.int8)
+    assert np.all(oracle.gemm("i8", M, N, K, 1, a, b) == 16384 * K)
+    a = np.ones((M, K), np.int8)
+    b = np.full((K, N), -1, np.int8)
+    assert np.all(oracle.gemm("i8", M, N, K, 1, a, b) == -K)
+    C0 = np.arange(M * N, dtype=np.int32).reshape(M, N)
+    assert np.array_equal(oracle.gemm("i8", M, N, K, -2, a, b, 3, C0), 2 * K + 3 * C0)
+
+
+def test_int8_wraps_modulo_2_32_and_counts_overflow():
+    M, N, K = 2, 3, 4096
+    a = np.full((M, K), 127, np.int8)
+    b = np.full((K, N), 127, np.int8)
+    alpha = 1000
+    got = oracle.gemm("i8", M, N, K, alpha, a, b)
+    exact = alpha * 127 * 127 * K
+    wrapped = ((exact + 2 ** 31) % 2 ** 32) - 2 ** 31
+    assert np.all(got == wrapped)
+    assert oracle.gemm.last_overflow[0] == M * N  # every output left int32
+    assert oracle.gemm.last_overflow[1] == 0      # raw sums still fit
+
+
+# ---------------------------------------------------------------- edge readings
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+def test_beta_zero_does_not_read_C0(dtype):
+    op = inputs.make_operands(dtype, 5, 6, 7, seed=3, beta=0.0)
+    A, B, C = op.numpy_views()  # C is poison (NaN / 0x7F7F7F7F)
+    got = oracle.gemm(dtype, 5, 6, 7, 1.0 if dtype != "i8" else 1, A, B, 0.0 if dtype != "i8" else 0, C)
+    if dtype == "i8":
+        ref = A[:, :7].astype(np.int64) @ B[:, :6].astype(np.int64)
+        assert np.array_equal(got, ref)
+    else:
+        assert np.all(np.isfinite(got))
+
+
+def test_K_zero_gives_beta_C0():
+    C0 = np.linspace(-1, 1, 20, dtype=np.float32).reshape(4, 5)
+    A = np.zeros((4, 1), np.float32)
+    B = np.zeros((1, 5), np.float32)
+    got = oracle.gemm("f32", 4, 5, 0, 1.0, A, B, 0.5, C0)
+    assert np.array_equal(got, 0.5 * C0.astype(np.float64))
+
+
+def test_row_sampling_equals_full_rows():
+    op = inputs.make_operands("bf16", 40, 33, 70, seed=9, lda=72, ldb=40)
+    A, B, _ = op.numpy_views()
+    full = oracle.gemm("bf16", 40, 33, 70, 1.0, A, B)
+    rows = [0, 7, 39, 12]
+    part = oracle.gemm("bf16", 40, 33, 70, 1.0, A, B, rows=rows)
+    assert np.array_equal(part, full[rows])
+    op8 = inputs.make_operands("i8", 20, 17, 50, seed=9)
+    A8, B8, _ = op8.numpy_views()
+    full8 = oracle.gemm("i8", 20, 17, 50, 1, A8, B8)
+    assert np.array_equal(oracle.gemm("i8", 20, 17, 50, 1, A8, B8, rows=[3, 19]), full8[[3, 19]])
+
+
+def test_rejects_bad_arguments():
+    a = np.zeros((2, 2), np.float32)
+    with pytest.raises(ValueError):
+        oracle.gemm("f32", 3, 2, 2, 1.0, a, a)
+    with pytest.raises(ValueError):
+        oracle.gemm("i8", 2, 2, 2, 0.5, a.astype(np.int8), a.astype(np.int8))
