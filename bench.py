@@ -1,0 +1,279 @@
+"""Benchmark of the software-pipelined GEMM on one MI355X.
+
+One JSON line on stdout.  A "step" is one call of the whole hot path
+(pgemm_gemm: plan, prologue, pipelined K loop, fused alpha/beta epilogue) on
+the headline workload, fp32 SGEMM M = N = K = 4096, alpha = 1, beta = 0.5,
+with inputs resident in HBM.  W untimed warm-up steps, then K timed steps
+between HIP events on the stream the kernels are launched on.
+
+Also reported (same JSON line, key "reports"): int8 / bf16 / fp16 at 4096^3,
+the stage-count sweep (1 vs 2 vs 3-4 stages) and producer comparison, and
+the bf16 K-sweep with the ragged 4000 x 3968 x 4001 shape.  The oracle is
+timed on a bounded sample of the headline workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--quick] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6, "i8": 5033.2}  # dense TFLOP/s (TOP/s), MI355X
+HBM_PEAK_GBS = 8000.0
+PAGE_SGEMM_GFLOPS = 32107.5  # 2-stage SGEMM 4096^3 on the first page's (unnamed NVIDIA) GPU
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "software_pipelined_tiled_loop_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def make_device_operands(dtype, M, N, K, seed, alpha, beta, lda=None, ldb=None, ldc=None):
+    from software_pipelined_tiled_loop_amd import inputs
+    op = inputs.make_operands(dtype, M, N, K, seed=seed, alpha=alpha, beta=beta, lda=lda, ldb=ldb, ldc=ldc)
+    return op, op.A.cuda(), op.B.cuda(), op.C.cuda()
+
+
+def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=20, warmup=3):
+    """Average ms per call over `reps` back-to-back launches (HIP events on the launch stream)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    opts = lib._opts(producer, tile)
+
+    def call():
+        r = lib.pgemm_gemm_ex(op.M, op.N, op.K, op.alpha, A, op.lda, B, op.ldb, op.beta, C, op.ldc, op.dtype,
+                              stages, opts, stream)
+        if r != 0:
+            raise lib.PgemmError(r)
+
+    for _ in range(warmup):
+        call()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def tflops(M, N, K, ms):
+    return 2.0 * M * N * K / (ms * 1e-3) / 1e12
+
+
+def algorithmic_bytes(dtype, M, N, K, beta):
+    from software_pipelined_tiled_loop_amd import inputs
+    s = inputs.ELEM_BYTES[dtype]
+    return M * K * s + K * N * s + M * N * 4 * (2 if beta != 0 else 1)
+
+
+def plan_of(lib, dtype, M, N, K, stages=0, producer=None, tile=None, aligned=1):
+    r, p = lib.pgemm_plan(M, N, K, dtype, stages, aligned, lib._opts(producer, tile))
+    return p if r == 0 else None
+
+
+def cpu_baseline(target_s=12.0):
+    """The oracle on a bounded sample of the headline workload: the first R
+    rows of the fp32 4096^3 GEMM (R chosen for ~target_s of CPU work)."""
+    import oracle
+    from software_pipelined_tiled_loop_amd import inputs
+    M = N = K = 4096
+    op = inputs.make_operands("f32", M, N, K, seed=inputs.seed_for(1), alpha=1.0, beta=0.5)
+    A, B, C0 = op.numpy_views()
+    threads = oracle.num_threads()
+    rows = 16
+    t0 = time.perf_counter()
+    oracle.gemm("f32", rows, N, K, 1.0, A[:rows], B, 0.5, C0[:rows])
+    t = time.perf_counter() - t0
+    rows = int(min(M, max(16, rows * target_s / max(t, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.gemm("f32", rows, N, K, 1.0, A[:rows], B, 0.5, C0[:rows])
+    t = time.perf_counter() - t0
+    return {"value": round(tflops(rows, N, K, t * 1e3), 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(t, 3),
+            "sample": "first %d of 4096 rows of the fp32 4096^3 GEMM (alpha=1, beta=0.5), fp64 accumulation"
+                      % rows}
+
+
+def load_traffic(kernel_key, src_hash):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None
+    when missing or taken on another version of the kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    e = d.get(kernel_key)
+    if not e or e.get("kernel_source_hash") != src_hash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library runs each GEMM on a single MI355X and has no "
+              "multi-GPU path (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from software_pipelined_tiled_loop_amd import binding as lib
+    from software_pipelined_tiled_loop_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    src_hash = kernel_source_hash()
+
+    # ---- headline: fp32 SGEMM 4096^3, alpha=1, beta=0.5 ----
+    M = N = K = 4096
+    op, A, B, C = make_device_operands("f32", M, N, K, inputs.seed_for(1), 1.0, 0.5)
+    plan = plan_of(lib, "f32", M, N, K)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        r = lib.pgemm_gemm(M, N, K, 1.0, A, K, B, N, 0.5, C, N, "f32", 0, stream)
+        if r != 0:
+            raise lib.PgemmError(r)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    value = tflops(M, N, K, ms)
+    kernel_key = "f32_%dx%dx%d_s%d_%s" % (plan["tile_m"], plan["tile_n"], plan["tile_k"], plan["stages"],
+                                          plan["producer"])
+    traffic = load_traffic(kernel_key, src_hash)
+    roofline = {"bound": "mfma", "achieved": round(value, 3), "peak": PEAK["f32"], "unit": "TFLOP/s",
+                "frac": round(value / PEAK["f32"], 4), "traffic": traffic,
+                "kernel": kernel_key, "algorithmic_flops_per_launch": 2 * M * N * K,
+                "algorithmic_bytes_per_launch": algorithmic_bytes("f32", M, N, K, 0.5)}
+    del A, B, C
+
+    reports = {}
+    if not args.quick:
+        reports = run_reports(lib, torch)
+
+    out = {
+        "metric": "GEMM TFLOP/s (int8 TOP/s) at 4096^3 and % of MI355X dtype peak; K-sweep by stages",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": round(value * 1000.0 / PAGE_SGEMM_GFLOPS, 4),
+        "dtype": "f32", "data": "synthetic (seeded uniform[-1,1) fp32)",
+        "config": {"workload": "fp32 SGEMM M=N=K=4096 row-major alpha=1 beta=0.5", "M": M, "N": N, "K": K,
+                   "pct_of_peak": round(100.0 * value / PEAK["f32"], 2), "plan": plan,
+                   "wall_s_timed_region": round(t_wall, 4), "kernel_source_hash": src_hash},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    if reports:
+        out["reports"] = reports
+    print(json.dumps(out))
+
+
+def run_reports(lib, torch):
+    from software_pipelined_tiled_loop_amd import inputs
+    rep = {}
+    M = N = K = 4096
+
+    # int8 4096^3: producer x stages
+    op, A, B, C = make_device_operands("i8", M, N, K, inputs.seed_for(2), 1, 0)
+    d = {}
+    for prod in ("direct", "register"):
+        for s in (1, 2, 3, 4):
+            try:
+                ms = time_gemm(lib, op, A, B, C, stages=s, producer=prod, tile=(256, 256, 64))
+                d["%s_s%d" % (prod, s)] = round(tflops(M, N, K, ms), 1)
+            except Exception as e:  # variant not compiled
+                d["%s_s%d" % (prod, s)] = str(e)[:60]
+    ms = time_gemm(lib, op, A, B, C)
+    auto = tflops(M, N, K, ms)
+    rep["int8_4096"] = {"auto_TOPs": round(auto, 1), "pct_peak": round(100 * auto / PEAK["i8"], 2),
+                        "plan": plan_of(lib, "i8", M, N, K), "by_producer_stage_TOPs": d}
+    del A, B, C
+
+    for dt in ("bf16", "f16"):
+        op, A, B, C = make_device_operands(dt, M, N, K, inputs.seed_for(3, 0 if dt == "bf16" else 1), 1.0, 0.0)
+        d = {}
+        for s in (1, 2, 3, 4):
+            ms = time_gemm(lib, op, A, B, C, stages=s)
+            d["s%d" % s] = round(tflops(M, N, K, ms), 1)
+        ms = time_gemm(lib, op, A, B, C)
+        auto = tflops(M, N, K, ms)
+        rep["%s_4096" % dt] = {"auto_TFLOPs": round(auto, 1), "pct_peak": round(100 * auto / PEAK[dt], 2),
+                               "plan": plan_of(lib, dt, M, N, K), "by_stages_TFLOPs": d}
+        del A, B, C
+
+    # fp32: the pages' tile class, 1 vs 2 stages
+    op, A, B, C = make_device_operands("f32", M, N, K, inputs.seed_for(1), 1.0, 0.5)
+    d = {}
+    for s in (1, 2):
+        ms = time_gemm(lib, op, A, B, C, stages=s, tile=(128, 64, 16), reps=10)
+        d["128x64x16_s%d" % s] = round(tflops(M, N, K, ms), 2)
+    rep["f32_4096_page_tile"] = d
+    del A, B, C
+
+    # bf16 K-sweep + ragged
+    sweep = {}
+    for Ks in (32, 64, 256, 1024, 4096, 16384):
+        op, A, B, C = make_device_operands("bf16", M, N, Ks, inputs.seed_for(4, Ks % 97), 1.0, 0.0)
+        row = {}
+        for s in (1, 2, 3, 4):
+            ms = time_gemm(lib, op, A, B, C, stages=s, reps=10)
+            row["s%d" % s] = round(tflops(M, N, Ks, ms), 1)
+        ms = time_gemm(lib, op, A, B, C, reps=10)
+        row["auto"] = round(tflops(M, N, Ks, ms), 1)
+        row["auto_plan"] = "%dx%dx%d s%d" % tuple(plan_of(lib, "bf16", M, N, Ks)[k]
+                                                  for k in ("tile_m", "tile_n", "tile_k", "stages"))
+        gbs = algorithmic_bytes("bf16", M, N, Ks, 0.0) / (ms * 1e-3) / 1e9
+        roof = min(PEAK["bf16"], 2.0 * M * N * Ks / algorithmic_bytes("bf16", M, N, Ks, 0.0) * HBM_PEAK_GBS / 1e3)
+        row["auto_pct_of_roof"] = round(100 * row["auto"] / roof, 1)
+        row["auto_GBs"] = round(gbs, 0)
+        sweep["K%d" % Ks] = row
+        del A, B, C
+    r = inputs.RAGGED
+    op, A, B, C = make_device_operands("bf16", r["M"], r["N"], r["K"], inputs.seed_for(4, 9), 1.0, 0.0,
+                                       lda=r["lda"], ldb=r["ldb"], ldc=r["ldc"])
+    ms = time_gemm(lib, op, A, B, C, reps=5)
+    p = plan_of(lib, "bf16", r["M"], r["N"], r["K"], aligned=0)
+    sweep["ragged_4000x3968x4001"] = {"auto": round(tflops(r["M"], r["N"], r["K"], ms), 1),
+                                      "plan": "%dx%dx%d s%d %s" % (p["tile_m"], p["tile_n"], p["tile_k"],
+                                                                   p["stages"], p["producer"])}
+    rep["bf16_k_sweep_TFLOPs"] = sweep
+    return rep
+
+
+if __name__ == "__main__":
+    main()

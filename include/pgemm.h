@@ -127,6 +127,27 @@ const char* pgemm_strerror(int status);
 int pgemm_num_variants(void);
 int pgemm_variant_info(int index, pgemm_plan_info* out, int* dtype);
 
+/* Planner models (host-only, exposed for tests and reports).
+ *
+ * pgemm_model_uncovered_cycles: load latency left exposed per K tile with a
+ * ring of `stages` buffers when one tile's arithmetic takes compute_per_tile
+ * cycles: max(0, latency - (stages-1)*compute_per_tile), and the whole latency
+ * for a single buffer.  Page "Software pipelines and asynchronous copies",
+ * section "Worked example: Choosing between two and four stages" (two stages:
+ * max(0, 500 - 220) = 280 cycles).
+ *
+ * pgemm_model_lds_bytes: bytes of a ring of `stages` A (BM x BK) and B
+ * (BK x BN) tiles, with `a_pad_elems_per_k` extra elements per A row of K
+ * (page "Double Buffering: Software Pipelining the K-Loop", section "The
+ * Kernel": As[2][BK*A_STRIDE] and Bs[2][BK*BN]).
+ *
+ * pgemm_model_global_loads_per_output: global loads per output element of a
+ * BM x BN tile over K, K/BN + K/BM (same page, section "What The Overlap
+ * Cost": 96 at 128 x 64 and K = 4096, unchanged by pipelining). */
+double pgemm_model_uncovered_cycles(double latency, double compute_per_tile, int stages);
+int64_t pgemm_model_lds_bytes(int bm, int bn, int bk, int stages, int elem_bytes, int a_pad_elems_per_k);
+double pgemm_model_global_loads_per_output(int bm, int bn, int64_t K);
+
 /* ABI version: major*10000 + minor*100 + patch. */
 int pgemm_version(void);
 

@@ -91,6 +91,19 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
+def _runs(rows):
+    """Split a row list into runs of consecutive rows: (output offset, first row, length)."""
+    out, start = [], 0
+    rows = [int(r) for r in rows]
+    while start < len(rows):
+        end = start + 1
+        while end < len(rows) and rows[end] == rows[end - 1] + 1:
+            end += 1
+        out.append((start, rows[start], end - start))
+        start = end
+    return out
+
+
 def _check_2d(name, a, rows, min_ld, dtype):
     if a.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, a.dtype))
@@ -135,11 +148,11 @@ def gemm(dtype: str, M: int, N: int, K: int, alpha, A: np.ndarray, B: np.ndarray
             return out
         out = np.empty((len(row_sel), N), np.int32)
         tot = [0, 0]
-        for n, i in enumerate(row_sel):
+        for start, i0, n in _runs(row_sel):
             ovf = ctypes.c_int64(0)
-            r = lib.oracle_gemm_i8(1, N, K, alpha_i, _ptr(A) + int(i) * A.shape[1], A.shape[1], _ptr(B),
-                                   B.shape[1], beta_i, _ptr(c0) + (int(i) * ldc * 4 if beta_i else 0), ldc,
-                                   _ptr(out) + n * N * 4, N, ctypes.byref(ovf))
+            r = lib.oracle_gemm_i8(n, N, K, alpha_i, _ptr(A) + i0 * A.shape[1], A.shape[1], _ptr(B),
+                                   B.shape[1], beta_i, _ptr(c0) + (i0 * ldc * 4 if beta_i else 0), ldc,
+                                   _ptr(out) + start * N * 4, N, ctypes.byref(ovf))
             if r < 0:
                 raise ValueError("oracle rejected arguments")
             tot[0] += int(r)
@@ -167,11 +180,11 @@ def gemm(dtype: str, M: int, N: int, K: int, alpha, A: np.ndarray, B: np.ndarray
             raise ValueError("oracle rejected arguments")
         return out
     out = np.empty((len(row_sel), N), np.float64)
-    for n, i in enumerate(row_sel):
-        r = lib.oracle_gemm_float(kind, 1, N, K, float(alpha), _ptr(A) + int(i) * A.shape[1] * esz,
+    for start, i0, n in _runs(row_sel):
+        r = lib.oracle_gemm_float(kind, n, N, K, float(alpha), _ptr(A) + i0 * A.shape[1] * esz,
                                   A.shape[1], _ptr(B), B.shape[1], beta,
-                                  _ptr(c0) + (int(i) * ldc * 4 if beta != 0.0 else 0), ldc,
-                                  _ptr(out) + n * N * 8, N, None)
+                                  _ptr(c0) + (i0 * ldc * 4 if beta != 0.0 else 0), ldc,
+                                  _ptr(out) + start * N * 8, N, None)
         if r < 0:
             raise ValueError("oracle rejected arguments")
     return out

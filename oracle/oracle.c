@@ -32,9 +32,10 @@
  *     (and, separately via *acc_overflow, how many raw sums did not) so tests
  *     can assert that a workload never wraps.
  *
- * Loop order: rows i in parallel (OpenMP), then k, then j with one double
- * accumulator per output of the row.  For each output the sum is therefore
- * formed in increasing k, independent of the thread count.
+ * Loop order: rows i in parallel (OpenMP), then k, then j with one
+ * accumulator per output of the row (double for floats, int64 for int8).  For
+ * each output the sum is therefore formed in increasing k, independent of the
+ * thread count.
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no -march, no
  * fast-math: the arithmetic is exactly what is written).
@@ -42,6 +43,7 @@
 #include <stdint.h>
 #include <string.h>
 #include <math.h>
+#include <stdlib.h>
 
 #ifdef _OPENMP
 #include <omp.h>
@@ -139,21 +141,28 @@ int64_t oracle_gemm_i8(int64_t M, int64_t N, int64_t K, int64_t alpha,
     if (lda < K || ldb < N || ldo < N || (beta != 0 && ldc < N)) return -1;
     int64_t n_out_over = 0, n_acc_over = 0;
     int64_t i;
-#pragma omp parallel for schedule(dynamic, 1) reduction(+ : n_out_over, n_acc_over)
+    int bad_alloc = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : n_out_over, n_acc_over, bad_alloc)
     for (i = 0; i < M; ++i) {
+        /* exact integer sums: the summation order does not matter */
+        int64_t* s = (int64_t*)calloc((size_t)N, sizeof(int64_t));
+        if (!s) { bad_alloc++; continue; }
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t a = (int64_t)A[i * lda + k];
+            for (int64_t j = 0; j < N; ++j)
+                s[j] += a * (int64_t)B[k * ldb + j];
+        }
         for (int64_t j = 0; j < N; ++j) {
-            int64_t s = 0;
-            for (int64_t k = 0; k < K; ++k)
-                s += (int64_t)A[i * lda + k] * (int64_t)B[k * ldb + j];
-            if (s < INT32_MIN || s > INT32_MAX) n_acc_over++;
-            /* alpha*s and beta*C0 can exceed int64 only for absurd scalars;
-               the caller keeps |alpha|,|beta| < 2^31, so |v| < 2^31 * 2^31 * 2. */
-            int64_t v = alpha * s;
+            if (s[j] < INT32_MIN || s[j] > INT32_MAX) n_acc_over++;
+            /* alpha*s and beta*C0 fit in int64: the caller keeps |alpha|,|beta| < 2^31. */
+            int64_t v = alpha * s[j];
             if (beta != 0) v += beta * (int64_t)C0[i * ldc + j];
             if (v < INT32_MIN || v > INT32_MAX) n_out_over++;
             out[i * ldo + j] = (int32_t)(uint32_t)(uint64_t)v;
         }
+        free(s);
     }
+    if (bad_alloc) return -1;
     if (acc_overflow) *acc_overflow = n_acc_over;
     return n_out_over;
 }

@@ -1,0 +1,190 @@
+"""ctypes binding of the C ABI in include/pgemm.h (argument marshalling only).
+
+Every entry point keeps its C name and argument order.  Pointer arguments
+accept either an integer device address or a torch tensor (its data_ptr());
+``stream`` accepts an integer hipStream_t, a torch stream, or None for torch's
+current stream on the current device.  The functions return the C status code;
+``gemm`` is a convenience wrapper that raises PgemmError on a nonzero status.
+
+Importing this module loads libpgemm.so and raises ImportError when the HIP
+library has not been built: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpgemm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libpgemm.so is not built (run __graft_entry__.build() or "
+                      "python -m software_pipelined_tiled_loop_amd.build); there is no fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+PGEMM_F32, PGEMM_F16, PGEMM_BF16, PGEMM_I8 = 0, 1, 2, 3
+DTYPE_CODE = {"f32": PGEMM_F32, "f16": PGEMM_F16, "bf16": PGEMM_BF16, "i8": PGEMM_I8}
+PRODUCER = {"auto": 0, "direct": 1, "register": 2, "generic": 3}
+PRODUCER_NAME = {v: k for k, v in PRODUCER.items()}
+STATUS = {0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED_DTYPE", -3: "BAD_STAGES", -4: "INFEASIBLE_PLAN",
+          -5: "NONINTEGRAL_SCALAR", -6: "HIP", -7: "TOO_LARGE"}
+
+
+class pgemm_opts(ctypes.Structure):
+    _fields_ = [("producer", ctypes.c_int), ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int),
+                ("tile_k", ctypes.c_int), ("reserved", ctypes.c_int * 4)]
+
+
+class pgemm_plan_info(ctypes.Structure):
+    _fields_ = [("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
+                ("stages", ctypes.c_int), ("stages_eff", ctypes.c_int), ("num_k_tiles", ctypes.c_int),
+                ("producer", ctypes.c_int), ("threads", ctypes.c_int), ("waves_m", ctypes.c_int),
+                ("waves_n", ctypes.c_int), ("lds_bytes", ctypes.c_int), ("wg_per_cu", ctypes.c_int),
+                ("grid", ctypes.c_int), ("variant", ctypes.c_int), ("est_uncovered_cycles", ctypes.c_double)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["producer"] = PRODUCER_NAME.get(d["producer"], d["producer"])
+        return d
+
+
+_i64, _dbl, _vp, _int = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
+_lib.pgemm_gemm.argtypes = [_i64, _i64, _i64, _dbl, _vp, _i64, _vp, _i64, _dbl, _vp, _i64, _int, _int, _vp]
+_lib.pgemm_gemm.restype = _int
+_lib.pgemm_gemm_ex.argtypes = [_i64, _i64, _i64, _dbl, _vp, _i64, _vp, _i64, _dbl, _vp, _i64, _int, _int,
+                               ctypes.POINTER(pgemm_opts), _vp]
+_lib.pgemm_gemm_ex.restype = _int
+_lib.pgemm_plan.argtypes = [_i64, _i64, _i64, _int, _int, _int, ctypes.POINTER(pgemm_opts),
+                            ctypes.POINTER(pgemm_plan_info)]
+_lib.pgemm_plan.restype = _int
+_lib.pgemm_strerror.argtypes = [_int]
+_lib.pgemm_strerror.restype = ctypes.c_char_p
+_lib.pgemm_num_variants.argtypes = []
+_lib.pgemm_num_variants.restype = _int
+_lib.pgemm_variant_info.argtypes = [_int, ctypes.POINTER(pgemm_plan_info), ctypes.POINTER(_int)]
+_lib.pgemm_variant_info.restype = _int
+_lib.pgemm_version.restype = _int
+_lib.pgemm_model_uncovered_cycles.argtypes = [_dbl, _dbl, _int]
+_lib.pgemm_model_uncovered_cycles.restype = _dbl
+_lib.pgemm_model_lds_bytes.argtypes = [_int, _int, _int, _int, _int, _int]
+_lib.pgemm_model_lds_bytes.restype = _i64
+_lib.pgemm_model_global_loads_per_output.argtypes = [_int, _int, _i64]
+_lib.pgemm_model_global_loads_per_output.restype = _dbl
+
+EXPORTED = ("pgemm_gemm", "pgemm_gemm_ex", "pgemm_plan", "pgemm_strerror", "pgemm_num_variants",
+            "pgemm_variant_info", "pgemm_version", "pgemm_model_uncovered_cycles", "pgemm_model_lds_bytes",
+            "pgemm_model_global_loads_per_output")
+
+
+class PgemmError(RuntimeError):
+    def __init__(self, status):
+        super().__init__("pgemm status %d (%s): %s" % (status, STATUS.get(status, "?"), pgemm_strerror(status)))
+        self.status = status
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _opts(producer=None, tile=None):
+    if producer is None and tile is None:
+        return None
+    o = pgemm_opts()
+    o.producer = PRODUCER[producer] if isinstance(producer, str) else int(producer or 0)
+    if tile is not None:
+        o.tile_m, o.tile_n, o.tile_k = (int(v) for v in tile)
+    return o
+
+
+def pgemm_gemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stages, stream=None):
+    return _lib.pgemm_gemm(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc,
+                           DTYPE_CODE.get(dtype, dtype), stages, _stream(stream))
+
+
+def pgemm_gemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stages, opts=None, stream=None):
+    if isinstance(opts, dict):
+        opts = _opts(opts.get("producer"), opts.get("tile"))
+    p = ctypes.byref(opts) if opts is not None else None
+    return _lib.pgemm_gemm_ex(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc,
+                              DTYPE_CODE.get(dtype, dtype), stages, p, _stream(stream))
+
+
+def pgemm_plan(M, N, K, dtype, stages=0, aligned=1, opts=None):
+    """Returns (status, plan dict or None)."""
+    if isinstance(opts, dict):
+        opts = _opts(opts.get("producer"), opts.get("tile"))
+    info = pgemm_plan_info()
+    r = _lib.pgemm_plan(M, N, K, DTYPE_CODE.get(dtype, dtype), stages, int(aligned),
+                        ctypes.byref(opts) if opts is not None else None, ctypes.byref(info))
+    return r, (info.as_dict() if r == 0 else None)
+
+
+def pgemm_strerror(status):
+    return _lib.pgemm_strerror(int(status)).decode()
+
+
+def pgemm_num_variants():
+    return _lib.pgemm_num_variants()
+
+
+def pgemm_variant_info(index):
+    info = pgemm_plan_info()
+    dt = _int(0)
+    r = _lib.pgemm_variant_info(index, ctypes.byref(info), ctypes.byref(dt))
+    if r != 0:
+        raise PgemmError(r)
+    d = info.as_dict()
+    d["dtype"] = {v: k for k, v in DTYPE_CODE.items()}[dt.value]
+    return d
+
+
+def pgemm_version():
+    return _lib.pgemm_version()
+
+
+def pgemm_model_uncovered_cycles(latency, compute, stages):
+    return _lib.pgemm_model_uncovered_cycles(float(latency), float(compute), int(stages))
+
+
+def pgemm_model_lds_bytes(bm, bn, bk, stages, elem_bytes, a_pad=0):
+    return _lib.pgemm_model_lds_bytes(bm, bn, bk, stages, elem_bytes, a_pad)
+
+
+def pgemm_model_global_loads_per_output(bm, bn, K):
+    return _lib.pgemm_model_global_loads_per_output(bm, bn, K)
+
+
+def gemm(A, B, C, alpha=1.0, beta=0.0, stages=0, producer=None, tile=None, M=None, N=None, K=None,
+         stream=None):
+    """C = alpha*A@B + beta*C on torch tensors (2-D, row-major, unit column stride).
+
+    dtype is taken from A: float32 -> f32, float16 -> f16, bfloat16 -> bf16, int8 -> i8.
+    Sizes default to the logical shapes; leading dimensions are the row strides.
+    """
+    import torch
+    dt = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8"}[A.dtype]
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise ValueError("%s must be a 2-D row-major tensor with unit column stride" % name)
+    M = A.shape[0] if M is None else M
+    K = A.shape[1] if K is None else K
+    N = B.shape[1] if N is None else N
+    r = pgemm_gemm_ex(M, N, K, alpha, A, max(A.stride(0), 1), B, max(B.stride(0), 1), beta, C,
+                      max(C.stride(0), 1), dt, stages, _opts(producer, tile), stream)
+    if r != 0:
+        raise PgemmError(r)
+    return C

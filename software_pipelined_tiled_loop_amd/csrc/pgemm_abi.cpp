@@ -1,0 +1,345 @@
+// pgemm_abi.cpp -- the C ABI: argument validation, the planner and the launch.
+//
+// The planner picks (tile, stages, producer) for a problem:
+//   * producer: DIRECT whenever the 16-byte vector rules hold, GENERIC
+//     otherwise (REGISTER only on request);
+//   * tile: the compiled tile class with the smallest estimated time, counting
+//     how many rounds of workgroups the problem needs on 256 CUs;
+//   * stages: the smallest ring depth whose lookahead covers the load latency,
+//     using the uncovered-latency estimate max(0, L - (S-1)*C) of page
+//     "Software pipelines and asynchronous copies" (section "Worked example:
+//     Choosing between two and four stages"), with C the MFMA time of one K
+//     tile on a SIMD.  The depth is clipped to the number of K tiles (section
+//     "Prologue, steady state, and epilogue": fewer K tiles than stages).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/pgemm.h"
+#include "variants.hpp"
+
+using namespace pgemm;
+
+namespace {
+
+constexpr int kNumCU = 256;
+constexpr int kLdsPerCU = 163840;
+constexpr double kLoadLatencyCycles = 2400.0;  // assumed HBM/MALL latency under load (~1 us at 2.4 GHz)
+
+struct Table {
+    const VariantDesc* v;
+    int n;
+};
+
+Table table_for(int dtype) {
+    Table t{nullptr, 0};
+    switch (dtype) {
+        case PGEMM_F32: t.v = variants_f32(&t.n); break;
+        case PGEMM_F16: t.v = variants_f16(&t.n); break;
+        case PGEMM_BF16: t.v = variants_bf16(&t.n); break;
+        case PGEMM_I8: t.v = variants_i8(&t.n); break;
+        default: break;
+    }
+    return t;
+}
+
+int elem_bytes(int dtype) { return dtype == PGEMM_F32 ? 4 : dtype == PGEMM_I8 ? 1 : 2; }
+
+// Dense MFMA rate per SIMD per clock for the dtype (MI355X: 256 CUs x 4 SIMDs at 2.4 GHz).
+double flops_per_simd_clk(int dtype) {
+    switch (dtype) {
+        case PGEMM_F32: return 64.0;
+        case PGEMM_I8: return 2048.0;
+        default: return 1024.0;
+    }
+}
+
+// Register estimate of a variant (accumulators + two fragment sets + staging
+// + addressing) -> waves per SIMD.  Used only to estimate residency.
+int est_vgprs(const VariantDesc& d) {
+    const int nw = d.wgm * d.wgn;
+    const int wm = d.bm / d.wgm, wn = d.bn / d.wgn;
+    const int fm = wm / 16, fn = wn / 16;
+    const int es = elem_bytes(d.dtype);
+    const int acc = fm * fn * 4;
+    const int frags = 2 * (fm + fn) * 4;
+    const int staging = d.producer == PROD_DIRECT ? 0 : (d.bm * d.bk + d.bk * d.bn) * es / (64 * nw) / 4;
+    return acc + frags + staging + 40;
+}
+
+int wg_per_cu(const VariantDesc& d) {
+    const int nw = d.wgm * d.wgn;
+    int v = est_vgprs(d);
+    v = (v + 7) / 8 * 8;
+    int waves_per_simd = 512 / (v < 512 ? v : 512);
+    if (waves_per_simd > 8) waves_per_simd = 8;
+    int by_regs = waves_per_simd * 4 / nw;
+    int by_lds = kLdsPerCU / d.lds_bytes;
+    int r = by_regs < by_lds ? by_regs : by_lds;
+    return r < 1 ? 1 : r;
+}
+
+// MFMA cycles of one K tile on one SIMD, with `share` workgroups per CU.
+double tile_compute_cycles(const VariantDesc& d, int share) {
+    const double flops = 2.0 * d.bm * d.bn * d.bk;
+    return flops / (4.0 * flops_per_simd_clk(d.dtype)) * share;
+}
+
+// Relative efficiency of a tile class (operand traffic per flop: larger
+// tiles need less L2->LDS and LDS->VGPR bandwidth per MFMA).
+double tile_efficiency(const VariantDesc& d) {
+    const double per = (double)(d.bm + d.bn) / (2.0 * d.bm * d.bn);  // bytes/flop per element byte
+    const double ref = 512.0 / (2.0 * 256 * 256);
+    double e = ref / per;
+    return e > 1.0 ? 1.0 : std::pow(e, 0.5);
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool producer_matches(const VariantDesc& d, int want) { return d.producer == want; }
+
+struct Choice {
+    int index = -1;
+    int stages_req = 0;
+    double uncovered = 0.0;
+};
+
+int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligned, const pgemm_opts* opts,
+              Choice& out) {
+    Table t = table_for(dtype);
+    if (!t.v) return PGEMM_ERR_UNSUPPORTED_DTYPE;
+    if (stages < 0 || stages > 4) return PGEMM_ERR_BAD_STAGES;
+    int want_prod = aligned ? PROD_DIRECT : PROD_GENERIC;
+    if (opts && opts->producer != PGEMM_PRODUCER_AUTO) {
+        if (opts->producer < PGEMM_PRODUCER_DIRECT || opts->producer > PGEMM_PRODUCER_GENERIC)
+            return PGEMM_ERR_INVALID_ARG;
+        if (!aligned && opts->producer != PGEMM_PRODUCER_GENERIC) return PGEMM_ERR_INFEASIBLE_PLAN;
+        want_prod = opts->producer;
+    }
+    const bool force_tile = opts && (opts->tile_m || opts->tile_n || opts->tile_k);
+
+    // 1. tile class: best estimated time among variants with the producer.
+    double best_time = 0.0;
+    int best = -1;
+    for (int i = 0; i < t.n; ++i) {
+        const VariantDesc& d = t.v[i];
+        if (!producer_matches(d, want_prod)) continue;
+        if (force_tile && (d.bm != opts->tile_m || d.bn != opts->tile_n || d.bk != opts->tile_k)) continue;
+        if (stages != 0) {
+            // the tile class must offer the requested depth
+            bool has = false;
+            for (int j = 0; j < t.n; ++j)
+                if (t.v[j].dtype == d.dtype && t.v[j].bm == d.bm && t.v[j].bn == d.bn && t.v[j].bk == d.bk &&
+                    t.v[j].wgm == d.wgm && t.v[j].wgn == d.wgn && producer_matches(t.v[j], want_prod) &&
+                    t.v[j].stages == stages)
+                    has = true;
+            if (!has) continue;
+        }
+        const int occ = wg_per_cu(d);
+        const int64_t tiles = ceil_div(M, d.bm) * ceil_div(N, d.bn);
+        const int64_t rounds = ceil_div(tiles, (int64_t)kNumCU * occ);
+        const double work = (double)d.bm * d.bn * (double)(ceil_div(K, d.bk) * d.bk + d.bk);
+        const double time = (double)rounds * occ * work / tile_efficiency(d);
+        if (best < 0 || time < best_time * 0.999) {
+            best = i;
+            best_time = time;
+        }
+    }
+    if (best < 0) return PGEMM_ERR_INFEASIBLE_PLAN;
+    const VariantDesc& bt = t.v[best];
+    const int nK = (int)ceil_div(K, bt.bk);
+
+    // 2. ring depth.
+    const int occ = wg_per_cu(bt);
+    const double C = tile_compute_cycles(bt, occ);
+    int S = stages;
+    if (S == 0) {
+        S = 4;
+        for (int s = 2; s <= 4; ++s) {
+            if (pgemm_model_uncovered_cycles(kLoadLatencyCycles, C, s) <= 0.0) {
+                S = s;
+                break;
+            }
+        }
+        if (S > nK) S = nK < 1 ? 1 : nK;  // no more stages than K tiles
+    }
+    // 3. pick the variant of this tile class with depth S (or the deepest below it).
+    int pick = -1;
+    for (int s = S; s >= 1 && pick < 0; --s) {
+        for (int i = 0; i < t.n; ++i) {
+            const VariantDesc& d = t.v[i];
+            if (d.bm == bt.bm && d.bn == bt.bn && d.bk == bt.bk && d.wgm == bt.wgm && d.wgn == bt.wgn &&
+                producer_matches(d, want_prod) && d.stages == s) {
+                pick = i;
+                break;
+            }
+        }
+        if (stages != 0) break;  // an explicit depth is not downgraded
+    }
+    if (pick < 0) return PGEMM_ERR_INFEASIBLE_PLAN;
+    out.index = pick;
+    out.stages_req = t.v[pick].stages;
+    out.uncovered = pgemm_model_uncovered_cycles(kLoadLatencyCycles, C, t.v[pick].stages);
+    return PGEMM_OK;
+}
+
+void fill_info(int dtype, const VariantDesc& d, int idx, int64_t M, int64_t N, int64_t K, double uncovered,
+               pgemm_plan_info* info) {
+    std::memset(info, 0, sizeof(*info));
+    info->tile_m = d.bm;
+    info->tile_n = d.bn;
+    info->tile_k = d.bk;
+    info->stages = d.stages;
+    info->num_k_tiles = (int)ceil_div(K, d.bk);
+    const int nk1 = info->num_k_tiles < 1 ? 1 : info->num_k_tiles;
+    info->stages_eff = d.stages < nk1 ? d.stages : nk1;
+    info->producer = d.producer;
+    info->threads = d.threads;
+    info->waves_m = d.wgm;
+    info->waves_n = d.wgn;
+    info->lds_bytes = d.lds_bytes;
+    info->wg_per_cu = wg_per_cu(d);
+    info->grid = (int)(ceil_div(M, d.bm) * ceil_div(N, d.bn));
+    int base = 0;  // global index: variants of lower dtypes come first
+    for (int t = 0; t < dtype; ++t) base += table_for(t).n;
+    info->variant = base + idx;
+    info->est_uncovered_cycles = uncovered;
+}
+
+bool is_aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+double pgemm_model_uncovered_cycles(double latency, double compute_per_tile, int stages) {
+    if (stages <= 1) return latency;
+    const double u = latency - (stages - 1) * compute_per_tile;
+    return u > 0.0 ? u : 0.0;
+}
+
+int64_t pgemm_model_lds_bytes(int bm, int bn, int bk, int stages, int elem_bytes, int a_pad_elems_per_k) {
+    // stages * (A tile + B tile) elements, plus any padding of the A rows
+    return (int64_t)stages * ((int64_t)bm * bk + (int64_t)bk * bn + (int64_t)bk * a_pad_elems_per_k) * elem_bytes;
+}
+
+double pgemm_model_global_loads_per_output(int bm, int bn, int64_t K) {
+    // A workgroup loads BM*K elements of A and K*BN of B for BM*BN outputs:
+    // K/BN + K/BM global loads per output element.
+    return (double)K / bn + (double)K / bm;
+}
+
+const char* pgemm_strerror(int status) {
+    switch (status) {
+        case PGEMM_OK: return "ok";
+        case PGEMM_ERR_INVALID_ARG: return "invalid argument (size, leading dimension or null pointer)";
+        case PGEMM_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+        case PGEMM_ERR_BAD_STAGES: return "stages must be 0 (auto) or 1..4";
+        case PGEMM_ERR_INFEASIBLE_PLAN: return "no compiled variant satisfies the requested options";
+        case PGEMM_ERR_NONINTEGRAL_SCALAR: return "int8 GEMM needs integer alpha and beta in int32 range";
+        case PGEMM_ERR_HIP: return "HIP runtime error at launch";
+        case PGEMM_ERR_TOO_LARGE: return "problem exceeds 32-bit tile addressing";
+        default: return "unknown status";
+    }
+}
+
+int pgemm_version(void) { return 10000; }
+
+int pgemm_num_variants(void) {
+    int n = 0;
+    for (int d = 0; d < 4; ++d) n += table_for(d).n;
+    return n;
+}
+
+int pgemm_variant_info(int index, pgemm_plan_info* out, int* dtype) {
+    if (!out || index < 0) return PGEMM_ERR_INVALID_ARG;
+    for (int d = 0; d < 4; ++d) {
+        Table t = table_for(d);
+        if (index < t.n) {
+            fill_info(d, t.v[index], index, t.v[index].bm, t.v[index].bn, t.v[index].bk, 0.0, out);
+            if (dtype) *dtype = d;
+            return PGEMM_OK;
+        }
+        index -= t.n;
+    }
+    return PGEMM_ERR_INVALID_ARG;
+}
+
+int pgemm_plan(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligned, const pgemm_opts* opts,
+               pgemm_plan_info* out) {
+    if (!out) return PGEMM_ERR_INVALID_ARG;
+    if (dtype < 0 || dtype > 3) return PGEMM_ERR_UNSUPPORTED_DTYPE;
+    if (M < 0 || N < 0 || K < 0) return PGEMM_ERR_INVALID_ARG;
+    Choice c;
+    int r = plan_impl(M, N, K, dtype, stages, aligned, opts, c);
+    if (r != PGEMM_OK) return r;
+    Table t = table_for(dtype);
+    fill_info(dtype, t.v[c.index], c.index, M, N, K, c.uncovered, out);
+    return PGEMM_OK;
+}
+
+int pgemm_gemm_ex(int64_t M, int64_t N, int64_t K, double alpha, const void* A, int64_t lda, const void* B,
+                  int64_t ldb, double beta, void* C, int64_t ldc, int dtype, int stages, const pgemm_opts* opts,
+                  void* stream) {
+    // ---- argument checks: all before anything touches the GPU ----
+    if (dtype < 0 || dtype > 3) return PGEMM_ERR_UNSUPPORTED_DTYPE;
+    if (stages < 0 || stages > 4) return PGEMM_ERR_BAD_STAGES;
+    if (M < 0 || N < 0 || K < 0) return PGEMM_ERR_INVALID_ARG;
+    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1)) return PGEMM_ERR_INVALID_ARG;
+    if (dtype == PGEMM_I8) {
+        if (!(std::isfinite(alpha) && std::isfinite(beta)) || alpha != std::floor(alpha) ||
+            beta != std::floor(beta) || std::fabs(alpha) > 2147483647.0 || std::fabs(beta) > 2147483647.0)
+            return PGEMM_ERR_NONINTEGRAL_SCALAR;
+    }
+    if (M == 0 || N == 0) return PGEMM_OK;
+    if (!C) return PGEMM_ERR_INVALID_ARG;
+    if (K > 0 && (!A || !B)) return PGEMM_ERR_INVALID_ARG;
+    const int es = elem_bytes(dtype);
+    const int epc = 16 / es;
+    // 32-bit tile addressing: byte offsets inside one tile must stay below 2^31.
+    if (M > 0x7fffffff || N > 0x7fffffff || K > 0x7fffffff) return PGEMM_ERR_TOO_LARGE;
+    if ((double)lda * es * 256.0 >= 2147483648.0 || (double)ldb * es * 128.0 >= 2147483648.0)
+        return PGEMM_ERR_TOO_LARGE;
+    if (ceil_div(M, 128) * ceil_div(N, 64) > 0x7fffffff) return PGEMM_ERR_TOO_LARGE;
+    // Element alignment is required; 16-byte alignment selects the vector producers.
+    if (((uintptr_t)A % es) || ((uintptr_t)B % es) || ((uintptr_t)C % 4)) return PGEMM_ERR_INVALID_ARG;
+    const int aligned = K == 0 || (is_aligned16(A) && is_aligned16(B) && (lda * es) % 16 == 0 &&
+                                   (ldb * es) % 16 == 0 && K % epc == 0 && N % epc == 0);
+
+    Choice c;
+    int r = plan_impl(M, N, K, dtype, stages, aligned, opts, c);
+    if (r != PGEMM_OK) return r;
+    const VariantDesc& d = table_for(dtype).v[c.index];
+
+    KernelArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.tiles_m = (int)ceil_div(M, d.bm);
+    a.tiles_n = (int)ceil_div(N, d.bn);
+    a.group_m = 4;
+    a.alpha = (float)alpha;
+    a.beta = (float)beta;
+    a.ialpha = dtype == PGEMM_I8 ? (int)(int64_t)alpha : 0;
+    a.ibeta = dtype == PGEMM_I8 ? (int)(int64_t)beta : 0;
+    a.beta_nonzero = beta != 0.0;
+    const int grid = a.tiles_m * a.tiles_n;
+    hipError_t e = d.launch(a, grid, (hipStream_t)stream);
+    return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_HIP;
+}
+
+int pgemm_gemm(int64_t M, int64_t N, int64_t K, double alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+               double beta, void* C, int64_t ldc, int dtype, int stages, void* stream) {
+    return pgemm_gemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stages, nullptr, stream);
+}
+
+}  // extern "C"

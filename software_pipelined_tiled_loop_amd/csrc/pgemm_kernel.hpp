@@ -1,0 +1,681 @@
+// pgemm_kernel.hpp -- the software-pipelined tiled GEMM kernel for gfx950.
+//
+// One workgroup computes a BM x BN tile of C = alpha*A*B + beta*C.  Its K loop
+// runs over a ring of S LDS stages, following the prologue / steady state /
+// epilogue structure of page "Software pipelines and asynchronous copies"
+// (section "Prologue, steady state, and epilogue") and the one-barrier
+// double-buffered loop of page "Double Buffering: Software Pipelining the
+// K-Loop" (section "Two Stages, One Barrier"), generalised to S stages:
+//
+//   prologue      issue tiles 0 .. S-2 into stages 0 .. S-2 (never past nK)
+//   iteration t   s_waitcnt: tile t has landed (loads of later tiles may
+//                 still be in flight: vmcnt = loads-per-stage * their count)
+//                 s_barrier: ready edge of stage t%S for every wave, and the
+//                 reuse edge of stage (t-1)%S (every wave finished reading it)
+//                 issue tile t+S-1 into stage (t-1)%S           [if < nK]
+//                 MFMA work on stage t%S
+//   drain         the last S-1 iterations issue nothing; the wait counts
+//                 shrink so only tiles that were issued are waited for.
+//
+// S == 1 is the single-buffer loop (load, wait, barrier, compute, barrier) of
+// the first page's section on kernel 10; with the REGISTER producer it is the
+// single-LDS-buffer register-prefetch variant of page "GPU-Kernel pipelinen",
+// step 1 (two barriers per tile, the loads of tile t+1 in flight during the
+// arithmetic on tile t).
+//
+// Producers (page "Double Buffering...", section "Two Stages, One Barrier";
+// page "GPU-Kernel pipelinen", step 2):
+//   DIRECT    buffer_load_dwordx4 ... lds: global memory straight into the LDS
+//             stage without registers; completion observed with vmcnt.
+//   REGISTER  buffer_load_dwordx4 into VGPRs at the top of the iteration,
+//             ds_write_b128 into the stage after the MFMA work.
+//   GENERIC   element-wise buffer loads (any alignment), then as REGISTER.
+// All three write byte-identical LDS images, so the arithmetic, and hence the
+// result, does not depend on the producer or on S.
+//
+// LDS layout (per stage): A tile as BM rows of BK elements (K contiguous),
+// B tile as BK rows of BN elements (N contiguous) -- both straight copies of
+// global memory, so both can use the direct producer.  16-byte chunks are
+// XOR-swizzled within each row against bank conflicts; the direct producer
+// realises the swizzle by choosing which global chunk each lane fetches (an
+// LDS-DMA instruction writes 1 KiB contiguously, lane l at byte 16*l).
+// MFMA operands: A fragments with ds_read_b128; B fragments with the gfx950
+// transposing reads ds_read_b64_tr_b16 (fp16/bf16) and ds_read_b64_tr_b8
+// (int8), which deliver K-contiguous fragments from the N-contiguous rows;
+// fp32 B fragments with ds_read_b32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pgemm {
+
+enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3 };
+enum Producer : int { PROD_DIRECT = 1, PROD_REGISTER = 2, PROD_GENERIC = 3 };
+
+struct KernelArgs {
+    const void* A;
+    const void* B;
+    void* C;
+    int64_t lda, ldb, ldc;  // elements
+    int M, N, K;
+    int tiles_m, tiles_n;
+    int group_m;            // tile-rows per raster group
+    float alpha, beta;      // float dtypes
+    int ialpha, ibeta;      // int8
+    int beta_nonzero;
+};
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+
+#define PGEMM_LDS __attribute__((address_space(3)))
+
+template <int D> struct Traits;
+template <> struct Traits<DT_F32> {
+    static constexpr int ES = 4;       // element bytes
+    static constexpr int EPC = 4;      // elements per 16-byte chunk
+    static constexpr int KSTEP = 16;   // K covered when each lane reads one A chunk
+    typedef f32x4 Acc;
+};
+template <> struct Traits<DT_F16> {
+    static constexpr int ES = 2, EPC = 8, KSTEP = 32;
+    typedef f32x4 Acc;
+};
+template <> struct Traits<DT_BF16> {
+    static constexpr int ES = 2, EPC = 8, KSTEP = 32;
+    typedef f32x4 Acc;
+};
+template <> struct Traits<DT_I8> {
+    static constexpr int ES = 1, EPC = 16, KSTEP = 64;
+    typedef i32x4 Acc;
+};
+
+// Buffer resource covering [base, base + 2^31): the kernel decides validity
+// itself and sends invalid lanes to offset 2^31, which the hardware range
+// check turns into zeros (no memory access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x80000000, 0x00020000);
+}
+// The same descriptor as four scalar dwords, for the inline-asm LDS-DMA load.
+__device__ __forceinline__ i32x4 make_rsrc_sgpr(const void* base) {
+    const uint64_t p = (uint64_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xffffu));  // stride 0
+    r[2] = (int)0x80000000u;                                                          // num_records
+    r[3] = 0x00020000;                                                                // 32-bit data format
+    return r;
+}
+static constexpr uint32_t OOB = 0x80000000u;
+
+// LDS-DMA: 16 bytes from buffer offset `voff` of lane l land at LDS byte
+// `lds_base + 16*l` (lds_base is wave-uniform and goes through M0).  The
+// load is issued from inline asm so that the compiler does not treat it as a
+// pending LDS write: it would otherwise wait for every outstanding LDS-DMA
+// (vmcnt(0)) before each later LDS read and serialise the pipeline.  The
+// kernel owns vmcnt for these loads and waits for them explicitly.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t lds_base) {
+    // s_nop: one wait state between an SALU write of M0 and an LDS-DMA load.
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds_base)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most VM vector-memory loads of this wave are outstanding and
+// all its LDS operations are done, then the workgroup barrier.  One asm
+// statement, so neither the compiler's scheduler nor its memory model moves
+// anything across it or adds a vmcnt(0).
+// The leading builtin lgkmcnt(0) is there for the compiler's own bookkeeping:
+// it then knows every earlier LDS read has completed and does not hold back
+// the next MFMAs on reads issued after the barrier.
+__device__ __forceinline__ void lgkm_drain() {
+    __builtin_amdgcn_s_waitcnt((15 & 15) | (7 << 4) | (0 << 8) | (3 << 14));  // vmcnt(63) expcnt(7) lgkmcnt(0)
+}
+template <int VM>
+__device__ __forceinline__ void wait_barrier() {
+    static_assert(VM >= 0 && VM <= 63, "vmcnt is 6 bits");
+    lgkm_drain();
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(VM) : "memory");
+}
+__device__ __forceinline__ void lgkm_barrier() {
+    lgkm_drain();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+// ---- LDS swizzles --------------------------------------------------------
+// A: rows of KC 16-byte chunks.  Chunk index L = row*KC + kc is placed in
+// 128-byte line L/8 at slot (L%8) ^ p(line), p(line) = (line%8) ^ ((line/8)%2):
+// 8 consecutive rows (and 16 rows for 256-byte LDS cycles) read by one
+// ds_read_b128 land on distinct banks.
+template <int KC>
+__device__ __forceinline__ constexpr int a_off(int row, int kc) {
+    const int L = row * KC + kc;
+    const int line = L >> 3;
+    const int p = (line & 7) ^ ((line >> 3) & 1);
+    return (line << 7) + ((((L & 7) ^ p)) << 4);
+}
+// B: rows k of NCH chunks; chunk c of row k sits at c ^ pb(k).  pb spreads the
+// rows that one transposing read touches over distinct banks.
+template <int D, int NCH>
+__device__ __forceinline__ constexpr int b_swz(int k) {
+    if constexpr (D == DT_I8) {
+        return ((k & 7) + (((k >> 4) & 1) << 3)) & (NCH - 1);
+    } else if constexpr (D == DT_F32) {
+        return (((k >> 2) & 3) << 2) & (NCH - 1);
+    } else {
+        return (((k & 3) << 1) + (((k >> 3) & 1) << 3)) & (NCH - 1);
+    }
+}
+
+template <int D, int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_, int P_>
+struct Cfg {
+    static constexpr int Dt = D, BM = BM_, BN = BN_, BK = BK_, S = S_, WGM = WGM_, WGN = WGN_, P = P_;
+    typedef Traits<D> T;
+    static constexpr int ES = T::ES, EPC = T::EPC, KSTEP = T::KSTEP;
+    static constexpr int NW = WGM * WGN;
+    static constexpr int NT = 64 * NW;
+    static constexpr int WM = BM / WGM, WN = BN / WGN;
+    static constexpr int FM = WM / 16, FN = WN / 16;
+    static constexpr int KC = BK * ES / 16;           // chunks per A row
+    static constexpr int NCH = BN * ES / 16;          // chunks per B row
+    static constexpr int A_BYTES = BM * BK * ES;
+    static constexpr int B_BYTES = BK * BN * ES;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = S * STAGE_BYTES;
+    static constexpr int A_INSTR = A_BYTES / 1024 / NW;   // 1-KiB chunk blocks per wave per stage
+    static constexpr int B_INSTR = B_BYTES / 1024 / NW;
+    static constexpr int LPS = A_INSTR + B_INSTR;         // vector loads per thread per stage
+    static constexpr int B_ROWS_PER_KB = 1024 / (BN * ES);  // B rows per 1-KiB block
+    static constexpr int A_ROWS_PER_KB = 1024 / (BK * ES);
+    static constexpr int NKS = BK / KSTEP;               // MFMA K steps per tile
+    static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be whole 16x16 blocks");
+    static_assert(BK % KSTEP == 0, "BK must be a multiple of the MFMA K step");
+    static_assert(KC == 4 || KC == 8, "A rows must be 64 or 128 bytes");
+    static_assert((NCH & (NCH - 1)) == 0 && NCH >= 4, "B rows must be a power-of-two number of chunks");
+    static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "stage must split into 1 KiB per wave");
+    static_assert(BN * ES <= 1024 && 1024 % (BN * ES) == 0, "B row must divide 1 KiB");
+    static_assert(LDS_BYTES <= 163840, "LDS ring exceeds 160 KiB");
+    static_assert(S >= 1 && S <= 4, "1..4 stages");
+    static_assert(LPS * (S > 2 ? S - 2 : 0) <= 63, "vmcnt is a 6-bit counter");
+};
+
+// ---- producers -------------------------------------------------------------
+
+// Chunk q (0..A_INSTR-1) that this lane moves for the A tile: the LDS byte of
+// the chunk is (wave*A_INSTR + q)*1024 + 16*lane within the stage's A region;
+// returns the (row, first element k) of global memory that belongs there.
+template <class C>
+__device__ __forceinline__ void a_chunk(int wave, int lane, int q, int& row, int& kel) {
+    const int lds_off = (wave * C::A_INSTR + q) * 1024 + lane * 16;
+    const int line = lds_off >> 7;
+    const int slot = (lds_off >> 4) & 7;
+    const int p = (line & 7) ^ ((line >> 3) & 1);
+    const int L = (line << 3) + (slot ^ p);
+    row = L / C::KC;
+    kel = (L % C::KC) * C::EPC;
+}
+// Same for the B tile: (row k, first element n).
+template <class C>
+__device__ __forceinline__ void b_chunk(int wave, int lane, int q, int& krow, int& nel) {
+    const int lds_off = (wave * C::B_INSTR + q) * 1024 + lane * 16;
+    krow = lds_off / (C::BN * C::ES);
+    const int pc = (lds_off % (C::BN * C::ES)) >> 4;
+    nel = (pc ^ b_swz<C::Dt, C::NCH>(krow)) * C::EPC;
+}
+
+template <class C>
+struct Staging {
+    i32x4 a[C::A_INSTR];
+    i32x4 b[C::B_INSTR];
+};
+
+// Element-wise load of one 16-byte chunk (GENERIC producer): elements at or
+// beyond `valid` are zero.  `off` is the byte offset of the first element.
+template <int ES>
+__device__ __forceinline__ i32x4 load_chunk_elementwise(__amdgpu_buffer_rsrc_t r, uint32_t off, int valid) {
+    i32x4 v = {0, 0, 0, 0};
+    if constexpr (ES == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t o = (e < valid) ? off + 4u * e : OOB;
+            v[e] = (int)__builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0);
+        }
+    } else if constexpr (ES == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t o = (e < valid) ? off + 2u * e : OOB;
+            const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, 0);
+            v[e >> 1] |= (int)(h << (16 * (e & 1)));
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t o = (e < valid) ? off + (uint32_t)e : OOB;
+            const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(r, o, 0, 0);
+            v[e >> 2] |= (int)(b << (8 * (e & 3)));
+        }
+    }
+    return v;
+}
+
+// Issue the global loads of K tile `kt`: DIRECT straight into LDS stage
+// `stage`, the other producers into the staging registers.  Lanes whose
+// chunk lies outside the matrix get offset 2^31 and receive zeros.
+template <class C>
+__device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, int kt, char PGEMM_LDS* stage,
+                                           Staging<C>& st, int wave, int lane) {
+    constexpr int ES = C::ES;
+    const int k0 = kt * C::BK;
+    // Tile-local bases keep every byte offset below 2^31.
+    const char* a_base = (const char*)g.A + ((int64_t)m0 * g.lda + k0) * ES;
+    const char* b_base = (const char*)g.B + ((int64_t)k0 * g.ldb + n0) * ES;
+    const int rows_left = g.M - m0, k_left = g.K - k0, n_left = g.N - n0;
+    if constexpr (C::P == PROD_DIRECT) {
+        const i32x4 ra = make_rsrc_sgpr(a_base);
+        const i32x4 rb = make_rsrc_sgpr(b_base);
+        const uint32_t sa = (uint32_t)(size_t)stage + (uint32_t)(wave * C::A_INSTR) * 1024u;
+        const uint32_t sb = (uint32_t)(size_t)stage + (uint32_t)C::A_BYTES + (uint32_t)(wave * C::B_INSTR) * 1024u;
+#pragma unroll
+        for (int q = 0; q < C::A_INSTR; ++q) {
+            int row, kel;
+            a_chunk<C>(wave, lane, q, row, kel);
+            const bool ok = row < rows_left && kel < k_left;
+            dma16(ra, ok ? (uint32_t)(row * (int)g.lda + kel) * ES : OOB, sa + q * 1024u);
+        }
+#pragma unroll
+        for (int q = 0; q < C::B_INSTR; ++q) {
+            int krow, nel;
+            b_chunk<C>(wave, lane, q, krow, nel);
+            const bool ok = krow < k_left && nel < n_left;
+            dma16(rb, ok ? (uint32_t)(krow * (int)g.ldb + nel) * ES : OOB, sb + q * 1024u);
+        }
+    } else {
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base);
+#pragma unroll
+        for (int q = 0; q < C::A_INSTR; ++q) {
+            int row, kel;
+            a_chunk<C>(wave, lane, q, row, kel);
+            const bool ok = row < rows_left && kel < k_left;
+            const uint32_t off = (uint32_t)(row * (int)g.lda + kel) * ES;
+            if constexpr (C::P == PROD_REGISTER) {
+                st.a[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? off : OOB, 0, 0);
+            } else {
+                st.a[q] = load_chunk_elementwise<ES>(ra, off, ok ? min(C::EPC, k_left - kel) : 0);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < C::B_INSTR; ++q) {
+            int krow, nel;
+            b_chunk<C>(wave, lane, q, krow, nel);
+            const bool ok = krow < k_left && nel < n_left;
+            const uint32_t off = (uint32_t)(krow * (int)g.ldb + nel) * ES;
+            if constexpr (C::P == PROD_REGISTER) {
+                st.b[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? off : OOB, 0, 0);
+            } else {
+                st.b[q] = load_chunk_elementwise<ES>(rb, off, ok ? min(C::EPC, n_left - nel) : 0);
+            }
+        }
+    }
+}
+
+// Register producers: write the staged chunks to the same LDS bytes the
+// direct producer fills.
+template <class C>
+__device__ __forceinline__ void store_tile(char PGEMM_LDS* stage, const Staging<C>& st, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < C::A_INSTR; ++q)
+        *(i32x4 PGEMM_LDS*)(stage + (wave * C::A_INSTR + q) * 1024 + lane * 16) = st.a[q];
+#pragma unroll
+    for (int q = 0; q < C::B_INSTR; ++q)
+        *(i32x4 PGEMM_LDS*)(stage + C::A_BYTES + (wave * C::B_INSTR + q) * 1024 + lane * 16) = st.b[q];
+}
+
+// ---- consumer: MFMA fragments from one LDS stage ------------------------------
+
+template <class C>
+struct Frags {
+    i32x4 a[C::FM];
+    i32x4 b[C::FN];  // fp32: the B values of the four MFMAs of a K step
+};
+
+template <class C>
+__device__ __forceinline__ void read_frags(const char PGEMM_LDS* stage, int ks, int wm0, int wn0, int lane,
+                                           Frags<C>& f) {
+    constexpr int D = C::Dt;
+    const int li = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+        f.a[i] = *(const i32x4 PGEMM_LDS*)(stage + a_off<C::KC>(wm0 + 16 * i + li, ks * 4 + lg));
+    const char PGEMM_LDS* bs = stage + C::A_BYTES;
+    constexpr int ROWB = C::BN * C::ES;
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+        const int nb = wn0 + 16 * j;  // first column of the 16-wide block
+        if constexpr (D == DT_F16 || D == DT_BF16) {
+            // ds_read_b64_tr_b16: lane i of a 16-lane block receives element
+            // i%4 of the 4-element row piece addressed by lane 4e + i/4
+            // (e = 0..3), so lane j addresses row kb + j/4, columns nb + 4*(j%4),
+            // and lane i ends up with B[kb + e][nb + i], e = 0..3.
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = ks * C::KSTEP + 8 * lg + 4 * h + (li >> 2);
+                const int n = nb + 4 * (li & 3);
+                const int off = k * ROWB + (((n / C::EPC) ^ b_swz<D, C::NCH>(k)) << 4) + (n % C::EPC) * 2;
+                const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 PGEMM_LDS*)(bs + off));
+                const i32x2 w = __builtin_bit_cast(i32x2, v);
+                f.b[j][2 * h] = w[0];
+                f.b[j][2 * h + 1] = w[1];
+            }
+        } else if constexpr (D == DT_I8) {
+            // ds_read_b64_tr_b8: lane i receives byte i%8 of the 8-byte row
+            // piece addressed by lane 2e + i/8 (e = 0..7): lane j addresses row
+            // kb + j/2, columns nb + 8*(j%2).
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = ks * C::KSTEP + 16 * lg + 8 * h + (li >> 1);
+                const int n = nb + 8 * (li & 1);
+                const int off = k * ROWB + (((n / C::EPC) ^ b_swz<D, C::NCH>(k)) << 4) + (n % C::EPC);
+                const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 PGEMM_LDS*)(bs + off));
+                f.b[j][2 * h] = w[0];
+                f.b[j][2 * h + 1] = w[1];
+            }
+        } else {
+            // fp32: MFMA jm of the K step takes k = 4*lg + jm in lane group lg
+            // (element jm of the lane's A chunk), so lane l reads B[k][nb + l%16].
+#pragma unroll
+            for (int jm = 0; jm < 4; ++jm) {
+                const int k = ks * C::KSTEP + 4 * lg + jm;
+                const int n = nb + li;
+                const int off = k * ROWB + (((n / C::EPC) ^ b_swz<D, C::NCH>(k)) << 4) + (n % C::EPC) * 4;
+                f.b[j][jm] = *(const int PGEMM_LDS*)(bs + off);
+            }
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_block(typename C::T::Acc& acc, const i32x4& a, const i32x4& b) {
+    constexpr int D = C::Dt;
+    if constexpr (D == DT_BF16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                      acc, 0, 0, 0);
+    } else if constexpr (D == DT_F16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc,
+                                                     0, 0, 0);
+    } else if constexpr (D == DT_I8) {
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+    } else {
+        // Bit-cast whole vectors, then index: hipcc (clang 22) lowers
+        // __builtin_bit_cast(float, v[i]) of an int vector element to element 0
+        // for every i, which silently fed the first k of the chunk to all four
+        // MFMAs.
+        const f32x4 af = __builtin_bit_cast(f32x4, a);
+        const f32x4 bf = __builtin_bit_cast(f32x4, b);
+#pragma unroll
+        for (int jm = 0; jm < 4; ++jm) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[jm], bf[jm], acc, 0, 0, 0);
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_all(typename C::T::Acc (&acc)[C::FM][C::FN], const Frags<C>& f) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) mfma_block<C>(acc[i][j], f.a[i], f.b[j]);
+}
+
+// ---- stage protocol -------------------------------------------------------------
+
+// Barrier B_t: the ready edge of tile t (its loads landed in every wave: at
+// most `pending` later tiles' loads may still be outstanding, since vector
+// loads retire in issue order) and the reuse edge of the stage the previous
+// tile occupied (every wave's LDS reads of it are complete: lgkmcnt(0)).
+template <class C>
+__device__ __forceinline__ void sync_ready(int pending) {
+    if constexpr (C::P == PROD_DIRECT) {
+        if constexpr (C::S >= 4) {
+            if (pending >= 2) {
+                wait_barrier<2 * C::LPS>();
+            } else if (pending == 1) {
+                wait_barrier<C::LPS>();
+            } else {
+                wait_barrier<0>();
+            }
+        } else if constexpr (C::S == 3) {
+            if (pending >= 1) {
+                wait_barrier<C::LPS>();
+            } else {
+                wait_barrier<0>();
+            }
+        } else {
+            wait_barrier<0>();
+        }
+    } else {
+        // Register producers: the compiler waited for the loads before their
+        // ds_write; the writes themselves are covered by lgkmcnt(0).
+        lgkm_barrier();
+    }
+}
+
+// Producer work right after B_t, into the stage freed by tile t-1.
+// DIRECT: issue tile t+S-1.  REGISTER/GENERIC: write tile t+S-1 (held in
+// registers since B_{t-1}) and start loading tile t+S.
+template <class C>
+__device__ __forceinline__ void produce_after_barrier(const KernelArgs& g, int m0, int n0, int t, int nK,
+                                                      char PGEMM_LDS* smem, int freed, Staging<C>& st, int wave,
+                                                      int lane) {
+    char PGEMM_LDS* stage = smem + freed * C::STAGE_BYTES;
+    if constexpr (C::P == PROD_DIRECT) {
+        if (t + C::S - 1 < nK) issue_tile<C>(g, m0, n0, t + C::S - 1, stage, st, wave, lane);
+    } else {
+        if (t + C::S - 1 < nK) store_tile<C>(stage, st, wave, lane);
+        if (t + C::S < nK) issue_tile<C>(g, m0, n0, t + C::S, stage, st, wave, lane);
+    }
+}
+
+// One K tile of the S >= 2 pipeline.  Fragments for K step ks+1 are read
+// while the MFMAs of step ks run; for the tile's last step the next reads
+// belong to tile t+1, so B_{t+1} and the producer's issue sit right before
+// them -- after the last LDS reads of tile t and before its last MFMAs.
+// PAR is the fragment buffer holding step 0 of this tile.
+template <class C, int PAR>
+__device__ __forceinline__ void tile_body(const KernelArgs& g, int m0, int n0, int t, int nK, char PGEMM_LDS* smem,
+                                          int& cur, Staging<C>& st, Frags<C> (&f)[2],
+                                          typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane, int wm0,
+                                          int wn0) {
+    constexpr int NKS = C::BK / C::KSTEP;
+    const char PGEMM_LDS* cstage = smem + cur * C::STAGE_BYTES;
+    const int nstage = (cur + 1 == C::S) ? 0 : cur + 1;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        Frags<C>& use = f[(PAR + ks) & 1];
+        Frags<C>& nxt = f[(PAR + ks + 1) & 1];
+        // The reads of `use` were issued a whole step ago; saying so lets the
+        // MFMAs below start without waiting on the reads issued next.
+        lgkm_drain();
+        if (ks + 1 < NKS) {
+            read_frags<C>(cstage, ks + 1, wm0, wn0, lane, nxt);
+        } else if (t + 1 < nK) {
+            sync_ready<C>(min(C::S - 2, nK - 2 - t));                                   // B_{t+1}
+            produce_after_barrier<C>(g, m0, n0, t + 1, nK, smem, cur, st, wave, lane);  // stage of tile t is free
+            read_frags<C>(smem + nstage * C::STAGE_BYTES, 0, wm0, wn0, lane, nxt);
+        }
+        mfma_all<C>(acc, use);
+    }
+    cur = nstage;
+}
+
+template <class C>
+__device__ __forceinline__ void pipelined_loop(const KernelArgs& g, int m0, int n0, int nK, char PGEMM_LDS* smem,
+                                               typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane, int wm0,
+                                               int wn0) {
+    constexpr int NKS = C::BK / C::KSTEP;
+    Staging<C> st;
+    Frags<C> f[2];
+    // Prologue: tiles 0 .. S-2 into stages 0 .. S-2, never past nK.
+#pragma unroll
+    for (int p = 0; p < C::S - 1; ++p) {
+        if (p < nK) {
+            issue_tile<C>(g, m0, n0, p, smem + p * C::STAGE_BYTES, st, wave, lane);
+            if constexpr (C::P != PROD_DIRECT) store_tile<C>(smem + p * C::STAGE_BYTES, st, wave, lane);
+        }
+    }
+    if constexpr (C::P != PROD_DIRECT) {
+        if (C::S - 1 < nK) issue_tile<C>(g, m0, n0, C::S - 1, smem, st, wave, lane);
+    }
+    sync_ready<C>(min(C::S - 2, nK - 1));                                      // B_0
+    produce_after_barrier<C>(g, m0, n0, 0, nK, smem, C::S - 1, st, wave, lane);  // stage S-1 was never used
+    read_frags<C>(smem, 0, wm0, wn0, lane, f[0]);
+    int cur = 0;
+    if constexpr (NKS % 2 == 0) {
+        for (int t = 0; t < nK; ++t)
+            tile_body<C, 0>(g, m0, n0, t, nK, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+    } else {
+        for (int t = 0; t < nK; t += 2) {
+            tile_body<C, 0>(g, m0, n0, t, nK, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+            if (t + 1 < nK) tile_body<C, 1>(g, m0, n0, t + 1, nK, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+        }
+    }
+}
+
+// MFMA work on one stage with the fragments of step ks+1 read under step ks.
+template <class C>
+__device__ __forceinline__ void compute_stage(const char PGEMM_LDS* stage, int wm0, int wn0, int lane,
+                                              typename C::T::Acc (&acc)[C::FM][C::FN]) {
+    constexpr int NKS = C::BK / C::KSTEP;
+    Frags<C> f[2];
+    read_frags<C>(stage, 0, wm0, wn0, lane, f[0]);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        if (ks > 0) lgkm_drain();
+        if (ks + 1 < NKS) read_frags<C>(stage, ks + 1, wm0, wn0, lane, f[(ks + 1) & 1]);
+        mfma_all<C>(acc, f[ks & 1]);
+    }
+}
+
+// Single LDS buffer.  DIRECT: load, wait, barrier, compute, barrier (nothing
+// of the load overlaps the arithmetic).  REGISTER/GENERIC: tile t+1 is
+// prefetched into registers before the arithmetic on tile t and written after
+// the second barrier.
+template <class C>
+__device__ __forceinline__ void single_buffer_loop(const KernelArgs& g, int m0, int n0, int nK, char PGEMM_LDS* smem,
+                                                   typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane,
+                                                   int wm0, int wn0) {
+    Staging<C> st;
+    if constexpr (C::P == PROD_DIRECT) {
+        for (int t = 0; t < nK; ++t) {
+            issue_tile<C>(g, m0, n0, t, smem, st, wave, lane);
+            wait_barrier<0>();  // ready
+            compute_stage<C>(smem, wm0, wn0, lane, acc);
+            lgkm_barrier();     // reuse
+        }
+    } else {
+        issue_tile<C>(g, m0, n0, 0, smem, st, wave, lane);
+        store_tile<C>(smem, st, wave, lane);
+        for (int t = 0; t < nK; ++t) {
+            lgkm_barrier();  // ready
+            const bool more = t + 1 < nK;
+            if (more) issue_tile<C>(g, m0, n0, t + 1, smem, st, wave, lane);
+            compute_stage<C>(smem, wm0, wn0, lane, acc);
+            lgkm_barrier();  // reuse
+            if (more) store_tile<C>(smem, st, wave, lane);
+        }
+    }
+}
+
+// Workgroup -> output tile.  Workgroups are dealt round-robin over the 8 XCDs
+// (each with its own L2); the remap gives every XCD a contiguous range of
+// logical tiles, and the grouped raster makes that range a compact block of
+// tile-rows x tile-columns so the XCD's L2 serves shared A and B panels.
+__device__ __forceinline__ void tile_of(const KernelArgs& g, int& tm, int& tn) {
+    const int G = g.tiles_m * g.tiles_n;
+    const int w = blockIdx.x;
+    const int per = G >> 3;
+    const int G8 = per << 3;
+    const int L = (w < G8) ? (w & 7) * per + (w >> 3) : w;
+    const int width = g.group_m * g.tiles_n;
+    const int grp = L / width;
+    const int first = grp * g.group_m;
+    const int gm = min(g.tiles_m - first, g.group_m);
+    const int r = L - grp * width;
+    tm = first + r % gm;
+    tn = r / gm;
+}
+
+// ---- epilogue: C = alpha*acc + beta*C (fused, as in the pages' kernel) -------------
+
+template <class C>
+__device__ __forceinline__ void store_c(const KernelArgs& g, int m0, int n0, int wm0, int wn0, int lane,
+                                        typename C::T::Acc (&acc)[C::FM][C::FN]) {
+    const int li = lane & 15, lg = lane >> 4;
+    const int rows_left = g.M - m0, n_left = g.N - n0;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = wm0 + 16 * i + 4 * lg + r;
+            if (row >= rows_left) continue;
+            const int64_t base = (int64_t)(m0 + row) * g.ldc + n0;
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                const int col = wn0 + 16 * j + li;
+                if (col >= n_left) continue;
+                if constexpr (C::Dt == DT_I8) {
+                    int* cp = (int*)g.C + base + col;
+                    uint32_t v = (uint32_t)g.ialpha * (uint32_t)acc[i][j][r];
+                    if (g.beta_nonzero) v += (uint32_t)g.ibeta * (uint32_t)(*cp);
+                    *cp = (int)v;
+                } else {
+                    float* cp = (float*)g.C + base + col;
+                    float v = g.alpha * acc[i][j][r];
+                    if (g.beta_nonzero) v = fmaf(g.beta, *cp, v);
+                    *cp = v;
+                }
+            }
+        }
+    }
+}
+
+// ---- the kernel -------------------------------------------------------------------------
+
+template <class C>
+__global__ void __launch_bounds__(C::NT) gemm_kernel(KernelArgs g) {
+    __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_BYTES];
+    char PGEMM_LDS* smem = (char PGEMM_LDS*)smem_raw;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm0 = (wave / C::WGN) * C::WM;
+    const int wn0 = (wave % C::WGN) * C::WN;
+    int tm, tn;
+    tile_of(g, tm, tn);
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    const int nK = (g.K + C::BK - 1) / C::BK;
+
+    typename C::T::Acc acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::T::Acc{0, 0, 0, 0};
+
+    if (nK > 0) {
+        if constexpr (C::S == 1) {
+            single_buffer_loop<C>(g, m0, n0, nK, smem, acc, wave, lane, wm0, wn0);
+        } else {
+            pipelined_loop<C>(g, m0, n0, nK, smem, acc, wave, lane, wm0, wn0);
+        }
+    }
+    store_c<C>(g, m0, n0, wm0, wn0, lane, acc);
+}
+
+}  // namespace pgemm

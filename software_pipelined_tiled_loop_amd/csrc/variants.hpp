@@ -1,0 +1,36 @@
+// variants.hpp -- the table of compiled kernel variants (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include "pgemm_kernel.hpp"
+
+namespace pgemm {
+
+typedef hipError_t (*LaunchFn)(const KernelArgs&, int grid, hipStream_t);
+
+struct VariantDesc {
+    int dtype, bm, bn, bk, stages, wgm, wgn, producer;
+    int threads, lds_bytes;
+    LaunchFn launch;
+};
+
+template <class C>
+hipError_t launch_variant(const KernelArgs& a, int grid, hipStream_t s) {
+    hipLaunchKernelGGL(gemm_kernel<C>, dim3(grid), dim3(C::NT), 0, s, a);
+    return hipGetLastError();
+}
+
+#define PGEMM_VARIANT(D, BM, BN, BK, S, WGM, WGN, P)                                      \
+    VariantDesc {                                                                         \
+        D, BM, BN, BK, S, WGM, WGN, P, Cfg<D, BM, BN, BK, S, WGM, WGN, P>::NT,             \
+            Cfg<D, BM, BN, BK, S, WGM, WGN, P>::LDS_BYTES,                                 \
+            &launch_variant<Cfg<D, BM, BN, BK, S, WGM, WGN, P>>                            \
+    }
+
+// Per-dtype tables, each defined in its own translation unit.
+const VariantDesc* variants_f32(int* n);
+const VariantDesc* variants_f16(int* n);
+const VariantDesc* variants_bf16(int* n);
+const VariantDesc* variants_i8(int* n);
+
+}  // namespace pgemm

@@ -30,8 +30,8 @@ MUTANTS = {
     "dropped_last_k": ("for (int64_t k = 0; k < K; ++k) {\n            double a", "for (int64_t k = 0; k + 1 < K; ++k) {\n            double a"),
     "f16_bias": ("v = ldexp((double)(1024 + m), e - 25);", "v = ldexp((double)(1024 + m), e - 24);"),
     "bf16_shift": ("uint32_t u = ((uint32_t)h) << 16;", "uint32_t u = ((uint32_t)h) << 15;"),
-    "int8_unsigned": ("s += (int64_t)A[i * lda + k] * (int64_t)B[k * ldb + j];",
-                      "s += (int64_t)(uint8_t)A[i * lda + k] * (int64_t)B[k * ldb + j];"),
+    "int8_unsigned": ("const int64_t a = (int64_t)A[i * lda + k];",
+                      "const int64_t a = (int64_t)(uint8_t)A[i * lda + k];"),
 }
 
 

@@ -1,0 +1,280 @@
+"""GPU parity: the HIP library against the oracle, through the C ABI.
+
+Rules (the benchmark's stated tolerances):
+  int8 -> int32   bit-exact
+  fp32            max|C - C_ref| <= 1e-5 * sqrt(K) * max|C_ref|
+  fp16 / bf16     max|C - C_ref| <= 2e-3 * sqrt(K) * max|C_ref|
+The oracle sees exactly the rounded inputs the GPU sees, so input rounding is
+not error.  Pipelining changes no arithmetic (page "GPU-Kernel pipelinen",
+step 5): within one tile class the output must also be bit-identical across
+ring depths and producers, which catches a stale, duplicated or missing K tile
+even in float.  Every case prints its parameters before it runs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from software_pipelined_tiled_loop_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from software_pipelined_tiled_loop_amd import binding
+    return binding
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def run_gpu(lib, op, stages=0, producer=None, tile=None, expect=0):
+    dev = torch.device("cuda:0")
+    A = op.A.to(dev)
+    B = op.B.to(dev)
+    C = op.C.to(dev)
+    o = lib._opts(producer, tile)
+    r = lib.pgemm_gemm_ex(op.M, op.N, op.K, op.alpha, A if op.M and op.K else 0, max(op.lda, 1),
+                          B if op.K and op.N else 0, max(op.ldb, 1), op.beta, C if op.M else 0, max(op.ldc, 1),
+                          op.dtype, stages, o, None)
+    assert r == expect, lib.pgemm_strerror(r)
+    torch.cuda.synchronize()
+    return C.cpu()
+
+
+def reference(op, rows=None):
+    A, B, C0 = op.numpy_views()
+    return oracle.gemm(op.dtype, op.M, op.N, op.K, op.alpha, A, B, op.beta, C0 if op.beta != 0 else None,
+                       rows=rows)
+
+
+def check(op, got, rows=None):
+    ref = reference(op, rows)
+    g = got[:, :op.N] if rows is None else got[rows, :op.N]
+    if op.dtype == "i8":
+        diff = np.nonzero(g.numpy() != ref)
+        assert diff[0].size == 0, "int8 mismatch at %s: got %s want %s" % (
+            list(zip(diff[0][:5], diff[1][:5])), g.numpy()[diff][:5], ref[diff][:5])
+        return 0.0
+    gd = g.to(torch.float64).numpy()
+    assert np.all(np.isfinite(gd)), "non-finite output"
+    err = np.max(np.abs(gd - ref)) if ref.size else 0.0
+    scale = np.max(np.abs(ref)) if ref.size else 0.0
+    bound = TOL[op.dtype] * math.sqrt(max(op.K, 1)) * scale
+    assert err <= bound, "max err %g > bound %g (scale %g)" % (err, bound, scale)
+    return err
+
+
+def padding_untouched(op, got):
+    """Columns n >= N of C are the caller's memory beyond the matrix: unchanged."""
+    if op.ldc > op.N and op.M:
+        pad = got[:, op.N:]
+        ref = op.C[:, op.N:]
+        if op.dtype == "i8":
+            assert torch.equal(pad, ref)
+        else:
+            assert torch.equal(torch.isnan(pad), torch.isnan(ref))
+
+
+# ------------------------------------------------------------------ small configs
+
+@pytest.mark.parametrize("stages", [1, 2])
+def test_config0_fp32_256_single_vs_double(lib, stages):
+    cfg = inputs.CONFIGS[0]
+    say("cfg0 fp32 256^3 stages", stages, "tile 128x64x16")
+    op = inputs.make_operands("f32", 256, 256, 256, seed=inputs.seed_for(0), alpha=1.0, beta=0.0)
+    got = run_gpu(lib, op, stages=stages, tile=(128, 64, 16))
+    check(op, got)
+    assert cfg["M"] == 256
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+@pytest.mark.parametrize("stages", [1, 2, 3, 4])
+def test_all_dtypes_all_stages_small(lib, dtype, stages):
+    # several tiles in M and N plus ragged tails; K spans several K tiles + tail
+    M, N, K = 300, 280, 16 * 37  # K multiple of 16 keeps every dtype on the vector path
+    say("small", dtype, "stages", stages, (M, N, K))
+    op = inputs.make_operands(dtype, M, N, K, seed=inputs.seed_for(3, stages), alpha=1.0, beta=0.0)
+    got = run_gpu(lib, op, stages=stages)
+    check(op, got)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+def test_alpha_beta_and_padded_leading_dims(lib, dtype):
+    M, N, K = 200, 136, 272
+    alpha, beta = (2, -3) if dtype == "i8" else (1.5, -0.5)
+    say("alpha/beta + ld padding", dtype)
+    op = inputs.make_operands(dtype, M, N, K, seed=77, alpha=alpha, beta=beta, lda=K + 16, ldb=N + 16,
+                              ldc=N + 5)
+    got = run_gpu(lib, op, stages=2)
+    check(op, got)
+    padding_untouched(op, got)
+
+
+# ------------------------------------------------------------------ invariance pins
+
+def tile_classes(lib, dtype):
+    seen = {}
+    for i in range(lib.pgemm_num_variants()):
+        v = lib.pgemm_variant_info(i)
+        if v["dtype"] != dtype or v["producer"] == "generic":
+            continue
+        key = (v["tile_m"], v["tile_n"], v["tile_k"])
+        seen.setdefault(key, []).append((v["stages"], v["producer"]))
+    return seen
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_bit_identical_across_stages_and_producers(lib, dtype):
+    """One tile class = one MFMA schedule: every ring depth and producer must
+    give the same bits (a stale, duplicated or skipped K tile would not)."""
+    M, N, K = 384, 320, 16 * 40
+    op = inputs.make_operands(dtype, M, N, K, seed=4242, alpha=1.0, beta=0.0)
+    for tile, variants in tile_classes(lib, dtype).items():
+        outs = []
+        for stages, producer in sorted(variants):
+            say("invariance", dtype, tile, stages, producer)
+            outs.append(((stages, producer), run_gpu(lib, op, stages=stages, producer=producer, tile=tile)))
+        check(op, outs[0][1])
+        for key, o in outs[1:]:
+            assert torch.equal(o.view(torch.int32), outs[0][1].view(torch.int32)), (tile, key, outs[0][0])
+
+
+@pytest.mark.parametrize("stages", [1, 2, 3, 4])
+def test_k_slice_fingerprint_int8(lib, stages):
+    """A = 1; B[k, j] = ((k // 64) + j) % 7 + 1: the exact column sums reveal a
+    dropped, duplicated or stale K tile (page "GPU-Kernel pipelinen", common
+    pitfalls: a forgotten epilogue tile silently drops the last BK columns)."""
+    M, N = 256, 256
+    for K in (64, 128, 192, 64 * stages, 64 * stages + 64, 64 * 9):
+        say("fingerprint stages", stages, "K", K)
+        op = inputs.make_operands("i8", M, N, K, seed=1, alpha=1, beta=0)
+        op.A[:, :K] = 1
+        kk = torch.arange(K).unsqueeze(1)
+        jj = torch.arange(N).unsqueeze(0)
+        op.B[:, :N] = (((kk // 64) + jj) % 7 + 1).to(torch.int8)
+        got = run_gpu(lib, op, stages=stages, tile=(256, 256, 64))
+        check(op, got)
+
+
+def test_alpha_scaling_is_exact(lib):
+    op = inputs.make_operands("bf16", 256, 256, 512, seed=8, alpha=1.0, beta=0.0)
+    c1 = run_gpu(lib, op, stages=2)
+    op.alpha = 2.0
+    c2 = run_gpu(lib, op, stages=2)
+    assert torch.equal(c2, 2.0 * c1)
+
+
+# ------------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_edge_sizes(lib, dtype):
+    """M, N around 16 and the tile edge; K around the K tile and the ring
+    depth, including fewer K tiles than stages and K = 0."""
+    es = inputs.ELEM_BYTES[dtype]
+    epc = 16 // es
+    bk = {"f32": 32, "f16": 64, "bf16": 64, "i8": 128}[dtype]
+    for (M, N) in [(1, 1), (15, 17), (16, 16), (127, 129), (128, 128), (129, 1)]:
+        for K in (0, 1, 3, epc, bk - epc, bk, bk + epc, 3 * bk, 4 * bk + 1):
+            for stages in (1, 4):
+                say("edge", dtype, (M, N, K), "stages", stages)
+                op = inputs.make_operands(dtype, M, N, K, seed=M * 1000 + N * 10 + K, alpha=1.0, beta=0.0)
+                got = run_gpu(lib, op, stages=stages)
+                check(op, got)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+def test_generic_producer_misaligned(lib, dtype):
+    """Odd leading dimensions force the element-wise producer."""
+    M, N, K = 130, 77, 203
+    say("misaligned", dtype)
+    op = inputs.make_operands(dtype, M, N, K, seed=5, alpha=1.0, beta=0.0, lda=K + 1, ldb=N + 2, ldc=N + 3)
+    got = run_gpu(lib, op, stages=3)
+    check(op, got)
+
+
+def test_beta_zero_ignores_nan_in_C_and_K0(lib):
+    op = inputs.make_operands("f32", 64, 64, 0, seed=2, alpha=1.0, beta=0.0)
+    got = run_gpu(lib, op)
+    assert torch.equal(got[:, :64], torch.zeros(64, 64))
+    op = inputs.make_operands("f32", 64, 64, 0, seed=2, alpha=1.0, beta=0.5)
+    got = run_gpu(lib, op)
+    assert torch.equal(got[:, :64], 0.5 * op.C[:, :64])
+
+
+def test_argument_errors_before_launch(lib):
+    op = inputs.make_operands("bf16", 8, 8, 8, seed=1)
+    say("errors")
+    A = op.A.cuda()
+    C = op.C.cuda()
+    assert lib.pgemm_gemm(8, 8, 8, 1.0, A, 4, A, 8, 0.0, C, 8, "bf16", 0) == -1  # lda < K
+    assert lib.pgemm_gemm(8, 8, 8, 1.0, A, 8, A, 8, 0.0, C, 8, 7, 0) == -2
+    assert lib.pgemm_gemm(8, 8, 8, 1.0, A, 8, A, 8, 0.0, C, 8, "bf16", 5) == -3
+    assert lib.pgemm_gemm(8, 8, 8, 0.5, A, 8, A, 8, 0.0, C, 8, "i8", 0) == -5
+    assert lib.pgemm_gemm(0, 8, 8, 1.0, 0, 8, 0, 8, 0.0, 0, 8, "bf16", 0) == 0
+
+
+# ------------------------------------------------------------------ full-size configs
+
+def sampled_rows(M, n=48, seed=0, run=12):
+    """Rows in runs of `run` consecutive rows (the oracle parallelises a run):
+    the first and last rows, a run across the first tile boundary, and random runs."""
+    g = np.random.default_rng(seed)
+    rows = set(range(0, min(run, M))) | set(range(max(0, M - run), M)) | set(range(250, min(262, M)))
+    for s in g.choice(max(1, M - run), size=max(1, n // run), replace=False).tolist():
+        rows |= set(range(s, min(M, s + run)))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name,dtype,M,N,K,alpha,beta,cfg", [
+    ("cfg1 fp32 4096^3 beta=0.5", "f32", 4096, 4096, 4096, 1.0, 0.5, 1),
+    ("cfg2 int8 4096^3", "i8", 4096, 4096, 4096, 1, 0, 2),
+    ("cfg3 bf16 4096^3", "bf16", 4096, 4096, 4096, 1.0, 0.0, 3),
+    ("cfg3 fp16 4096^3", "f16", 4096, 4096, 4096, 1.0, 0.0, 3),
+    ("cfg4 bf16 K=16384", "bf16", 4096, 4096, 16384, 1.0, 0.0, 4),
+])
+def test_full_size_sampled(lib, name, dtype, M, N, K, alpha, beta, cfg):
+    """The benchmark shapes with the planner's own launch (what bench.py times),
+    checked on sampled rows against the oracle."""
+    say(name)
+    op = inputs.make_operands(dtype, M, N, K, seed=inputs.seed_for(cfg), alpha=alpha, beta=beta)
+    got = run_gpu(lib, op, stages=0)
+    rows = sampled_rows(M, seed=cfg)
+    check(op, got, rows=rows)
+
+
+@pytest.mark.parametrize("K", [32, 64, 256, 1024])
+def test_k_sweep_sampled(lib, K):
+    say("k-sweep K", K)
+    op = inputs.make_operands("bf16", 4096, 4096, K, seed=inputs.seed_for(4, K % 97), alpha=1.0, beta=0.0)
+    for stages in (0, 1, 4):
+        got = run_gpu(lib, op, stages=stages)
+        check(op, got, rows=sampled_rows(4096, n=24, seed=K))
+
+
+def test_ragged_4000_3968_4001(lib):
+    r = inputs.RAGGED
+    say("ragged", r)
+    op = inputs.make_operands("bf16", r["M"], r["N"], r["K"], seed=inputs.seed_for(4, 9), alpha=1.0, beta=0.0,
+                              lda=r["lda"], ldb=r["ldb"], ldc=r["ldc"])
+    got = run_gpu(lib, op, stages=0)
+    check(op, got, rows=sampled_rows(r["M"], n=24, seed=9))
+
+
+def test_identity_B_full_size_is_exact(lib):
+    """B = I gives C = A exactly (one nonzero product per sum), over every tile
+    of a 4096 x 4096 problem."""
+    say("identity 4096")
+    N = 4096
+    A = inputs.draw("bf16", 4096, N, seed=31).cuda()
+    B = torch.eye(N, dtype=torch.bfloat16).cuda()
+    C = torch.empty(4096, N, dtype=torch.float32).cuda()
+    assert lib.pgemm_gemm(4096, N, N, 1.0, A, N, B, N, 0.0, C, N, "bf16", 0) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(C, A.float())
