@@ -32,6 +32,18 @@ HBM_PEAK_GBS = 8000.0
 PAGE_SGEMM_GFLOPS = 32107.5  # 2-stage SGEMM 4096^3 on the first page's (unnamed NVIDIA) GPU
 
 
+WORKLOADS = {
+    "f32": dict(name="fp32 SGEMM M=N=K=4096 row-major alpha=1 beta=0.5", dtype="f32", M=4096, N=4096, K=4096,
+                alpha=1.0, beta=0.5, cfg=1, data="seeded uniform[-1,1) fp32"),
+    "i8": dict(name="int8 IGEMM M=N=K=4096 int32 out", dtype="i8", M=4096, N=4096, K=4096, alpha=1, beta=0,
+               cfg=2, data="seeded uniform int8 [-128,127]"),
+    "bf16": dict(name="bf16 GEMM M=N=K=4096 fp32 out", dtype="bf16", M=4096, N=4096, K=4096, alpha=1.0,
+                 beta=0.0, cfg=3, data="seeded normal(0,1) rounded to bf16"),
+    "f16": dict(name="fp16 GEMM M=N=K=4096 fp32 out", dtype="f16", M=4096, N=4096, K=4096, alpha=1.0,
+                beta=0.0, cfg=3, data="seeded normal(0,1) rounded to fp16"),
+}
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "software_pipelined_tiled_loop_amd", "csrc")
@@ -131,6 +143,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="f32", choices=sorted(WORKLOADS),
+                    help="timed workload (default: the fp32 4096^3 headline); others are for profiling")
+    ap.add_argument("--stages", type=int, default=0, help="ring depth (0 = planner)")
+    ap.add_argument("--producer", default=None, choices=[None, "direct", "register", "generic"])
+    ap.add_argument("--tile", default=None, help="BMxBNxBK, e.g. 256x256x32")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library runs each GEMM on a single MI355X and has no "
@@ -147,16 +166,31 @@ def main():
     torch.cuda.set_device(0)
     src_hash = kernel_source_hash()
 
-    # ---- headline: fp32 SGEMM 4096^3, alpha=1, beta=0.5 ----
-    M = N = K = 4096
-    op, A, B, C = make_device_operands("f32", M, N, K, inputs.seed_for(1), 1.0, 0.5)
-    plan = plan_of(lib, "f32", M, N, K)
+    # ---- timed workload (default: fp32 SGEMM 4096^3, alpha=1, beta=0.5) ----
+    w = WORKLOADS[args.workload]
+    dt, M, N, K, alpha, beta, cfg_idx = w["dtype"], w["M"], w["N"], w["K"], w["alpha"], w["beta"], w["cfg"]
+    tile = tuple(int(x) for x in args.tile.split("x")) if args.tile else None
+    op, A, B, C = make_device_operands(dt, M, N, K, inputs.seed_for(cfg_idx), alpha, beta)
+    plan = plan_of(lib, dt, M, N, K, args.stages, args.producer, tile)
+    if plan is None:
+        print("no compiled variant for these options", file=sys.stderr)
+        sys.exit(1)
     stream = torch.cuda.current_stream()
+    opts = lib._opts(args.producer, tile)
 
     def step():
-        r = lib.pgemm_gemm(M, N, K, 1.0, A, K, B, N, 0.5, C, N, "f32", 0, stream)
+        r = lib.pgemm_gemm_ex(M, N, K, alpha, A, K, B, N, beta, C, N, dt, args.stages, opts, stream)
         if r != 0:
             raise lib.PgemmError(r)
+
+    if args.copy_calibration:
+        # a plain copy of 512 MiB: reads and writes exactly 512 MiB of HBM
+        src = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -172,13 +206,13 @@ def main():
     t_wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / args.steps
     value = tflops(M, N, K, ms)
-    kernel_key = "f32_%dx%dx%d_s%d_%s" % (plan["tile_m"], plan["tile_n"], plan["tile_k"], plan["stages"],
-                                          plan["producer"])
+    kernel_key = "%s_%dx%dx%d_s%d_%s" % (dt, plan["tile_m"], plan["tile_n"], plan["tile_k"], plan["stages"],
+                                         plan["producer"])
     traffic = load_traffic(kernel_key, src_hash)
-    roofline = {"bound": "mfma", "achieved": round(value, 3), "peak": PEAK["f32"], "unit": "TFLOP/s",
-                "frac": round(value / PEAK["f32"], 4), "traffic": traffic,
+    roofline = {"bound": "mfma", "achieved": round(value, 3), "peak": PEAK[dt], "unit": "TFLOP/s",
+                "frac": round(value / PEAK[dt], 4), "traffic": traffic,
                 "kernel": kernel_key, "algorithmic_flops_per_launch": 2 * M * N * K,
-                "algorithmic_bytes_per_launch": algorithmic_bytes("f32", M, N, K, 0.5)}
+                "algorithmic_bytes_per_launch": algorithmic_bytes(dt, M, N, K, beta)}
     del A, B, C
 
     reports = {}
@@ -189,89 +223,84 @@ def main():
         "metric": "GEMM TFLOP/s (int8 TOP/s) at 4096^3 and % of MI355X dtype peak; K-sweep by stages",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": round(value * 1000.0 / PAGE_SGEMM_GFLOPS, 4),
-        "dtype": "f32", "data": "synthetic (seeded uniform[-1,1) fp32)",
-        "config": {"workload": "fp32 SGEMM M=N=K=4096 row-major alpha=1 beta=0.5", "M": M, "N": N, "K": K,
-                   "pct_of_peak": round(100.0 * value / PEAK["f32"], 2), "plan": plan,
+        "vs_baseline": round(value * 1000.0 / PAGE_SGEMM_GFLOPS, 4) if args.workload == "f32" else None,
+        "dtype": dt, "data": "synthetic (%s)" % w["data"],
+        "config": {"workload": w["name"], "M": M, "N": N, "K": K,
+                   "pct_of_peak": round(100.0 * value / PEAK[dt], 2), "plan": plan,
                    "wall_s_timed_region": round(t_wall, 4), "kernel_source_hash": src_hash},
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "f32":
         out["cpu_baseline"] = cpu_baseline()
     if reports:
         out["reports"] = reports
     print(json.dumps(out))
 
 
+def plan_label(p):
+    return "%dx%dx%d s%d %s" % (p["tile_m"], p["tile_n"], p["tile_k"], p["stages"], p["producer"])
+
+
+def variant_sweep(lib, op, A, B, C, M, N, K, reps=20):
+    """Every compiled vector-producer variant of the dtype on this problem."""
+    out = {}
+    for i in range(lib.pgemm_num_variants()):
+        v = lib.pgemm_variant_info(i)
+        if v["dtype"] != op.dtype or v["producer"] == "generic":
+            continue
+        tile = (v["tile_m"], v["tile_n"], v["tile_k"])
+        ms = time_gemm(lib, op, A, B, C, stages=v["stages"], producer=v["producer"], tile=tile, reps=reps)
+        out[plan_label(v)] = round(tflops(M, N, K, ms), 1)
+    return out
+
+
 def run_reports(lib, torch):
     from software_pipelined_tiled_loop_amd import inputs
     rep = {}
     M = N = K = 4096
-
-    # int8 4096^3: producer x stages
-    op, A, B, C = make_device_operands("i8", M, N, K, inputs.seed_for(2), 1, 0)
-    d = {}
-    for prod in ("direct", "register"):
-        for s in (1, 2, 3, 4):
-            try:
-                ms = time_gemm(lib, op, A, B, C, stages=s, producer=prod, tile=(256, 256, 64))
-                d["%s_s%d" % (prod, s)] = round(tflops(M, N, K, ms), 1)
-            except Exception as e:  # variant not compiled
-                d["%s_s%d" % (prod, s)] = str(e)[:60]
-    ms = time_gemm(lib, op, A, B, C)
-    auto = tflops(M, N, K, ms)
-    rep["int8_4096"] = {"auto_TOPs": round(auto, 1), "pct_peak": round(100 * auto / PEAK["i8"], 2),
-                        "plan": plan_of(lib, "i8", M, N, K), "by_producer_stage_TOPs": d}
-    del A, B, C
-
-    for dt in ("bf16", "f16"):
-        op, A, B, C = make_device_operands(dt, M, N, K, inputs.seed_for(3, 0 if dt == "bf16" else 1), 1.0, 0.0)
-        d = {}
-        for s in (1, 2, 3, 4):
-            ms = time_gemm(lib, op, A, B, C, stages=s)
-            d["s%d" % s] = round(tflops(M, N, K, ms), 1)
+    for dt, cfg, alpha, beta in (("i8", 2, 1, 0), ("bf16", 3, 1.0, 0.0), ("f16", 3, 1.0, 0.0)):
+        op, A, B, C = make_device_operands(dt, M, N, K, inputs.seed_for(cfg, 0 if dt != "f16" else 1), alpha, beta)
         ms = time_gemm(lib, op, A, B, C)
         auto = tflops(M, N, K, ms)
-        rep["%s_4096" % dt] = {"auto_TFLOPs": round(auto, 1), "pct_peak": round(100 * auto / PEAK[dt], 2),
-                               "plan": plan_of(lib, dt, M, N, K), "by_stages_TFLOPs": d}
+        rep["%s_4096" % dt] = {"auto": round(auto, 1), "pct_peak": round(100 * auto / PEAK[dt], 2),
+                               "plan": plan_label(plan_of(lib, dt, M, N, K)),
+                               "variants": variant_sweep(lib, op, A, B, C, M, N, K)}
         del A, B, C
 
-    # fp32: the pages' tile class, 1 vs 2 stages
+    # fp32: the pages' tile class, 1 vs 2 stages, and the planner's choice
     op, A, B, C = make_device_operands("f32", M, N, K, inputs.seed_for(1), 1.0, 0.5)
     d = {}
     for s in (1, 2):
         ms = time_gemm(lib, op, A, B, C, stages=s, tile=(128, 64, 16), reps=10)
-        d["128x64x16_s%d" % s] = round(tflops(M, N, K, ms), 2)
+        d["128x64x16 s%d direct" % s] = round(tflops(M, N, K, ms), 2)
     rep["f32_4096_page_tile"] = d
     del A, B, C
 
-    # bf16 K-sweep + ragged
+    # bf16 K-sweep by ring depth (the planner picks the tile for each depth) + ragged
     sweep = {}
     for Ks in (32, 64, 256, 1024, 4096, 16384):
         op, A, B, C = make_device_operands("bf16", M, N, Ks, inputs.seed_for(4, Ks % 97), 1.0, 0.0)
         row = {}
         for s in (1, 2, 3, 4):
+            p = plan_of(lib, "bf16", M, N, Ks, stages=s)
             ms = time_gemm(lib, op, A, B, C, stages=s, reps=10)
-            row["s%d" % s] = round(tflops(M, N, Ks, ms), 1)
+            row["s%d" % s] = {"tflops": round(tflops(M, N, Ks, ms), 1), "plan": plan_label(p)}
         ms = time_gemm(lib, op, A, B, C, reps=10)
-        row["auto"] = round(tflops(M, N, Ks, ms), 1)
-        row["auto_plan"] = "%dx%dx%d s%d" % tuple(plan_of(lib, "bf16", M, N, Ks)[k]
-                                                  for k in ("tile_m", "tile_n", "tile_k", "stages"))
-        gbs = algorithmic_bytes("bf16", M, N, Ks, 0.0) / (ms * 1e-3) / 1e9
-        roof = min(PEAK["bf16"], 2.0 * M * N * Ks / algorithmic_bytes("bf16", M, N, Ks, 0.0) * HBM_PEAK_GBS / 1e3)
-        row["auto_pct_of_roof"] = round(100 * row["auto"] / roof, 1)
-        row["auto_GBs"] = round(gbs, 0)
+        byts = algorithmic_bytes("bf16", M, N, Ks, 0.0)
+        roof = min(PEAK["bf16"], 2.0 * M * N * Ks / byts * HBM_PEAK_GBS / 1e3)
+        row["auto"] = {"tflops": round(tflops(M, N, Ks, ms), 1), "plan": plan_label(plan_of(lib, "bf16", M, N, Ks)),
+                       "pct_of_roof": round(100 * tflops(M, N, Ks, ms) / roof, 1),
+                       "roof": "hbm" if roof < PEAK["bf16"] else "mfma",
+                       "GBs": round(byts / (ms * 1e-3) / 1e9, 0)}
         sweep["K%d" % Ks] = row
         del A, B, C
     r = inputs.RAGGED
     op, A, B, C = make_device_operands("bf16", r["M"], r["N"], r["K"], inputs.seed_for(4, 9), 1.0, 0.0,
                                        lda=r["lda"], ldb=r["ldb"], ldc=r["ldc"])
     ms = time_gemm(lib, op, A, B, C, reps=5)
-    p = plan_of(lib, "bf16", r["M"], r["N"], r["K"], aligned=0)
-    sweep["ragged_4000x3968x4001"] = {"auto": round(tflops(r["M"], r["N"], r["K"], ms), 1),
-                                      "plan": "%dx%dx%d s%d %s" % (p["tile_m"], p["tile_n"], p["tile_k"],
-                                                                   p["stages"], p["producer"])}
-    rep["bf16_k_sweep_TFLOPs"] = sweep
+    sweep["ragged_4000x3968x4001"] = {"tflops": round(tflops(r["M"], r["N"], r["K"], ms), 1),
+                                      "plan": plan_label(plan_of(lib, "bf16", r["M"], r["N"], r["K"], aligned=0))}
+    rep["bf16_k_sweep"] = sweep
     return rep
 
 

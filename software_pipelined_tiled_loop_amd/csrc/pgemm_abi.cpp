@@ -26,7 +26,11 @@ namespace {
 
 constexpr int kNumCU = 256;
 constexpr int kLdsPerCU = 163840;
-constexpr double kLoadLatencyCycles = 2400.0;  // assumed HBM/MALL latency under load (~1 us at 2.4 GHz)
+// Effective global->LDS latency the ring has to cover, in SIMD clocks.  Set
+// from measurement on MI355X at 4096^3: one K tile of a 256 x 256 tile
+// (>= 1024 MFMA cycles) covers it, and deeper rings measured slower there
+// (more loads in flight, same L2 bandwidth), so the model asks for S = 2.
+constexpr double kLoadLatencyCycles = 1000.0;
 
 struct Table {
     const VariantDesc* v;
@@ -87,13 +91,24 @@ double tile_compute_cycles(const VariantDesc& d, int share) {
     return flops / (4.0 * flops_per_simd_clk(d.dtype)) * share;
 }
 
-// Relative efficiency of a tile class (operand traffic per flop: larger
-// tiles need less L2->LDS and LDS->VGPR bandwidth per MFMA).
+// Measured efficiency of a tile class (fraction of dense peak at 4096^3 with
+// its best ring depth, seeded inputs, MI355X): the re-run tile search that
+// follows any change to the pipelined kernel.  Classes not listed fall back
+// to an operand-traffic estimate.
 double tile_efficiency(const VariantDesc& d) {
-    const double per = (double)(d.bm + d.bn) / (2.0 * d.bm * d.bn);  // bytes/flop per element byte
+    struct E { int dt, bm, bn, bk; double e; };
+    static const E table[] = {
+        {PGEMM_BF16, 256, 256, 64, 0.50}, {PGEMM_BF16, 256, 256, 32, 0.44}, {PGEMM_BF16, 128, 128, 64, 0.42},
+        {PGEMM_F16, 256, 256, 64, 0.48},  {PGEMM_F16, 256, 256, 32, 0.44},  {PGEMM_F16, 128, 128, 64, 0.40},
+        {PGEMM_I8, 256, 256, 128, 0.44},  {PGEMM_I8, 256, 256, 64, 0.41},   {PGEMM_I8, 128, 128, 128, 0.32},
+        {PGEMM_F32, 256, 256, 32, 0.90},  {PGEMM_F32, 128, 64, 16, 0.86},   {PGEMM_F32, 128, 128, 32, 0.82},
+    };
+    for (const E& x : table)
+        if (x.dt == d.dtype && x.bm == d.bm && x.bn == d.bn && x.bk == d.bk) return x.e;
+    const double per = (double)(d.bm + d.bn) / (2.0 * d.bm * d.bn);
     const double ref = 512.0 / (2.0 * 256 * 256);
-    double e = ref / per;
-    return e > 1.0 ? 1.0 : std::pow(e, 0.5);
+    const double e = ref / per;
+    return 0.4 * (e > 1.0 ? 1.0 : std::pow(e, 0.5));
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -267,6 +267,50 @@ __device__ __forceinline__ i32x4 load_chunk_elementwise(__amdgpu_buffer_rsrc_t r
     return v;
 }
 
+// DIRECT producer state for one K tile: buffer descriptors of the tile's A
+// and B panels, the LDS bases of the stage and the remaining extents.
+struct DmaTile {
+    i32x4 ra, rb;
+    uint32_t sa, sb;
+    int rows_left, k_left, n_left;
+};
+
+template <class C>
+__device__ __forceinline__ DmaTile dma_setup(const KernelArgs& g, int m0, int n0, int kt, char PGEMM_LDS* stage,
+                                             int wave) {
+    constexpr int ES = C::ES;
+    const int k0 = kt * C::BK;
+    DmaTile d;
+    // Tile-local bases keep every byte offset below 2^31.
+    d.ra = make_rsrc_sgpr((const char*)g.A + ((int64_t)m0 * g.lda + k0) * ES);
+    d.rb = make_rsrc_sgpr((const char*)g.B + ((int64_t)k0 * g.ldb + n0) * ES);
+    d.sa = (uint32_t)(size_t)stage + (uint32_t)(wave * C::A_INSTR) * 1024u;
+    d.sb = (uint32_t)(size_t)stage + (uint32_t)C::A_BYTES + (uint32_t)(wave * C::B_INSTR) * 1024u;
+    d.rows_left = g.M - m0;
+    d.k_left = g.K - k0;
+    d.n_left = g.N - n0;
+    return d;
+}
+
+// Load piece q (0..LPS-1) of the tile: one 1-KiB LDS-DMA block of A (q <
+// A_INSTR) or of B.
+template <class C>
+__device__ __forceinline__ void dma_piece(const KernelArgs& g, const DmaTile& d, int q, int wave, int lane) {
+    constexpr int ES = C::ES;
+    if (q < C::A_INSTR) {
+        int row, kel;
+        a_chunk<C>(wave, lane, q, row, kel);
+        const bool ok = row < d.rows_left && kel < d.k_left;
+        dma16(d.ra, ok ? (uint32_t)(row * (int)g.lda + kel) * ES : OOB, d.sa + (uint32_t)q * 1024u);
+    } else {
+        const int qb = q - C::A_INSTR;
+        int krow, nel;
+        b_chunk<C>(wave, lane, qb, krow, nel);
+        const bool ok = krow < d.k_left && nel < d.n_left;
+        dma16(d.rb, ok ? (uint32_t)(krow * (int)g.ldb + nel) * ES : OOB, d.sb + (uint32_t)qb * 1024u);
+    }
+}
+
 // Issue the global loads of K tile `kt`: DIRECT straight into LDS stage
 // `stage`, the other producers into the staging registers.  Lanes whose
 // chunk lies outside the matrix get offset 2^31 and receive zeros.
@@ -280,24 +324,9 @@ __device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, 
     const char* b_base = (const char*)g.B + ((int64_t)k0 * g.ldb + n0) * ES;
     const int rows_left = g.M - m0, k_left = g.K - k0, n_left = g.N - n0;
     if constexpr (C::P == PROD_DIRECT) {
-        const i32x4 ra = make_rsrc_sgpr(a_base);
-        const i32x4 rb = make_rsrc_sgpr(b_base);
-        const uint32_t sa = (uint32_t)(size_t)stage + (uint32_t)(wave * C::A_INSTR) * 1024u;
-        const uint32_t sb = (uint32_t)(size_t)stage + (uint32_t)C::A_BYTES + (uint32_t)(wave * C::B_INSTR) * 1024u;
+        const DmaTile d = dma_setup<C>(g, m0, n0, kt, stage, wave);
 #pragma unroll
-        for (int q = 0; q < C::A_INSTR; ++q) {
-            int row, kel;
-            a_chunk<C>(wave, lane, q, row, kel);
-            const bool ok = row < rows_left && kel < k_left;
-            dma16(ra, ok ? (uint32_t)(row * (int)g.lda + kel) * ES : OOB, sa + q * 1024u);
-        }
-#pragma unroll
-        for (int q = 0; q < C::B_INSTR; ++q) {
-            int krow, nel;
-            b_chunk<C>(wave, lane, q, krow, nel);
-            const bool ok = krow < k_left && nel < n_left;
-            dma16(rb, ok ? (uint32_t)(krow * (int)g.ldb + nel) * ES : OOB, sb + q * 1024u);
-        }
+        for (int q = 0; q < C::LPS; ++q) dma_piece<C>(g, d, q, wave, lane);
     } else {
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base);
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base);
@@ -349,57 +378,81 @@ struct Frags {
 };
 
 template <class C>
-__device__ __forceinline__ void read_frags(const char PGEMM_LDS* stage, int ks, int wm0, int wn0, int lane,
-                                           Frags<C>& f) {
+__device__ __forceinline__ void read_a(const char PGEMM_LDS* stage, int ks, int i, int wm0, int lane, i32x4& out) {
+    out = *(const i32x4 PGEMM_LDS*)(stage + a_off<C::KC>(wm0 + 16 * i + (lane & 15), ks * 4 + (lane >> 4)));
+}
+
+template <class C>
+__device__ __forceinline__ void read_b(const char PGEMM_LDS* stage, int ks, int j, int wn0, int lane, i32x4& out) {
     constexpr int D = C::Dt;
     const int li = lane & 15, lg = lane >> 4;
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-        f.a[i] = *(const i32x4 PGEMM_LDS*)(stage + a_off<C::KC>(wm0 + 16 * i + li, ks * 4 + lg));
     const char PGEMM_LDS* bs = stage + C::A_BYTES;
     constexpr int ROWB = C::BN * C::ES;
+    const int nb = wn0 + 16 * j;  // first column of the 16-wide block
+    if constexpr (D == DT_F16 || D == DT_BF16) {
+        // ds_read_b64_tr_b16: lane i of a 16-lane block receives element
+        // i%4 of the 4-element row piece addressed by lane 4e + i/4
+        // (e = 0..3), so lane j addresses row kb + j/4, columns nb + 4*(j%4),
+        // and lane i ends up with B[kb + e][nb + i], e = 0..3.
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-        const int nb = wn0 + 16 * j;  // first column of the 16-wide block
-        if constexpr (D == DT_F16 || D == DT_BF16) {
-            // ds_read_b64_tr_b16: lane i of a 16-lane block receives element
-            // i%4 of the 4-element row piece addressed by lane 4e + i/4
-            // (e = 0..3), so lane j addresses row kb + j/4, columns nb + 4*(j%4),
-            // and lane i ends up with B[kb + e][nb + i], e = 0..3.
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int k = ks * C::KSTEP + 8 * lg + 4 * h + (li >> 2);
-                const int n = nb + 4 * (li & 3);
-                const int off = k * ROWB + (((n / C::EPC) ^ b_swz<D, C::NCH>(k)) << 4) + (n % C::EPC) * 2;
-                const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 PGEMM_LDS*)(bs + off));
-                const i32x2 w = __builtin_bit_cast(i32x2, v);
-                f.b[j][2 * h] = w[0];
-                f.b[j][2 * h + 1] = w[1];
-            }
-        } else if constexpr (D == DT_I8) {
-            // ds_read_b64_tr_b8: lane i receives byte i%8 of the 8-byte row
-            // piece addressed by lane 2e + i/8 (e = 0..7): lane j addresses row
-            // kb + j/2, columns nb + 8*(j%2).
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int k = ks * C::KSTEP + 16 * lg + 8 * h + (li >> 1);
-                const int n = nb + 8 * (li & 1);
-                const int off = k * ROWB + (((n / C::EPC) ^ b_swz<D, C::NCH>(k)) << 4) + (n % C::EPC);
-                const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 PGEMM_LDS*)(bs + off));
-                f.b[j][2 * h] = w[0];
-                f.b[j][2 * h + 1] = w[1];
-            }
-        } else {
-            // fp32: MFMA jm of the K step takes k = 4*lg + jm in lane group lg
-            // (element jm of the lane's A chunk), so lane l reads B[k][nb + l%16].
-#pragma unroll
-            for (int jm = 0; jm < 4; ++jm) {
-                const int k = ks * C::KSTEP + 4 * lg + jm;
-                const int n = nb + li;
-                const int off = k * ROWB + (((n / C::EPC) ^ b_swz<D, C::NCH>(k)) << 4) + (n % C::EPC) * 4;
-                f.b[j][jm] = *(const int PGEMM_LDS*)(bs + off);
-            }
+        for (int h = 0; h < 2; ++h) {
+            const int k = ks * C::KSTEP + 8 * lg + 4 * h + (li >> 2);
+            const int n = nb + 4 * (li & 3);
+            const int off = k * ROWB + (((n / C::EPC) ^ b_swz<D, C::NCH>(k)) << 4) + (n % C::EPC) * 2;
+            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 PGEMM_LDS*)(bs + off));
+            const i32x2 w = __builtin_bit_cast(i32x2, v);
+            out[2 * h] = w[0];
+            out[2 * h + 1] = w[1];
         }
+    } else if constexpr (D == DT_I8) {
+        // ds_read_b64_tr_b8: lane i receives byte i%8 of the 8-byte row
+        // piece addressed by lane 2e + i/8 (e = 0..7): lane j addresses row
+        // kb + j/2, columns nb + 8*(j%2).
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = ks * C::KSTEP + 16 * lg + 8 * h + (li >> 1);
+            const int n = nb + 8 * (li & 1);
+            const int off = k * ROWB + (((n / C::EPC) ^ b_swz<D, C::NCH>(k)) << 4) + (n % C::EPC);
+            const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 PGEMM_LDS*)(bs + off));
+            out[2 * h] = w[0];
+            out[2 * h + 1] = w[1];
+        }
+    } else {
+        // fp32: MFMA jm of the K step takes k = 4*lg + jm in lane group lg
+        // (element jm of the lane's A chunk), so lane l reads B[k][nb + l%16].
+#pragma unroll
+        for (int jm = 0; jm < 4; ++jm) {
+            const int k = ks * C::KSTEP + 4 * lg + jm;
+            const int n = nb + li;
+            const int off = k * ROWB + (((n / C::EPC) ^ b_swz<D, C::NCH>(k)) << 4) + (n % C::EPC) * 4;
+            out[jm] = *(const int PGEMM_LDS*)(bs + off);
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void read_frags(const char PGEMM_LDS* stage, int ks, int wm0, int wn0, int lane,
+                                           Frags<C>& f) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) read_a<C>(stage, ks, i, wm0, lane, f.a[i]);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) read_b<C>(stage, ks, j, wn0, lane, f.b[j]);
+}
+
+// The r-th fragment read of a K step, in the order the MFMAs consume them
+// (MFMA blocks run row-major: block (i, j) needs a[i] and b[j]):
+// b0, a0, b1 .. b(FN-1), a1 .. a(FM-1).
+template <class C>
+__device__ __forceinline__ void read_item(const char PGEMM_LDS* stage, int ks, int r, int wm0, int wn0, int lane,
+                                          Frags<C>& f) {
+    if (r == 0) {
+        read_b<C>(stage, ks, 0, wn0, lane, f.b[0]);
+    } else if (r == 1) {
+        read_a<C>(stage, ks, 0, wm0, lane, f.a[0]);
+    } else if (r <= C::FN) {
+        read_b<C>(stage, ks, r - 1, wn0, lane, f.b[r - 1]);
+    } else {
+        read_a<C>(stage, ks, r - C::FN, wm0, lane, f.a[r - C::FN]);
     }
 }
 
@@ -436,81 +489,88 @@ __device__ __forceinline__ void mfma_all(typename C::T::Acc (&acc)[C::FM][C::FN]
 
 // ---- stage protocol -------------------------------------------------------------
 
-// Barrier B_t: the ready edge of tile t (its loads landed in every wave: at
-// most `pending` later tiles' loads may still be outstanding, since vector
-// loads retire in issue order) and the reuse edge of the stage the previous
-// tile occupied (every wave's LDS reads of it are complete: lgkmcnt(0)).
-template <class C>
-__device__ __forceinline__ void sync_ready(int pending) {
-    if constexpr (C::P == PROD_DIRECT) {
-        if constexpr (C::S >= 4) {
-            if (pending >= 2) {
-                wait_barrier<2 * C::LPS>();
-            } else if (pending == 1) {
-                wait_barrier<C::LPS>();
-            } else {
-                wait_barrier<0>();
-            }
-        } else if constexpr (C::S == 3) {
-            if (pending >= 1) {
-                wait_barrier<C::LPS>();
-            } else {
-                wait_barrier<0>();
-            }
-        } else {
-            wait_barrier<0>();
+// The MFMA work of one K step, cut into (up to) eight groups.  After each
+// group: one piece of the producer's work (an LDS-DMA block of the tile being
+// issued) and the next step's fragment reads, so none of that issue time
+// leaves the matrix pipe idle.  sched_barrier keeps the groups in this order.
+template <class C, bool READS, bool DMA>
+__device__ __forceinline__ void mfma_step(typename C::T::Acc (&acc)[C::FM][C::FN], const Frags<C>& use,
+                                          Frags<C>& nxt, const char PGEMM_LDS* rstage, int rks,
+                                          const KernelArgs& g, const DmaTile& d, int wave, int lane, int wm0,
+                                          int wn0) {
+    constexpr int NMF = C::FM * C::FN;
+    constexpr int NG = NMF < 8 ? NMF : 8;
+    constexpr int GS = NMF / NG;
+    constexpr int NR = C::FM + C::FN;
+    constexpr int RPG = (NR + NG - 1) / NG;
+    constexpr int NP = C::LPS;
+    constexpr int PPG = (NP + NG - 1) / NG;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+        for (int m = gi * GS; m < (gi + 1) * GS; ++m) mfma_block<C>(acc[m / C::FN][m % C::FN], use.a[m / C::FN], use.b[m % C::FN]);
+        if constexpr (DMA) {
+#pragma unroll
+            for (int p = gi * PPG; p < (gi + 1) * PPG; ++p)
+                if (p < NP) dma_piece<C>(g, d, p, wave, lane);
         }
-    } else {
-        // Register producers: the compiler waited for the loads before their
-        // ds_write; the writes themselves are covered by lgkmcnt(0).
-        lgkm_barrier();
+        if constexpr (READS) {
+#pragma unroll
+            for (int r = gi * RPG; r < (gi + 1) * RPG; ++r)
+                if (r < NR) read_item<C>(rstage, rks, r, wm0, wn0, lane, nxt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// Producer work right after B_t, into the stage freed by tile t-1.
-// DIRECT: issue tile t+S-1.  REGISTER/GENERIC: write tile t+S-1 (held in
-// registers since B_{t-1}) and start loading tile t+S.
+// Barrier of the uniform pipelined loop: every K-tile slot issues exactly
+// LPS loads (real, or all-out-of-range for slots past nK), so when tile t+1
+// must have landed the loads of the S-2 later slots may still be in flight.
 template <class C>
-__device__ __forceinline__ void produce_after_barrier(const KernelArgs& g, int m0, int n0, int t, int nK,
-                                                      char PGEMM_LDS* smem, int freed, Staging<C>& st, int wave,
-                                                      int lane) {
-    char PGEMM_LDS* stage = smem + freed * C::STAGE_BYTES;
+__device__ __forceinline__ void sync_ring() {
     if constexpr (C::P == PROD_DIRECT) {
-        if (t + C::S - 1 < nK) issue_tile<C>(g, m0, n0, t + C::S - 1, stage, st, wave, lane);
+        wait_barrier<C::LPS * (C::S - 2)>();
     } else {
-        if (t + C::S - 1 < nK) store_tile<C>(stage, st, wave, lane);
-        if (t + C::S < nK) issue_tile<C>(g, m0, n0, t + C::S, stage, st, wave, lane);
+        lgkm_barrier();
     }
 }
 
 // One K tile of the S >= 2 pipeline.  Fragments for K step ks+1 are read
 // while the MFMAs of step ks run; for the tile's last step the next reads
-// belong to tile t+1, so B_{t+1} and the producer's issue sit right before
-// them -- after the last LDS reads of tile t and before its last MFMAs.
+// belong to tile t+1, so barrier B_{t+1} and the producer's issue sit right
+// before them -- after the last LDS reads of tile t and before its last
+// MFMAs.  The body is the same for every t: slots past the last K tile load
+// nothing (every lane out of range, zeros land in a stage nobody reads), so
+// the loop has no drain branches and the wait count is a constant.
 // PAR is the fragment buffer holding step 0 of this tile.
 template <class C, int PAR>
-__device__ __forceinline__ void tile_body(const KernelArgs& g, int m0, int n0, int t, int nK, char PGEMM_LDS* smem,
-                                          int& cur, Staging<C>& st, Frags<C> (&f)[2],
+__device__ __forceinline__ void tile_body(const KernelArgs& g, int m0, int n0, int t, char PGEMM_LDS* smem, int& cur,
+                                          Staging<C>& st, Frags<C> (&f)[2],
                                           typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane, int wm0,
                                           int wn0) {
     constexpr int NKS = C::BK / C::KSTEP;
     const char PGEMM_LDS* cstage = smem + cur * C::STAGE_BYTES;
     const int nstage = (cur + 1 == C::S) ? 0 : cur + 1;
+    const DmaTile none{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
         Frags<C>& use = f[(PAR + ks) & 1];
         Frags<C>& nxt = f[(PAR + ks + 1) & 1];
-        // The reads of `use` were issued a whole step ago; saying so lets the
-        // MFMAs below start without waiting on the reads issued next.
-        lgkm_drain();
         if (ks + 1 < NKS) {
-            read_frags<C>(cstage, ks + 1, wm0, wn0, lane, nxt);
-        } else if (t + 1 < nK) {
-            sync_ready<C>(min(C::S - 2, nK - 2 - t));                                   // B_{t+1}
-            produce_after_barrier<C>(g, m0, n0, t + 1, nK, smem, cur, st, wave, lane);  // stage of tile t is free
-            read_frags<C>(smem + nstage * C::STAGE_BYTES, 0, wm0, wn0, lane, nxt);
+            mfma_step<C, true, false>(acc, use, nxt, cstage, ks + 1, g, none, wave, lane, wm0, wn0);
+        } else {
+            sync_ring<C>();  // B_{t+1}: tile t+1 ready, stage of tile t free
+            const char PGEMM_LDS* rstage = smem + nstage * C::STAGE_BYTES;
+            char PGEMM_LDS* freed = smem + cur * C::STAGE_BYTES;
+            if constexpr (C::P == PROD_DIRECT) {
+                const DmaTile d = dma_setup<C>(g, m0, n0, t + C::S, freed, wave);  // tile t+S (maybe none)
+                mfma_step<C, true, true>(acc, use, nxt, rstage, 0, g, d, wave, lane, wm0, wn0);
+            } else {
+                store_tile<C>(freed, st, wave, lane);                      // tile t+S, loaded since B_t
+                issue_tile<C>(g, m0, n0, t + C::S + 1, freed, st, wave, lane);  // tile t+S+1 into registers
+                mfma_step<C, true, false>(acc, use, nxt, rstage, 0, g, none, wave, lane, wm0, wn0);
+            }
         }
-        mfma_all<C>(acc, use);
     }
     cur = nstage;
 }
@@ -522,30 +582,35 @@ __device__ __forceinline__ void pipelined_loop(const KernelArgs& g, int m0, int 
     constexpr int NKS = C::BK / C::KSTEP;
     Staging<C> st;
     Frags<C> f[2];
-    // Prologue: tiles 0 .. S-2 into stages 0 .. S-2, never past nK.
+    // Prologue: K-tile slots 0 .. S-2 into stages 0 .. S-2 (slots >= nK load nothing).
 #pragma unroll
     for (int p = 0; p < C::S - 1; ++p) {
-        if (p < nK) {
-            issue_tile<C>(g, m0, n0, p, smem + p * C::STAGE_BYTES, st, wave, lane);
-            if constexpr (C::P != PROD_DIRECT) store_tile<C>(smem + p * C::STAGE_BYTES, st, wave, lane);
-        }
+        issue_tile<C>(g, m0, n0, p, smem + p * C::STAGE_BYTES, st, wave, lane);
+        if constexpr (C::P != PROD_DIRECT) store_tile<C>(smem + p * C::STAGE_BYTES, st, wave, lane);
     }
-    if constexpr (C::P != PROD_DIRECT) {
-        if (C::S - 1 < nK) issue_tile<C>(g, m0, n0, C::S - 1, smem, st, wave, lane);
+    if constexpr (C::P != PROD_DIRECT) issue_tile<C>(g, m0, n0, C::S - 1, smem, st, wave, lane);
+    sync_ring<C>();  // B_0
+    // Stage S-1 has never been used: slot S-1 goes there now.
+    if constexpr (C::P == PROD_DIRECT) {
+        issue_tile<C>(g, m0, n0, C::S - 1, smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
+    } else {
+        store_tile<C>(smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
+        issue_tile<C>(g, m0, n0, C::S, smem, st, wave, lane);
     }
-    sync_ready<C>(min(C::S - 2, nK - 1));                                      // B_0
-    produce_after_barrier<C>(g, m0, n0, 0, nK, smem, C::S - 1, st, wave, lane);  // stage S-1 was never used
     read_frags<C>(smem, 0, wm0, wn0, lane, f[0]);
     int cur = 0;
     if constexpr (NKS % 2 == 0) {
-        for (int t = 0; t < nK; ++t)
-            tile_body<C, 0>(g, m0, n0, t, nK, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+        for (int t = 0; t < nK; ++t) tile_body<C, 0>(g, m0, n0, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
     } else {
-        for (int t = 0; t < nK; t += 2) {
-            tile_body<C, 0>(g, m0, n0, t, nK, smem, cur, st, f, acc, wave, lane, wm0, wn0);
-            if (t + 1 < nK) tile_body<C, 1>(g, m0, n0, t + 1, nK, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+        int t = 0;
+        for (; t + 1 < nK; t += 2) {
+            tile_body<C, 0>(g, m0, n0, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+            tile_body<C, 1>(g, m0, n0, t + 1, smem, cur, st, f, acc, wave, lane, wm0, wn0);
         }
+        if (t < nK) tile_body<C, 0>(g, m0, n0, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
     }
+    // No load may still be writing LDS when the workgroup retires.
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 // MFMA work on one stage with the fragments of step ks+1 read under step ks.

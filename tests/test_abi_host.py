@@ -1,0 +1,155 @@
+"""Host-only checks of the C ABI (no GPU needed).
+
+* libpgemm.so loads and exports every function include/pgemm.h declares;
+* argument errors come back before anything is launched;
+* planner invariants: LDS ring within 160 KiB, effective depth clipped to the
+  number of K tiles, explicit depths honoured or refused, misaligned data
+  routed to the element-wise producer;
+* the planner's models reproduce the figures the pages print
+  (tests/golden/page_models.json).
+"""
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+from software_pipelined_tiled_loop_amd import binding as lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pgemm.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "page_models.json")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(pgemm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("pgemm_gemm", "pgemm_gemm_ex", "pgemm_plan", "pgemm_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", lib.LIB_PATH], stdout=subprocess.PIPE, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s(\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(lib._lib, n)
+    assert set(lib.EXPORTED) <= set(names)
+
+
+FAKE = 1 << 20  # never dereferenced: every case below fails validation first
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(dtype=7), -2),
+    (dict(stages=5), -3),
+    (dict(stages=-1), -3),
+    (dict(M=-1), -1),
+    (dict(lda=7), -1),
+    (dict(ldb=3), -1),
+    (dict(ldc=3), -1),
+    (dict(dtype="i8", alpha=0.5), -5),
+    (dict(dtype="i8", beta=float("nan")), -5),
+    (dict(dtype="i8", alpha=2.0 ** 40), -5),
+    (dict(A=None), -1),
+    (dict(C=None), -1),
+    (dict(lda=1 << 26, dtype="f32"), -7),
+    (dict(A=FAKE + 1, dtype="f32"), -1),   # not element aligned
+])
+def test_argument_errors_before_any_launch(args, code):
+    a = dict(M=8, N=8, K=8, alpha=1.0, A=FAKE, lda=8, B=FAKE, ldb=8, beta=0.0, C=FAKE, ldc=8, dtype="bf16",
+             stages=0)
+    a.update(args)
+    r = lib._lib.pgemm_gemm(a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"], a["B"], a["ldb"], a["beta"],
+                            a["C"], a["ldc"], lib.DTYPE_CODE.get(a["dtype"], a["dtype"]), a["stages"], None)
+    assert r == code, (args, r, lib.pgemm_strerror(r))
+
+
+def test_empty_problems_are_noops():
+    assert lib._lib.pgemm_gemm(0, 8, 8, 1.0, None, 8, None, 8, 0.0, None, 8, 2, 0, None) == 0
+    assert lib._lib.pgemm_gemm(8, 0, 8, 1.0, None, 8, None, 8, 0.0, None, 8, 2, 0, None) == 0
+
+
+def test_strerror_covers_every_status():
+    for code in range(0, -8, -1):
+        assert lib.pgemm_strerror(code) != "unknown status"
+    assert lib.pgemm_strerror(-99) == "unknown status"
+
+
+def all_variants():
+    return [lib.pgemm_variant_info(i) for i in range(lib.pgemm_num_variants())]
+
+
+def test_variant_table_invariants():
+    es = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
+    vs = all_variants()
+    assert len(vs) >= 40
+    for v in vs:
+        assert v["lds_bytes"] <= 163840
+        assert v["lds_bytes"] == lib.pgemm_model_lds_bytes(v["tile_m"], v["tile_n"], v["tile_k"], v["stages"],
+                                                           es[v["dtype"]], 0)
+        assert 1 <= v["stages"] <= 4
+        assert v["threads"] == 64 * v["waves_m"] * v["waves_n"]
+    # every dtype offers 1..4 stages and both vector producers somewhere
+    for dt in es:
+        mine = [v for v in vs if v["dtype"] == dt]
+        assert {v["stages"] for v in mine} == {1, 2, 3, 4}
+        assert {"direct", "register", "generic"} <= {v["producer"] for v in mine}
+    # the pages' SGEMM tile class exists with 1 and 2 stages
+    page = [v for v in vs if v["dtype"] == "f32" and (v["tile_m"], v["tile_n"], v["tile_k"]) == (128, 64, 16)]
+    assert {1, 2} <= {v["stages"] for v in page}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_planner_clips_depth_to_k_tiles(dtype):
+    for K in (1, 16, 32, 64, 100, 256, 4096, 16384):
+        r, p = lib.pgemm_plan(4096, 4096, K, dtype, 0, 1)
+        assert r == 0
+        assert p["stages"] <= max(p["num_k_tiles"], 1)
+        assert p["stages_eff"] == min(p["stages"], max(p["num_k_tiles"], 1))
+        assert p["lds_bytes"] <= 163840
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_planner_honours_explicit_depth(dtype):
+    for S in (1, 2, 3, 4):
+        r, p = lib.pgemm_plan(1024, 1024, 2048, dtype, S, 1)
+        assert r == 0 and p["stages"] == S
+    r, _ = lib.pgemm_plan(1024, 1024, 2048, dtype, 0, 0, {"producer": "direct"})
+    assert r == -4  # the direct producer needs the 16-byte rules
+    r, p = lib.pgemm_plan(1024, 1024, 2047, dtype, 0, 0)
+    assert r == 0 and p["producer"] == "generic"
+    r, _ = lib.pgemm_plan(1024, 1024, 2048, dtype, 0, 1, {"tile": (8, 8, 8)})
+    assert r == -4
+
+
+def test_planner_prefers_big_tiles_for_big_problems_and_small_for_small():
+    r, big = lib.pgemm_plan(4096, 4096, 4096, "bf16", 0, 1)
+    r2, small = lib.pgemm_plan(512, 512, 4096, "bf16", 0, 1)
+    assert r == 0 and r2 == 0
+    assert big["tile_m"] * big["tile_n"] >= small["tile_m"] * small["tile_n"]
+    assert small["grid"] >= 16
+
+
+def test_page_models_golden():
+    g = json.load(open(GOLDEN))
+    u = g["uncovered_cycles_two_stages"]
+    assert lib.pgemm_model_uncovered_cycles(u["latency"], u["compute_per_tile"], u["stages"]) == u["expected"]
+    # deeper rings cover more of the same latency; a single buffer covers none of it
+    assert lib.pgemm_model_uncovered_cycles(500, 220, 4) == 0
+    assert lib.pgemm_model_uncovered_cycles(500, 220, 1) == 500
+    q = g["global_loads_per_output_128x64_K4096"]
+    assert lib.pgemm_model_global_loads_per_output(q["bm"], q["bn"], q["K"]) == q["expected"]
+    for key in ("page_kernel_lds_bytes", "page_kernel_single_buffer_lds_bytes"):
+        s = g[key]
+        assert lib.pgemm_model_lds_bytes(s["bm"], s["bn"], s["bk"], s["stages"], s["elem_bytes"],
+                                         s["a_pad_elems_per_k"]) == s["expected"]
