@@ -45,10 +45,11 @@ WORKLOADS = {
 
 
 def kernel_source_hash() -> str:
+    """Hash of the files that define the kernels (not the host planner)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "software_pipelined_tiled_loop_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
+        if f.endswith((".hip", ".hpp")):
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 

@@ -1,0 +1,240 @@
+"""Model check of the LDS stage protocol (host only).
+
+Page "Software pipelines and asynchronous copies" (section "Producer-consumer
+synchronization") gives each stage two transitions: after the producer
+finishes writing it, consumers may read it (ready); after every consumer
+finishes reading it, the producer may overwrite it (reuse).  Section
+"Prologue, steady state, and epilogue" adds that the prologue must not run
+past K and the epilogue must not consume a stage whose load was not waited
+for.
+
+This test replays the event sequence of the kernel's K loop (the functions
+pipelined_loop / tile_body / single_buffer_loop of pgemm_kernel.hpp) for
+every producer, ring depth S = 1..4, K steps per tile NKS = 1..2 and number of
+K tiles nK = 0..12, and checks, for a workgroup of waves that all run the
+same program and meet only at barriers:
+
+  ready   every read of a stage sees the tile the step expects; that tile's
+          load was waited for (vector loads retire in issue order, so a wait
+          with P pending groups completes all but the last P) or written by
+          ds_write, and a barrier lies between that and the read;
+  reuse   between any read of a stage and a later load into it there is a
+          barrier (our barriers drain LDS reads first), and the stage's
+          previous load had completed (no two loads race into one stage);
+  order   every K tile is multiplied exactly once, its steps in order, from
+          fragments read after its ready edge; no real load targets a tile
+          >= nK; nothing is in flight when the workgroup ends.
+"""
+import itertools
+
+import pytest
+
+
+class Trace:
+    def __init__(self, nK):
+        self.nK = nK
+        self.ev = []          # (kind, ...) in program order
+
+    def issue(self, tile, stage, direct):
+        # direct: an LDS-DMA group into the stage; else a register load (no LDS effect)
+        self.ev.append(("issue", tile, stage if direct else None, tile < self.nK))
+
+    def write(self, tile, stage):
+        self.ev.append(("write", tile, stage, tile < self.nK))
+
+    def wait(self, pending):
+        self.ev.append(("wait", pending))
+
+    def barrier(self):
+        self.ev.append(("barrier",))
+
+    def read(self, stage, tile, ks):
+        self.ev.append(("read", stage, tile, ks))
+
+    def mfma(self, tile, ks):
+        self.ev.append(("mfma", tile, ks))
+
+    def waitall(self):
+        self.ev.append(("wait", 0))
+
+
+# ---- the kernel's control flow, event by event -------------------------------
+
+def pipelined_loop(S, NKS, nK, direct):
+    tr = Trace(nK)
+    for p in range(S - 1):                       # prologue slots 0..S-2
+        tr.issue(p, p, direct)
+        if not direct:
+            tr.write(p, p)
+    if not direct:
+        tr.issue(S - 1, None, False)             # slot S-1 into registers
+    sync_ring(tr, S, direct)                     # B_0
+    if direct:
+        tr.issue(S - 1, S - 1, True)             # stage S-1 never used before
+    else:
+        tr.write(S - 1, S - 1)
+        tr.issue(S, None, False)
+    tr.read(0, 0, 0)
+    cur = 0
+    for t in range(nK):
+        nstage = (cur + 1) % S
+        for ks in range(NKS):
+            if ks + 1 < NKS:
+                tr.read(cur, t, ks + 1)
+            else:
+                sync_ring(tr, S, direct)         # B_{t+1}
+                if direct:
+                    tr.issue(t + S, cur, True)
+                else:
+                    tr.write(t + S, cur)
+                    tr.issue(t + S + 1, None, False)
+                tr.read(nstage, t + 1, 0)
+            tr.mfma(t, ks)
+        cur = nstage
+    tr.waitall()
+    return tr
+
+
+def sync_ring(tr, S, direct):
+    if direct:
+        tr.wait(S - 2)
+    tr.barrier()
+
+
+def single_buffer_loop(NKS, nK, direct):
+    tr = Trace(nK)
+    if direct:
+        for t in range(nK):
+            tr.issue(t, 0, True)
+            tr.wait(0)
+            tr.barrier()
+            for ks in range(NKS):
+                tr.read(0, t, ks)
+                tr.mfma(t, ks)
+            tr.barrier()
+    else:
+        if nK > 0:
+            tr.issue(0, None, False)
+            tr.write(0, 0)
+        for t in range(nK):
+            tr.barrier()
+            more = t + 1 < nK
+            if more:
+                tr.issue(t + 1, None, False)
+            for ks in range(NKS):
+                tr.read(0, t, ks)
+                tr.mfma(t, ks)
+            tr.barrier()
+            if more:
+                tr.write(t + 1, 0)
+    tr.waitall()
+    return tr
+
+
+def kernel_trace(S, NKS, nK, direct):
+    if nK == 0:
+        return Trace(0)                          # the kernel skips the loop
+    if S == 1:
+        return single_buffer_loop(NKS, nK, direct)
+    return pipelined_loop(S, NKS, nK, direct)
+
+
+# ---- the checker ----------------------------------------------------------------
+
+def check(tr, S, NKS):
+    ev = tr.ev
+    dma = []                 # (position, tile, stage) of DMA groups in issue order
+    completed = set()        # indexes into dma known complete
+    stage_content = {}       # stage -> (tile, position of the load/write, kind)
+    reads_since = {}         # stage -> positions of reads of its current content
+    last_barrier = -1
+    read_ok = {}             # (tile, ks) -> position of a valid read
+    consumed = []
+    for pos, e in enumerate(ev):
+        kind = e[0]
+        if kind == "barrier":
+            last_barrier = pos
+        elif kind == "wait":
+            pending = e[1]
+            for i in range(len(dma) - pending):
+                completed.add(i)
+        elif kind in ("issue", "write"):
+            tile, stage, real = e[1], e[2], e[3]
+            if kind == "issue" and stage is None:
+                continue                          # register load: no LDS effect yet
+            if kind == "issue":
+                dma.append((pos, tile, stage))
+            # reuse edge: every read of the stage's current content precedes a barrier before us
+            for rp in reads_since.get(stage, []):
+                assert rp < last_barrier, "stage %d overwritten at %d while read at %d" % (stage, pos, rp)
+            prev = stage_content.get(stage)
+            if prev is not None and prev[2] == "issue":
+                i = [k for k, d in enumerate(dma) if d[0] == prev[1]][0]
+                assert i in completed, "stage %d re-filled before its previous load completed" % stage
+            stage_content[stage] = (tile, pos, kind)
+            reads_since[stage] = []
+        elif kind == "read":
+            stage, tile, ks = e[1], e[2], e[3]
+            content = stage_content.get(stage)
+            if tile >= tr.nK:
+                continue                          # look-ahead read past the last tile: never multiplied
+            assert content is not None and content[0] == tile, \
+                "read of stage %d expects tile %d, holds %s" % (stage, tile, content)
+            # ready edge
+            if content[2] == "issue":
+                i = [k for k, d in enumerate(dma) if d[0] == content[1]][0]
+                assert i in completed, "tile %d read before its load was waited for" % tile
+                waits = [p for p in range(content[1], pos) if ev[p][0] == "wait"]
+                assert waits, "no wait between load and read of tile %d" % tile
+            assert last_barrier > content[1], "tile %d read without a barrier after its load/write" % tile
+            reads_since.setdefault(stage, []).append(pos)
+            read_ok[(tile, ks)] = pos
+        elif kind == "mfma":
+            tile, ks = e[1], e[2]
+            assert (tile, ks) in read_ok and read_ok[(tile, ks)] < pos, "MFMA on unread fragments %s" % ((tile, ks),)
+            consumed.append((tile, ks))
+    # order: each tile once, steps in order
+    assert consumed == [(t, k) for t in range(tr.nK) for k in range(NKS)]
+    # nothing in flight at the end
+    assert len(completed) == len(dma)
+    # no real load targets a tile >= nK
+    for e in ev:
+        if e[0] in ("issue", "write"):
+            assert e[3] == (e[1] < tr.nK)
+
+
+@pytest.mark.parametrize("direct", [True, False], ids=["direct", "register"])
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("NKS", [1, 2])
+def test_stage_protocol(direct, S, NKS):
+    for nK in range(0, 13):
+        check(kernel_trace(S, NKS, nK, direct), S, NKS)
+
+
+def test_checker_catches_a_missing_reuse_barrier():
+    """Sensitivity: drop the barrier before the producer's issue (the reuse
+    edge of the practice exercise on the second page) and the model fails."""
+    tr = kernel_trace(2, 1, 6, True)
+    ev = tr.ev
+    # remove the second barrier B_1 (ready of tile 1 and reuse of stage 0)
+    idx = [i for i, e in enumerate(ev) if e[0] == "barrier"][1]
+    del ev[idx]
+    with pytest.raises(AssertionError):
+        check(tr, 2, 1)
+
+
+def test_checker_catches_a_short_wait():
+    """Sensitivity: waiting for one group fewer than needed breaks the ready edge."""
+    tr = kernel_trace(3, 1, 8, True)
+    tr.ev = [("wait", e[1] + 1) if e[0] == "wait" and e[1] > 0 else e for e in tr.ev]
+    with pytest.raises(AssertionError):
+        check(tr, 3, 1)
+
+
+def test_checker_catches_a_forgotten_epilogue_tile():
+    """Sensitivity: skipping the last tile's MFMAs (page "GPU-Kernel
+    pipelinen", common pitfalls) is caught by the order check."""
+    tr = kernel_trace(2, 2, 5, True)
+    tr.ev = [e for e in tr.ev if not (e[0] == "mfma" and e[1] == 4)]
+    with pytest.raises(AssertionError):
+        check(tr, 2, 2)
