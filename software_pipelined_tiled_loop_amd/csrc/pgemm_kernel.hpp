@@ -152,21 +152,51 @@ __device__ __forceinline__ void lgkm_barrier() {
 }
 
 // ---- LDS swizzles --------------------------------------------------------
-// A: rows of KC 16-byte chunks.  Chunk index L = row*KC + kc is placed in
-// 128-byte line L/8 at slot (L%8) ^ p(line), p(line) = (line%8) ^ ((line/8)%2):
-// 8 consecutive rows (and 16 rows for 256-byte LDS cycles) read by one
-// ds_read_b128 land on distinct banks.
+// A: rows of KC 16-byte chunks, read by ds_read_b128 fragments that touch 16
+// consecutive rows at 4 consecutive chunks.  Measured on gfx950 (per-variant
+// SQ_LDS_BANK_CONFLICT), the LDS serves a ds_read_b128 16 lanes per cycle
+// across 64 banks (256 bytes), grouping lanes that share lane-id bits 0 and
+// 5: eight rows of one parity at two adjacent chunks.
+//  * 64-byte rows (KC = 4): chunk L = row*KC + kc sits in 128-byte line L/8
+//    at slot (L%8) ^ (line%8) ^ (line/8 %2) -- conflict-free.
+//  * 128-byte rows (KC = 8): rows of one parity would all fall in the same
+//    half of the 256-byte bank window (a 2-way conflict for any XOR inside a
+//    line), so the swizzle works on 256-byte super-lines of two rows: slot
+//    ((row%2)*8 + kc) ^ 2*(superline%8).  This removed the 2-way conflict
+//    (8 -> 4 LDS cycles per fragment read).
+#define PGEMM_HD __host__ __device__ __forceinline__
+
 template <int KC>
-__device__ __forceinline__ constexpr int a_off(int row, int kc) {
-    const int L = row * KC + kc;
-    const int line = L >> 3;
-    const int p = (line & 7) ^ ((line >> 3) & 1);
-    return (line << 7) + ((((L & 7) ^ p)) << 4);
+PGEMM_HD constexpr int a_off(int row, int kc) {
+    if constexpr (KC == 8) {
+        const int sl = row >> 1;
+        const int u = ((row & 1) << 3) + kc;
+        return (sl << 8) + ((u ^ ((sl & 7) << 1)) << 4);
+    } else {
+        const int L = row * KC + kc;
+        const int line = L >> 3;
+        return (line << 7) + ((((L & 7) ^ (line & 7) ^ ((line >> 3) & 1))) << 4);
+    }
+}
+// Inverse of a_off: the (row, chunk) stored at LDS byte `off` of the A region.
+template <int KC>
+PGEMM_HD void a_inv(int off, int& row, int& kc) {
+    if constexpr (KC == 8) {
+        const int sl = off >> 8;
+        const int u = ((off >> 4) & 15) ^ ((sl & 7) << 1);
+        row = (sl << 1) + (u >> 3);
+        kc = u & 7;
+    } else {
+        const int line = off >> 7;
+        const int L = (line << 3) + (((off >> 4) & 7) ^ (line & 7) ^ ((line >> 3) & 1));
+        row = L / KC;
+        kc = L % KC;
+    }
 }
 // B: rows k of NCH chunks; chunk c of row k sits at c ^ pb(k).  pb spreads the
 // rows that one transposing read touches over distinct banks.
 template <int D, int NCH>
-__device__ __forceinline__ constexpr int b_swz(int k) {
+PGEMM_HD constexpr int b_swz(int k) {
     if constexpr (D == DT_I8) {
         return ((k & 7) + (((k >> 4) & 1) << 3)) & (NCH - 1);
     } else if constexpr (D == DT_F32) {
@@ -214,18 +244,14 @@ struct Cfg {
 // the chunk is (wave*A_INSTR + q)*1024 + 16*lane within the stage's A region;
 // returns the (row, first element k) of global memory that belongs there.
 template <class C>
-__device__ __forceinline__ void a_chunk(int wave, int lane, int q, int& row, int& kel) {
-    const int lds_off = (wave * C::A_INSTR + q) * 1024 + lane * 16;
-    const int line = lds_off >> 7;
-    const int slot = (lds_off >> 4) & 7;
-    const int p = (line & 7) ^ ((line >> 3) & 1);
-    const int L = (line << 3) + (slot ^ p);
-    row = L / C::KC;
-    kel = (L % C::KC) * C::EPC;
+PGEMM_HD void a_chunk(int wave, int lane, int q, int& row, int& kel) {
+    int kc;
+    a_inv<C::KC>((wave * C::A_INSTR + q) * 1024 + lane * 16, row, kc);
+    kel = kc * C::EPC;
 }
 // Same for the B tile: (row k, first element n).
 template <class C>
-__device__ __forceinline__ void b_chunk(int wave, int lane, int q, int& krow, int& nel) {
+PGEMM_HD void b_chunk(int wave, int lane, int q, int& krow, int& nel) {
     const int lds_off = (wave * C::B_INSTR + q) * 1024 + lane * 16;
     krow = lds_off / (C::BN * C::ES);
     const int pc = (lds_off % (C::BN * C::ES)) >> 4;
@@ -377,56 +403,72 @@ struct Frags {
     i32x4 b[C::FN];  // fp32: the B values of the four MFMAs of a K step
 };
 
+// LDS byte offset (within the stage's A region) of lane `lane`'s 16-byte A
+// fragment for K step ks and 16-row block i of the wave.
+template <class C>
+PGEMM_HD int a_frag_off(int ks, int i, int wm0, int lane) {
+    return a_off<C::KC>(wm0 + 16 * i + (lane & 15), ks * 4 + (lane >> 4));
+}
+
+// LDS byte offset (within the stage's B region) that lane `lane` addresses
+// for B block j: h selects the half (0/1) of a 16-bit / 8-bit fragment
+// (two transposing reads), or the MFMA jm (0..3) of an fp32 K step.
+//  * ds_read_b64_tr_b16: lane i of a 16-lane block receives element i%4 of
+//    the 4-element row piece addressed by lane 4e + i/4 (e = 0..3), so lane
+//    j addresses row kb + j/4, columns nb + 4*(j%4), and lane i ends up with
+//    B[kb + e][nb + i], e = 0..3.
+//  * ds_read_b64_tr_b8: lane i receives byte i%8 of the 8-byte row piece
+//    addressed by lane 2e + i/8 (e = 0..7): lane j addresses row kb + j/2,
+//    columns nb + 8*(j%2).
+//  * fp32: MFMA jm of the K step takes k = 4*lg + jm in lane group lg
+//    (element jm of the lane's A chunk), so lane l reads B[k][nb + l%16].
+template <class C>
+PGEMM_HD int b_frag_off(int ks, int j, int wn0, int lane, int h) {
+    constexpr int D = C::Dt;
+    constexpr int ROWB = C::BN * C::ES;
+    const int li = lane & 15, lg = lane >> 4;
+    const int nb = wn0 + 16 * j;
+    int k, n;
+    if constexpr (D == DT_F16 || D == DT_BF16) {
+        k = ks * C::KSTEP + 8 * lg + 4 * h + (li >> 2);
+        n = nb + 4 * (li & 3);
+    } else if constexpr (D == DT_I8) {
+        k = ks * C::KSTEP + 16 * lg + 8 * h + (li >> 1);
+        n = nb + 8 * (li & 1);
+    } else {
+        k = ks * C::KSTEP + 4 * lg + h;
+        n = nb + li;
+    }
+    return k * ROWB + (((n / C::EPC) ^ b_swz<D, C::NCH>(k)) << 4) + (n % C::EPC) * C::ES;
+}
+
 template <class C>
 __device__ __forceinline__ void read_a(const char PGEMM_LDS* stage, int ks, int i, int wm0, int lane, i32x4& out) {
-    out = *(const i32x4 PGEMM_LDS*)(stage + a_off<C::KC>(wm0 + 16 * i + (lane & 15), ks * 4 + (lane >> 4)));
+    out = *(const i32x4 PGEMM_LDS*)(stage + a_frag_off<C>(ks, i, wm0, lane));
 }
 
 template <class C>
 __device__ __forceinline__ void read_b(const char PGEMM_LDS* stage, int ks, int j, int wn0, int lane, i32x4& out) {
     constexpr int D = C::Dt;
-    const int li = lane & 15, lg = lane >> 4;
     const char PGEMM_LDS* bs = stage + C::A_BYTES;
-    constexpr int ROWB = C::BN * C::ES;
-    const int nb = wn0 + 16 * j;  // first column of the 16-wide block
     if constexpr (D == DT_F16 || D == DT_BF16) {
-        // ds_read_b64_tr_b16: lane i of a 16-lane block receives element
-        // i%4 of the 4-element row piece addressed by lane 4e + i/4
-        // (e = 0..3), so lane j addresses row kb + j/4, columns nb + 4*(j%4),
-        // and lane i ends up with B[kb + e][nb + i], e = 0..3.
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int k = ks * C::KSTEP + 8 * lg + 4 * h + (li >> 2);
-            const int n = nb + 4 * (li & 3);
-            const int off = k * ROWB + (((n / C::EPC) ^ b_swz<D, C::NCH>(k)) << 4) + (n % C::EPC) * 2;
-            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 PGEMM_LDS*)(bs + off));
+            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 PGEMM_LDS*)(bs + b_frag_off<C>(ks, j, wn0, lane, h)));
             const i32x2 w = __builtin_bit_cast(i32x2, v);
             out[2 * h] = w[0];
             out[2 * h + 1] = w[1];
         }
     } else if constexpr (D == DT_I8) {
-        // ds_read_b64_tr_b8: lane i receives byte i%8 of the 8-byte row
-        // piece addressed by lane 2e + i/8 (e = 0..7): lane j addresses row
-        // kb + j/2, columns nb + 8*(j%2).
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int k = ks * C::KSTEP + 16 * lg + 8 * h + (li >> 1);
-            const int n = nb + 8 * (li & 1);
-            const int off = k * ROWB + (((n / C::EPC) ^ b_swz<D, C::NCH>(k)) << 4) + (n % C::EPC);
-            const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 PGEMM_LDS*)(bs + off));
+            const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 PGEMM_LDS*)(bs + b_frag_off<C>(ks, j, wn0, lane, h)));
             out[2 * h] = w[0];
             out[2 * h + 1] = w[1];
         }
     } else {
-        // fp32: MFMA jm of the K step takes k = 4*lg + jm in lane group lg
-        // (element jm of the lane's A chunk), so lane l reads B[k][nb + l%16].
 #pragma unroll
-        for (int jm = 0; jm < 4; ++jm) {
-            const int k = ks * C::KSTEP + 4 * lg + jm;
-            const int n = nb + li;
-            const int off = k * ROWB + (((n / C::EPC) ^ b_swz<D, C::NCH>(k)) << 4) + (n % C::EPC) * 4;
-            out[jm] = *(const int PGEMM_LDS*)(bs + off);
-        }
+        for (int jm = 0; jm < 4; ++jm) out[jm] = *(const int PGEMM_LDS*)(bs + b_frag_off<C>(ks, j, wn0, lane, jm));
     }
 }
 

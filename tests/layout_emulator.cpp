@@ -1,0 +1,210 @@
+// Host emulation of the kernel's data path (no GPU): producer placement into
+// the LDS stage, fragment reads (ds_read_b128, the transposing ds_read_b64_tr
+// reads, ds_read_b32) and the MFMA lane layouts, using the kernel's own index
+// functions from pgemm_kernel.hpp.  For every tile class it checks that
+//   * the producer writes every byte of the stage exactly once,
+//   * every fragment read stays inside its region,
+//   * the emulated MFMA results equal a naive GEMM of the tile.
+// Lane semantics of the gfx950 instructions were probed in-bounds on the GPU:
+//   ds_read_b64_tr_b16: lane i (of a 16-lane block) element e <- element i%4
+//                       of the piece addressed by lane 4e + i/4
+//   ds_read_b64_tr_b8:  lane i byte e <- byte i%8 of lane 2e + i/8
+//   MFMA 16x16xK: A lane l holds row l%16, B lane l column l%16, K in lane
+//   groups l/16; D lane l holds rows 4*(l/16)+r, column l%16.
+// Prints "OK <n>" on success; exits non-zero on the first mismatch.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../software_pipelined_tiled_loop_amd/csrc/pgemm_kernel.hpp"
+
+using namespace pgemm;
+
+static uint32_t rng_state = 12345;
+static int small_int() {
+    rng_state = rng_state * 1664525u + 1013904223u;
+    return (int)((rng_state >> 24) % 7) - 3;
+}
+
+template <int D>
+static void encode(int v, uint8_t* dst) {
+    if constexpr (D == DT_F32) {
+        float f = (float)v;
+        memcpy(dst, &f, 4);
+    } else if constexpr (D == DT_BF16) {
+        float f = (float)v;
+        uint32_t u;
+        memcpy(&u, &f, 4);
+        uint16_t h = (uint16_t)(u >> 16);
+        memcpy(dst, &h, 2);
+    } else if constexpr (D == DT_F16) {
+        _Float16 h = (_Float16)v;
+        memcpy(dst, &h, 2);
+    } else {
+        int8_t b = (int8_t)v;
+        memcpy(dst, &b, 1);
+    }
+}
+template <int D>
+static int decode(const uint8_t* src) {
+    if constexpr (D == DT_F32) {
+        float f;
+        memcpy(&f, src, 4);
+        return (int)f;
+    } else if constexpr (D == DT_BF16) {
+        uint16_t h;
+        memcpy(&h, src, 2);
+        uint32_t u = (uint32_t)h << 16;
+        float f;
+        memcpy(&f, &u, 4);
+        return (int)f;
+    } else if constexpr (D == DT_F16) {
+        _Float16 h;
+        memcpy(&h, src, 2);
+        return (int)(float)h;
+    } else {
+        return (int)(int8_t)src[0];
+    }
+}
+
+#define FAIL(...)                                  \
+    do {                                           \
+        printf("FAIL %s: ", name);                 \
+        printf(__VA_ARGS__);                       \
+        printf("\n");                              \
+        exit(1);                                   \
+    } while (0)
+
+template <class C>
+static void emulate(const char* name) {
+    constexpr int D = C::Dt, ES = C::ES, EPC = C::EPC;
+    std::vector<int> A(C::BM * C::BK), B(C::BK * C::BN);
+    for (int& v : A) v = small_int();
+    for (int& v : B) v = small_int();
+    std::vector<uint8_t> lds(C::STAGE_BYTES, 0);
+    std::vector<int> hits(C::STAGE_BYTES / 16, 0);
+    // producer placement
+    for (int w = 0; w < C::NW; ++w)
+        for (int l = 0; l < 64; ++l) {
+            for (int q = 0; q < C::A_INSTR; ++q) {
+                int row, kel;
+                a_chunk<C>(w, l, q, row, kel);
+                const int off = (w * C::A_INSTR + q) * 1024 + l * 16;
+                if (row < 0 || row >= C::BM || kel < 0 || kel + EPC > C::BK) FAIL("A chunk out of tile");
+                for (int e = 0; e < EPC; ++e) encode<D>(A[row * C::BK + kel + e], &lds[off + e * ES]);
+                hits[off / 16]++;
+            }
+            for (int q = 0; q < C::B_INSTR; ++q) {
+                int krow, nel;
+                b_chunk<C>(w, l, q, krow, nel);
+                const int off = C::A_BYTES + (w * C::B_INSTR + q) * 1024 + l * 16;
+                if (krow < 0 || krow >= C::BK || nel < 0 || nel + EPC > C::BN) FAIL("B chunk out of tile");
+                for (int e = 0; e < EPC; ++e) encode<D>(B[krow * C::BN + nel + e], &lds[off + e * ES]);
+                hits[off / 16]++;
+            }
+        }
+    for (size_t i = 0; i < hits.size(); ++i)
+        if (hits[i] != 1) FAIL("LDS chunk %zu written %d times", i, hits[i]);
+    // consumer
+    std::vector<long> out(C::BM * C::BN, 0);
+    for (int w = 0; w < C::NW; ++w) {
+        const int wm0 = (w / C::WGN) * C::WM, wn0 = (w % C::WGN) * C::WN;
+        for (int ks = 0; ks < C::BK / C::KSTEP; ++ks)
+            for (int i = 0; i < C::FM; ++i)
+                for (int j = 0; j < C::FN; ++j) {
+                    // A fragment: EPC elements per lane
+                    int af[64][16], bf[64][16];
+                    for (int l = 0; l < 64; ++l) {
+                        const int off = a_frag_off<C>(ks, i, wm0, l);
+                        if (off < 0 || off + 16 > C::A_BYTES) FAIL("A read out of region");
+                        for (int e = 0; e < EPC; ++e) af[l][e] = decode<D>(&lds[off + e * ES]);
+                    }
+                    if constexpr (D == DT_F16 || D == DT_BF16) {
+                        for (int h = 0; h < 2; ++h) {
+                            int R[64][4];
+                            for (int l = 0; l < 64; ++l) {
+                                const int off = b_frag_off<C>(ks, j, wn0, l, h);
+                                if (off < 0 || off + 8 > C::B_BYTES) FAIL("B read out of region");
+                                for (int e = 0; e < 4; ++e) R[l][e] = decode<D>(&lds[C::A_BYTES + off + e * 2]);
+                            }
+                            for (int l = 0; l < 64; ++l)
+                                for (int e = 0; e < 4; ++e) {
+                                    const int i16 = l & 15, blk = l & ~15;
+                                    bf[l][4 * h + e] = R[blk + 4 * e + i16 / 4][i16 % 4];
+                                }
+                        }
+                    } else if constexpr (D == DT_I8) {
+                        for (int h = 0; h < 2; ++h) {
+                            int R[64][8];
+                            for (int l = 0; l < 64; ++l) {
+                                const int off = b_frag_off<C>(ks, j, wn0, l, h);
+                                if (off < 0 || off + 8 > C::B_BYTES) FAIL("B read out of region");
+                                for (int e = 0; e < 8; ++e) R[l][e] = decode<D>(&lds[C::A_BYTES + off + e]);
+                            }
+                            for (int l = 0; l < 64; ++l)
+                                for (int e = 0; e < 8; ++e) {
+                                    const int i16 = l & 15, blk = l & ~15;
+                                    bf[l][8 * h + e] = R[blk + 2 * e + i16 / 8][i16 % 8];
+                                }
+                        }
+                    } else {
+                        for (int jm = 0; jm < 4; ++jm)
+                            for (int l = 0; l < 64; ++l) {
+                                const int off = b_frag_off<C>(ks, j, wn0, l, jm);
+                                if (off < 0 || off + 4 > C::B_BYTES) FAIL("B read out of region");
+                                bf[l][jm] = decode<D>(&lds[C::A_BYTES + off]);
+                            }
+                    }
+                    // MFMA(s) of this block and K step
+                    long dblk[16][16] = {};
+                    if constexpr (D == DT_F32) {
+                        for (int jm = 0; jm < 4; ++jm)
+                            for (int r = 0; r < 16; ++r)
+                                for (int c = 0; c < 16; ++c)
+                                    for (int g = 0; g < 4; ++g)
+                                        dblk[r][c] += (long)af[r + 16 * g][jm] * bf[c + 16 * g][jm];
+                    } else {
+                        constexpr int KPL = (D == DT_I8) ? 16 : 8;  // K per lane group
+                        for (int r = 0; r < 16; ++r)
+                            for (int c = 0; c < 16; ++c)
+                                for (int k = 0; k < 4 * KPL; ++k)
+                                    dblk[r][c] += (long)af[r + 16 * (k / KPL)][k % KPL] * bf[c + 16 * (k / KPL)][k % KPL];
+                    }
+                    for (int r = 0; r < 16; ++r)
+                        for (int c = 0; c < 16; ++c) out[(wm0 + 16 * i + r) * C::BN + wn0 + 16 * j + c] += dblk[r][c];
+                }
+    }
+    for (int r = 0; r < C::BM; ++r)
+        for (int c = 0; c < C::BN; ++c) {
+            long ref = 0;
+            for (int k = 0; k < C::BK; ++k) ref += (long)A[r * C::BK + k] * B[k * C::BN + c];
+            if (out[r * C::BN + c] != ref) FAIL("C[%d][%d] = %ld, want %ld", r, c, out[r * C::BN + c], ref);
+        }
+}
+
+#define CHECK(D, BM, BN, BK, WGM, WGN)                                              \
+    do {                                                                           \
+        emulate<Cfg<D, BM, BN, BK, 2, WGM, WGN, PROD_DIRECT>>(#D " " #BM "x" #BN "x" #BK); \
+        ++n;                                                                       \
+        printf("class %d %d %d %d %d %d\n", D, BM, BN, BK, WGM, WGN);              \
+    } while (0)
+
+int main() {
+    int n = 0;
+    CHECK(DT_BF16, 256, 256, 32, 2, 4);
+    CHECK(DT_BF16, 256, 256, 64, 2, 4);
+    CHECK(DT_BF16, 128, 128, 64, 2, 2);
+    CHECK(DT_F16, 256, 256, 32, 2, 4);
+    CHECK(DT_F16, 256, 256, 64, 2, 4);
+    CHECK(DT_F16, 128, 128, 64, 2, 2);
+    CHECK(DT_I8, 256, 256, 64, 2, 4);
+    CHECK(DT_I8, 256, 256, 128, 2, 4);
+    CHECK(DT_I8, 128, 128, 128, 2, 2);
+    CHECK(DT_F32, 128, 64, 16, 2, 2);
+    CHECK(DT_F32, 256, 256, 32, 2, 4);
+    CHECK(DT_F32, 128, 128, 32, 2, 2);
+    printf("OK %d\n", n);
+    return 0;
+}
