@@ -81,7 +81,10 @@ typedef struct pgemm_opts {
     int tile_m;    /* 0 = planner's choice; else force BM (with tile_n, tile_k) */
     int tile_n;
     int tile_k;
-    int reserved[4];
+    int reserved[4]; /* reserved[0]: stress-test skew, 0..64 (0 = off): in every
+                        K tile one wave of each workgroup (rotating) sleeps
+                        reserved[0] x 8128 cycles after the ready barrier.
+                        Results are unchanged; only timing is.  Others: 0. */
 } pgemm_opts;
 
 /* What the planner chose (pgemm_plan output). */

@@ -100,13 +100,14 @@ def _stream(s):
     return s.cuda_stream
 
 
-def _opts(producer=None, tile=None):
-    if producer is None and tile is None:
+def _opts(producer=None, tile=None, skew=0):
+    if producer is None and tile is None and not skew:
         return None
     o = pgemm_opts()
     o.producer = PRODUCER[producer] if isinstance(producer, str) else int(producer or 0)
     if tile is not None:
         o.tile_m, o.tile_n, o.tile_k = (int(v) for v in tile)
+    o.reserved[0] = int(skew)
     return o
 
 
@@ -117,7 +118,7 @@ def pgemm_gemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stages, stre
 
 def pgemm_gemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stages, opts=None, stream=None):
     if isinstance(opts, dict):
-        opts = _opts(opts.get("producer"), opts.get("tile"))
+        opts = _opts(opts.get("producer"), opts.get("tile"), opts.get("skew", 0))
     p = ctypes.byref(opts) if opts is not None else None
     return _lib.pgemm_gemm_ex(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc,
                               DTYPE_CODE.get(dtype, dtype), stages, p, _stream(stream))

@@ -134,6 +134,7 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligne
         want_prod = opts->producer;
     }
     const bool force_tile = opts && (opts->tile_m || opts->tile_n || opts->tile_k);
+    if (opts && (opts->reserved[0] < 0 || opts->reserved[0] > 64)) return PGEMM_ERR_INVALID_ARG;
 
     // 1. tile class: best estimated time among variants with the producer.
     double best_time = 0.0;
@@ -347,6 +348,7 @@ int pgemm_gemm_ex(int64_t M, int64_t N, int64_t K, double alpha, const void* A, 
     a.ialpha = dtype == PGEMM_I8 ? (int)(int64_t)alpha : 0;
     a.ibeta = dtype == PGEMM_I8 ? (int)(int64_t)beta : 0;
     a.beta_nonzero = beta != 0.0;
+    a.dbg_sleep = opts ? opts->reserved[0] : 0;
     const int grid = a.tiles_m * a.tiles_n;
     hipError_t e = d.launch(a, grid, (hipStream_t)stream);
     return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_HIP;

@@ -64,7 +64,17 @@ struct KernelArgs {
     float alpha, beta;      // float dtypes
     int ialpha, ibeta;      // int8
     int beta_nonzero;
+    int dbg_sleep;          // test hook: wave (t % NW) sleeps dbg_sleep x 8128 cycles per K tile (0 = off)
 };
+
+// Test hook for stress runs: skew one wave per K tile (rotating) so that the
+// stage protocol is exercised with waves far apart.  Off (one scalar compare)
+// unless the caller asks for it.
+__device__ __forceinline__ void debug_skew(const KernelArgs& g, int t, int wave, int nw) {
+    if (g.dbg_sleep != 0 && wave == t % nw) {
+        for (int i = 0; i < g.dbg_sleep; ++i) __builtin_amdgcn_s_sleep(127);
+    }
+}
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
@@ -602,6 +612,7 @@ __device__ __forceinline__ void tile_body(const KernelArgs& g, int m0, int n0, i
             mfma_step<C, true, false>(acc, use, nxt, cstage, ks + 1, g, none, wave, lane, wm0, wn0);
         } else {
             sync_ring<C>();  // B_{t+1}: tile t+1 ready, stage of tile t free
+            debug_skew(g, t, wave, C::NW);
             const char PGEMM_LDS* rstage = smem + nstage * C::STAGE_BYTES;
             char PGEMM_LDS* freed = smem + cur * C::STAGE_BYTES;
             if constexpr (C::P == PROD_DIRECT) {
@@ -683,6 +694,7 @@ __device__ __forceinline__ void single_buffer_loop(const KernelArgs& g, int m0, 
         for (int t = 0; t < nK; ++t) {
             issue_tile<C>(g, m0, n0, t, smem, st, wave, lane);
             wait_barrier<0>();  // ready
+            debug_skew(g, t, wave, C::NW);
             compute_stage<C>(smem, wm0, wn0, lane, acc);
             lgkm_barrier();     // reuse
         }
@@ -691,6 +703,7 @@ __device__ __forceinline__ void single_buffer_loop(const KernelArgs& g, int m0, 
         store_tile<C>(smem, st, wave, lane);
         for (int t = 0; t < nK; ++t) {
             lgkm_barrier();  // ready
+            debug_skew(g, t, wave, C::NW);
             const bool more = t + 1 < nK;
             if (more) issue_tile<C>(g, m0, n0, t + 1, smem, st, wave, lane);
             compute_stage<C>(smem, wm0, wn0, lane, acc);

@@ -1,0 +1,64 @@
+"""Stress of the stage protocol on the GPU (correct protocol only).
+
+Page "Software pipelines and asynchronous copies" (section "Practice") asks
+for many repeated runs with randomised input and an artificial delay in one
+consumer, with failure counts.  Here the library's stress hook skews one wave
+of every workgroup per K tile (rotating) by ~8k cycles after the ready
+barrier, so the other waves reach the next barrier, and issue the next
+tile's loads into the freed stage, far ahead of it.  Every launch must give
+exactly the same int8 result, equal to the oracle.  A version with a wait
+removed is not run on the GPU: the host model checker
+(tests/test_schedule_model.py) shows that removing the reuse edge is detected.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from software_pipelined_tiled_loop_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("producer,stages,tile", [
+    ("direct", 2, (256, 256, 128)), ("direct", 3, (256, 256, 64)), ("direct", 4, (256, 256, 64)),
+    ("register", 2, (256, 256, 64)), ("direct", 1, (256, 256, 64)), ("register", 1, (256, 256, 64)),
+])
+def test_skewed_waves_many_runs_bit_exact(producer, stages, tile):
+    from software_pipelined_tiled_loop_amd import binding as lib
+    M, N, K = 1024, 1024, 768
+    runs = 200
+    print("[case] stress", producer, stages, tile, "runs", runs, flush=True)
+    op = inputs.make_operands("i8", M, N, K, seed=4321 + stages, alpha=1, beta=0)
+    A, B = op.A.cuda(), op.B.cuda()
+    ref = oracle.gemm("i8", M, N, K, 1, *op.numpy_views()[:2])
+    first = None
+    failures = 0
+    for r in range(runs):
+        C = torch.full((M, N), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
+        skew = 1 + (r % 2)
+        st = lib.pgemm_gemm_ex(M, N, K, 1, A, K, B, N, 0, C, N, "i8", stages,
+                               lib._opts(producer, tile, skew), None)
+        assert st == 0, lib.pgemm_strerror(st)
+        if first is None:
+            torch.cuda.synchronize()
+            first = C.clone()
+            assert np.array_equal(first.cpu().numpy(), ref)
+        elif not torch.equal(C, first):
+            failures += 1
+    torch.cuda.synchronize()
+    assert failures == 0, "%d of %d skewed runs differed" % (failures, runs)
+    # the hook really skews: a skewed launch is slower by about nK sleeps
+    def timed(skew):
+        C = torch.empty((M, N), dtype=torch.int32, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        assert lib.pgemm_gemm_ex(M, N, K, 1, A, K, B, N, 0, C, N, "i8", stages, lib._opts(producer, tile, skew),
+                                 None) == 0
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3  # us
+    base = min(timed(0) for _ in range(3))
+    skewed = min(timed(2) for _ in range(3))
+    nk = (K + tile[2] - 1) // tile[2]
+    assert skewed - base > 0.5 * nk * 2 * 8128 / 2.5e3, (base, skewed)
