@@ -16,6 +16,8 @@ static const VariantDesc k_table[] = {
     V(128, 128, 32, 3, 2, 2, PROD_DIRECT),    V(128, 128, 32, 4, 2, 2, PROD_DIRECT),
     V(128, 128, 32, 1, 2, 2, PROD_GENERIC),   V(128, 128, 32, 2, 2, 2, PROD_GENERIC),
     V(128, 128, 32, 3, 2, 2, PROD_GENERIC),   V(128, 128, 32, 4, 2, 2, PROD_GENERIC),
+    V(128, 64, 16, 1, 2, 2, PROD_GENERIC),    V(128, 64, 16, 2, 2, 2, PROD_GENERIC),
+    V(256, 256, 32, 1, 2, 4, PROD_GENERIC),   V(256, 256, 32, 2, 2, 4, PROD_GENERIC),
 };
 #undef V
 

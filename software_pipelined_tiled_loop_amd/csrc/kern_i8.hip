@@ -16,6 +16,7 @@ static const VariantDesc k_table[] = {
     V(128, 128, 128, 3, 2, 2, PROD_DIRECT),   V(128, 128, 128, 4, 2, 2, PROD_DIRECT),
     V(128, 128, 128, 1, 2, 2, PROD_GENERIC),  V(128, 128, 128, 2, 2, 2, PROD_GENERIC),
     V(128, 128, 128, 3, 2, 2, PROD_GENERIC),  V(128, 128, 128, 4, 2, 2, PROD_GENERIC),
+    V(256, 256, 64, 1, 2, 4, PROD_GENERIC), V(256, 256, 64, 2, 2, 4, PROD_GENERIC),
 };
 #undef V
 

@@ -5,12 +5,14 @@
 //     otherwise (REGISTER only on request);
 //   * tile: the compiled tile class with the smallest estimated time, counting
 //     how many rounds of workgroups the problem needs on 256 CUs;
-//   * stages: the smallest ring depth whose lookahead covers the load latency,
+//   * stages (DIRECT): the smallest ring depth whose lookahead covers the load latency,
 //     using the uncovered-latency estimate max(0, L - (S-1)*C) of page
 //     "Software pipelines and asynchronous copies" (section "Worked example:
 //     Choosing between two and four stages"), with C the MFMA time of one K
 //     tile on a SIMD.  The depth is clipped to the number of K tiles (section
 //     "Prologue, steady state, and epilogue": fewer K tiles than stages).
+//   * register-staged producers take tile and depth together from measured
+//     per-variant efficiencies (register pressure decides their depth).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -111,6 +113,46 @@ double tile_efficiency(const VariantDesc& d) {
     return 0.4 * (e > 1.0 ? 1.0 : std::pow(e, 0.5));
 }
 
+// Register-staged producers (REGISTER, GENERIC): measured efficiency of each
+// (tile class, ring depth) pair, MI355X, seeded inputs (GENERIC on the ragged
+// 4000 x 3968 x 4001 problem with lda = 4001; REGISTER at 4096^3).  For these
+// producers the best depth is set by register pressure, not by latency: the
+// staging registers plus the doubled fragment set exceed the 256 registers a
+// wave of a two-waves-per-SIMD workgroup may hold at S >= 2 on 256 x 256
+// tiles, and the spills cost more than the deeper ring gains.  The planner
+// therefore picks the (tile, depth) pair directly from this table.
+double staged_efficiency(const VariantDesc& d) {
+    struct E { int dt, bm, bn, bk, s, p; double e; };
+    static const E table[] = {
+        {PGEMM_BF16, 256, 256, 32, 1, PROD_GENERIC, 0.28},  {PGEMM_BF16, 256, 256, 32, 2, PROD_GENERIC, 0.32},
+        {PGEMM_BF16, 128, 128, 64, 1, PROD_GENERIC, 0.21},  {PGEMM_BF16, 128, 128, 64, 2, PROD_GENERIC, 0.21},
+        {PGEMM_BF16, 128, 128, 64, 3, PROD_GENERIC, 0.13},  {PGEMM_BF16, 128, 128, 64, 4, PROD_GENERIC, 0.13},
+        {PGEMM_F16, 256, 256, 32, 1, PROD_GENERIC, 0.28},   {PGEMM_F16, 256, 256, 32, 2, PROD_GENERIC, 0.31},
+        {PGEMM_F16, 128, 128, 64, 1, PROD_GENERIC, 0.20},   {PGEMM_F16, 128, 128, 64, 2, PROD_GENERIC, 0.21},
+        {PGEMM_F16, 128, 128, 64, 3, PROD_GENERIC, 0.13},   {PGEMM_F16, 128, 128, 64, 4, PROD_GENERIC, 0.13},
+        {PGEMM_I8, 256, 256, 64, 1, PROD_GENERIC, 0.246},   {PGEMM_I8, 256, 256, 64, 2, PROD_GENERIC, 0.21},
+        {PGEMM_I8, 128, 128, 128, 1, PROD_GENERIC, 0.11},   {PGEMM_I8, 128, 128, 128, 2, PROD_GENERIC, 0.117},
+        {PGEMM_I8, 128, 128, 128, 3, PROD_GENERIC, 0.118},  {PGEMM_I8, 128, 128, 128, 4, PROD_GENERIC, 0.116},
+        {PGEMM_F32, 256, 256, 32, 1, PROD_GENERIC, 0.745},  {PGEMM_F32, 256, 256, 32, 2, PROD_GENERIC, 0.53},
+        {PGEMM_F32, 128, 64, 16, 1, PROD_GENERIC, 0.69},    {PGEMM_F32, 128, 64, 16, 2, PROD_GENERIC, 0.64},
+        {PGEMM_F32, 128, 128, 32, 1, PROD_GENERIC, 0.67},   {PGEMM_F32, 128, 128, 32, 2, PROD_GENERIC, 0.645},
+        {PGEMM_F32, 128, 128, 32, 3, PROD_GENERIC, 0.49},   {PGEMM_F32, 128, 128, 32, 4, PROD_GENERIC, 0.495},
+        {PGEMM_BF16, 256, 256, 32, 1, PROD_REGISTER, 0.38}, {PGEMM_BF16, 256, 256, 32, 2, PROD_REGISTER, 0.34},
+        {PGEMM_BF16, 256, 256, 32, 3, PROD_REGISTER, 0.25}, {PGEMM_BF16, 256, 256, 32, 4, PROD_REGISTER, 0.256},
+        {PGEMM_BF16, 128, 128, 64, 2, PROD_REGISTER, 0.345},
+        {PGEMM_F16, 256, 256, 32, 1, PROD_REGISTER, 0.37},  {PGEMM_F16, 256, 256, 32, 2, PROD_REGISTER, 0.34},
+        {PGEMM_F16, 256, 256, 32, 3, PROD_REGISTER, 0.25},  {PGEMM_F16, 256, 256, 32, 4, PROD_REGISTER, 0.256},
+        {PGEMM_F16, 128, 128, 64, 2, PROD_REGISTER, 0.335},
+        {PGEMM_I8, 256, 256, 64, 1, PROD_REGISTER, 0.328},  {PGEMM_I8, 256, 256, 64, 2, PROD_REGISTER, 0.288},
+        {PGEMM_I8, 256, 256, 64, 3, PROD_REGISTER, 0.216},  {PGEMM_I8, 256, 256, 64, 4, PROD_REGISTER, 0.221},
+        {PGEMM_F32, 128, 64, 16, 1, PROD_REGISTER, 0.856},  {PGEMM_F32, 128, 64, 16, 2, PROD_REGISTER, 0.858},
+    };
+    for (const E& x : table)
+        if (x.dt == d.dtype && x.bm == d.bm && x.bn == d.bn && x.bk == d.bk && x.s == d.stages && x.p == d.producer)
+            return x.e;
+    return 0.5 * tile_efficiency(d);
+}
+
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool producer_matches(const VariantDesc& d, int want) { return d.producer == want; }
@@ -135,6 +177,34 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligne
     }
     const bool force_tile = opts && (opts->tile_m || opts->tile_n || opts->tile_k);
     if (opts && (opts->reserved[0] < 0 || opts->reserved[0] > 64)) return PGEMM_ERR_INVALID_ARG;
+
+    // Register-staged producers: the (tile, depth) pair with the best measured
+    // time; an explicit depth restricts the choice to variants of that depth.
+    if (want_prod != PROD_DIRECT) {
+        double best_time = 0.0;
+        int best = -1;
+        for (int i = 0; i < t.n; ++i) {
+            const VariantDesc& d = t.v[i];
+            if (!producer_matches(d, want_prod)) continue;
+            if (force_tile && (d.bm != opts->tile_m || d.bn != opts->tile_n || d.bk != opts->tile_k)) continue;
+            if (stages != 0 && d.stages != stages) continue;
+            const int occ = wg_per_cu(d);
+            const int64_t tiles = ceil_div(M, d.bm) * ceil_div(N, d.bn);
+            const int64_t rounds = ceil_div(tiles, (int64_t)kNumCU * occ);
+            const double work = (double)d.bm * d.bn * (double)(ceil_div(K, d.bk) * d.bk + d.bk);
+            const double time = (double)rounds * occ * work / staged_efficiency(d);
+            if (best < 0 || time < best_time * 0.999) {
+                best = i;
+                best_time = time;
+            }
+        }
+        if (best < 0) return PGEMM_ERR_INFEASIBLE_PLAN;
+        const VariantDesc& d = t.v[best];
+        out.index = best;
+        out.stages_req = d.stages;
+        out.uncovered = pgemm_model_uncovered_cycles(kLoadLatencyCycles, tile_compute_cycles(d, wg_per_cu(d)), d.stages);
+        return PGEMM_OK;
+    }
 
     // 1. tile class: best estimated time among variants with the producer.
     double best_time = 0.0;

@@ -274,8 +274,16 @@ struct Staging {
     i32x4 b[C::B_INSTR];
 };
 
-// Element-wise load of one 16-byte chunk (GENERIC producer): elements at or
-// beyond `valid` are zero.  `off` is the byte offset of the first element.
+// True when EPC elements read from element (r, c) of a row-major matrix with
+// `rows` rows, `cols` columns and leading dimension `ld` end at or before the
+// matrix's last element, so that a 16-byte read of a chunk that is partly
+// outside the columns never leaves the caller's allocation.
+PGEMM_HD bool chunk_fits(int r, int c, int64_t ld, int rows, int cols, int epc) {
+    return c + epc <= cols || (int64_t)r * ld + c + epc <= (int64_t)(rows - 1) * ld + cols;
+}
+
+// Element-wise load of one 16-byte chunk: elements at or beyond `valid` are
+// zero.  `off` is the byte offset of the first element.
 template <int ES>
 __device__ __forceinline__ i32x4 load_chunk_elementwise(__amdgpu_buffer_rsrc_t r, uint32_t off, int valid) {
     i32x4 v = {0, 0, 0, 0};
@@ -301,6 +309,35 @@ __device__ __forceinline__ i32x4 load_chunk_elementwise(__amdgpu_buffer_rsrc_t r
         }
     }
     return v;
+}
+
+// Zero the elements of a chunk at or beyond `valid` (0 <= valid <= 16/ES).
+template <int ES>
+__device__ __forceinline__ i32x4 zero_tail(i32x4 v, int valid) {
+    const int vbytes = valid * ES;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int keep = vbytes - 4 * d;  // bytes of dword d that stay
+        const uint32_t m = keep >= 4 ? 0xffffffffu : keep <= 0 ? 0u : (0xffffffffu >> (8 * (4 - keep)));
+        v[d] = (int)((uint32_t)v[d] & m);
+    }
+    return v;
+}
+
+// GENERIC producer: any element-aligned address.  One 16-byte load when the
+// 16 bytes lie inside the caller's matrix (`vec_ok`; the target runs in
+// unaligned-access mode, which the compiler itself relies on for unaligned
+// vector accesses), with the tail beyond `valid` zeroed; element-wise loads
+// for a partial chunk at the very end of the matrix, where a 16-byte load
+// could run past the allocation.
+template <int ES>
+__device__ __forceinline__ i32x4 load_chunk_any(__amdgpu_buffer_rsrc_t r, uint32_t off, int valid, bool vec_ok) {
+    if (valid <= 0) return i32x4{0, 0, 0, 0};
+    if (vec_ok) {
+        const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        return valid >= 16 / ES ? v : zero_tail<ES>(v, valid);
+    }
+    return load_chunk_elementwise<ES>(r, off, valid);
 }
 
 // DIRECT producer state for one K tile: buffer descriptors of the tile's A
@@ -375,7 +412,8 @@ __device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, 
             if constexpr (C::P == PROD_REGISTER) {
                 st.a[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? off : OOB, 0, 0);
             } else {
-                st.a[q] = load_chunk_elementwise<ES>(ra, off, ok ? min(C::EPC, k_left - kel) : 0);
+                const bool vec_ok = chunk_fits(row, kel, g.lda, rows_left, k_left, C::EPC);
+                st.a[q] = load_chunk_any<ES>(ra, off, ok ? min(C::EPC, k_left - kel) : 0, vec_ok);
             }
         }
 #pragma unroll
@@ -387,7 +425,8 @@ __device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, 
             if constexpr (C::P == PROD_REGISTER) {
                 st.b[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? off : OOB, 0, 0);
             } else {
-                st.b[q] = load_chunk_elementwise<ES>(rb, off, ok ? min(C::EPC, n_left - nel) : 0);
+                const bool vec_ok = chunk_fits(krow, nel, g.ldb, k_left, n_left, C::EPC);
+                st.b[q] = load_chunk_any<ES>(rb, off, ok ? min(C::EPC, n_left - nel) : 0, vec_ok);
             }
         }
     }

@@ -16,6 +16,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <vector>
 
 #include "../software_pipelined_tiled_loop_amd/csrc/pgemm_kernel.hpp"
@@ -184,6 +185,34 @@ static void emulate(const char* name) {
         }
 }
 
+
+// The generic producer reads a whole 16-byte chunk wherever chunk_fits says
+// so.  Brute force over small matrices: the allocation ends at the largest
+// r*ld + c over the matrix's elements; every admitted read must end there or
+// before, and every chunk lying wholly inside one row must be admitted.
+static int check_chunk_fits() {
+    const char* name = "chunk_fits";
+    int cases = 0;
+    for (int epc : {4, 8, 16})
+        for (int rows = 1; rows <= 5; ++rows)
+            for (int cols = 1; cols <= 40; ++cols)
+                for (int ld = cols; ld <= cols + 20; ++ld) {
+                    long last = -1;
+                    for (int r = 0; r < rows; ++r)
+                        for (int c = 0; c < cols; ++c) last = std::max(last, (long)r * ld + c);
+                    for (int r = 0; r < rows; ++r)
+                        for (int c = 0; c < cols; ++c) {
+                            const bool fits = chunk_fits(r, c, ld, rows, cols, epc);
+                            const long end = (long)r * ld + c + epc - 1;
+                            if (fits && end > last) FAIL("read of %d at (%d,%d) ld %d ends past the matrix", epc, r, c, ld);
+                            if (!fits && c + epc <= cols) FAIL("in-row chunk at (%d,%d) rejected", r, c);
+                            if (!fits && end <= last) FAIL("in-bounds chunk at (%d,%d) ld %d rejected", r, c, ld);
+                            ++cases;
+                        }
+                }
+    return cases;
+}
+
 #define CHECK(D, BM, BN, BK, WGM, WGN)                                              \
     do {                                                                           \
         emulate<Cfg<D, BM, BN, BK, 2, WGM, WGN, PROD_DIRECT>>(#D " " #BM "x" #BN "x" #BK); \
@@ -205,6 +234,7 @@ int main() {
     CHECK(DT_F32, 128, 64, 16, 2, 2);
     CHECK(DT_F32, 256, 256, 32, 2, 4);
     CHECK(DT_F32, 128, 128, 32, 2, 2);
+    printf("chunk_fits %d cases\n", check_chunk_fits());
     printf("OK %d\n", n);
     return 0;
 }

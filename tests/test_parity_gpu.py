@@ -189,14 +189,54 @@ def test_edge_sizes(lib, dtype):
                 check(op, got)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
 def test_generic_producer_misaligned(lib, dtype):
-    """Odd leading dimensions force the element-wise producer."""
-    M, N, K = 130, 77, 203
-    say("misaligned", dtype)
-    op = inputs.make_operands(dtype, M, N, K, seed=5, alpha=1.0, beta=0.0, lda=K + 1, ldb=N + 2, ldc=N + 3)
-    got = run_gpu(lib, op, stages=3)
-    check(op, got)
+    """Odd K, N and leading dimensions select the generic producer.  Its
+    16-byte reads cross the end of a row (into NaN/0x7F padding when the
+    leading dimension is padded, into the next row when it is tight) and must
+    zero every element past K or N; element-wise reads take the chunk at the
+    very end of the matrix."""
+    for (M, N, K, pa, pb, pc) in [(130, 77, 203, 1, 2, 3), (129, 131, 97, 0, 0, 0), (64, 5, 3, 0, 1, 0),
+                                  (200, 255, 1001, 3, 0, 1)]:
+        for stages in (1, 2, 3, 4):
+            say("misaligned", dtype, (M, N, K), "ld pads", (pa, pb, pc), "stages", stages)
+            op = inputs.make_operands(dtype, M, N, K, seed=5 + K, alpha=1.0, beta=0.0, lda=K + pa, ldb=N + pb,
+                                      ldc=N + pc)
+            got = run_gpu(lib, op, stages=stages)
+            check(op, got)
+            padding_untouched(op, got)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_generic_matches_direct_on_zero_padded_copy(lib, dtype):
+    """The generic producer on an odd-sized problem fills each LDS stage with
+    exactly the bytes the direct producer copies from a zero-padded, aligned
+    copy of the same matrices (K and N rounded up to 16 bytes), so within one
+    tile class C is bit-identical, for every tile class and depth the generic
+    producer is compiled for."""
+    epc = 16 // inputs.ELEM_BYTES[dtype]
+    classes = {}
+    for i in range(lib.pgemm_num_variants()):
+        v = lib.pgemm_variant_info(i)
+        if v["dtype"] == dtype and v["producer"] == "generic":
+            classes.setdefault((v["tile_m"], v["tile_n"], v["tile_k"]), []).append(v["stages"])
+    assert classes
+    for tile, depths in sorted(classes.items()):
+        M, N, K = 2 * tile[0] + 3, tile[1] + 5, 3 * tile[2] + 5
+        Kp, Np = -(-K // epc) * epc, -(-N // epc) * epc
+        op = inputs.make_operands(dtype, M, N, K, seed=99, alpha=1.0, beta=0.0, lda=K + 1, ldb=N)
+        pad = inputs.make_operands(dtype, M, Np, Kp, seed=99, alpha=1.0, beta=0.0)
+        pad.A.zero_()
+        pad.B.zero_()
+        pad.A[:, :K] = op.A[:, :K]
+        pad.B[:K, :N] = op.B[:, :N]
+        say("generic vs direct", dtype, tile, (M, N, K), "padded", (Kp, Np))
+        ref = run_gpu(lib, pad, stages=1, producer="direct", tile=tile)[:, :N]
+        for stages in sorted(depths):
+            say("generic", dtype, tile, "stages", stages)
+            got = run_gpu(lib, op, stages=stages, producer="generic", tile=tile)[:, :N]
+            assert torch.equal(got.contiguous().view(torch.int32), ref.contiguous().view(torch.int32)), (tile, stages)
+        check(op, run_gpu(lib, op, stages=min(depths), producer="generic", tile=tile))
 
 
 def test_beta_zero_ignores_nan_in_C_and_K0(lib):
