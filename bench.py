@@ -41,6 +41,9 @@ WORKLOADS = {
                  beta=0.0, cfg=3, data="seeded normal(0,1) rounded to bf16"),
     "f16": dict(name="fp16 GEMM M=N=K=4096 fp32 out", dtype="f16", M=4096, N=4096, K=4096, alpha=1.0,
                 beta=0.0, cfg=3, data="seeded normal(0,1) rounded to fp16"),
+    "ragged": dict(name="bf16 GEMM M=4000 N=3968 K=4001 lda=4001 ldb=ldc=3968 fp32 out", dtype="bf16", M=4000,
+                   N=3968, K=4001, lda=4001, ldb=3968, ldc=3968, alpha=1.0, beta=0.0, cfg=4,
+                   data="seeded normal(0,1) rounded to bf16"),
 }
 
 
@@ -171,8 +174,10 @@ def main():
     w = WORKLOADS[args.workload]
     dt, M, N, K, alpha, beta, cfg_idx = w["dtype"], w["M"], w["N"], w["K"], w["alpha"], w["beta"], w["cfg"]
     tile = tuple(int(x) for x in args.tile.split("x")) if args.tile else None
-    op, A, B, C = make_device_operands(dt, M, N, K, inputs.seed_for(cfg_idx), alpha, beta)
-    plan = plan_of(lib, dt, M, N, K, args.stages, args.producer, tile)
+    lda, ldb, ldc = w.get("lda", K), w.get("ldb", N), w.get("ldc", N)
+    aligned = int(all(x * inputs.ELEM_BYTES[dt] % 16 == 0 for x in (lda, ldb, K, N)))
+    op, A, B, C = make_device_operands(dt, M, N, K, inputs.seed_for(cfg_idx), alpha, beta, lda, ldb, ldc)
+    plan = plan_of(lib, dt, M, N, K, args.stages, args.producer, tile, aligned=aligned)
     if plan is None:
         print("no compiled variant for these options", file=sys.stderr)
         sys.exit(1)
@@ -180,7 +185,7 @@ def main():
     opts = lib._opts(args.producer, tile)
 
     def step():
-        r = lib.pgemm_gemm_ex(M, N, K, alpha, A, K, B, N, beta, C, N, dt, args.stages, opts, stream)
+        r = lib.pgemm_gemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dt, args.stages, opts, stream)
         if r != 0:
             raise lib.PgemmError(r)
 
