@@ -29,7 +29,11 @@
  *   - stream: a hipStream_t (NULL = the default stream).  The call only
  *     enqueues work and returns; completion is observed through the stream.
  *   - Misaligned pointers or leading dimensions are not an error: they select
- *     the element-wise producer (slower, same results).
+ *     the generic producer (16-byte loads through registers wherever the bytes
+ *     lie inside the matrix, element loads at its very end; slower, same
+ *     results).
+ *   - 32-bit tile addressing: M, N, K < 2^31, lda * elem * 256, ldb * elem *
+ *     128 and ldc * 4 * 256 below 2^31 bytes; otherwise PGEMM_ERR_TOO_LARGE.
  *   - Return value: PGEMM_OK (0) or a negative pgemm_status.  Argument errors
  *     are detected on the host before anything is enqueued.
  */
@@ -66,7 +70,9 @@ enum pgemm_status {
  *               with no register involvement (the cp.async analogue).
  *   REGISTER -- global memory into VGPRs at the top of the iteration, written
  *               to the LDS stage after the iteration's MFMA work.
- *   GENERIC  -- element-wise loads through VGPRs; used for misaligned data. */
+ *   GENERIC  -- as REGISTER, for any element-aligned layout: 16-byte loads
+ *               with the elements past K or N zeroed in registers, element
+ *               loads for the last chunk of a matrix. */
 enum pgemm_producer {
     PGEMM_PRODUCER_AUTO = 0,
     PGEMM_PRODUCER_DIRECT = 1,
@@ -81,10 +87,14 @@ typedef struct pgemm_opts {
     int tile_m;    /* 0 = planner's choice; else force BM (with tile_n, tile_k) */
     int tile_n;
     int tile_k;
-    int reserved[4]; /* reserved[0]: stress-test skew, 0..64 (0 = off): in every
-                        K tile one wave of each workgroup (rotating) sleeps
-                        reserved[0] x 8128 cycles after the ready barrier.
-                        Results are unchanged; only timing is.  Others: 0. */
+    int skew;      /* stress test, 0..64 (0 = off): in every K tile one wave of
+                      each workgroup (rotating) sleeps skew x 8128 cycles after
+                      the ready barrier.  Results are unchanged; only timing is. */
+    int workgroups; /* 0 = planner's choice; else launch this many persistent
+                       workgroups (rounded up to a multiple of 8, at most one per
+                       output tile), each looping over its share of the tiles
+                       with one K-tile ring running across tile boundaries. */
+    int reserved[2]; /* must be 0 */
 } pgemm_opts;
 
 /* What the planner chose (pgemm_plan output). */

@@ -33,7 +33,8 @@ STATUS = {0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED_DTYPE", -3: "BAD_STAGES",
 
 class pgemm_opts(ctypes.Structure):
     _fields_ = [("producer", ctypes.c_int), ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int),
-                ("tile_k", ctypes.c_int), ("reserved", ctypes.c_int * 4)]
+                ("tile_k", ctypes.c_int), ("skew", ctypes.c_int), ("workgroups", ctypes.c_int),
+                ("reserved", ctypes.c_int * 2)]
 
 
 class pgemm_plan_info(ctypes.Structure):
@@ -100,15 +101,20 @@ def _stream(s):
     return s.cuda_stream
 
 
-def _opts(producer=None, tile=None, skew=0):
-    if producer is None and tile is None and not skew:
+def _opts(producer=None, tile=None, skew=0, workgroups=0):
+    if producer is None and tile is None and not skew and not workgroups:
         return None
     o = pgemm_opts()
     o.producer = PRODUCER[producer] if isinstance(producer, str) else int(producer or 0)
     if tile is not None:
         o.tile_m, o.tile_n, o.tile_k = (int(v) for v in tile)
-    o.reserved[0] = int(skew)
+    o.skew = int(skew)
+    o.workgroups = int(workgroups)
     return o
+
+
+def _opts_from(d):
+    return _opts(d.get("producer"), d.get("tile"), d.get("skew", 0), d.get("workgroups", 0))
 
 
 def pgemm_gemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stages, stream=None):
@@ -118,7 +124,7 @@ def pgemm_gemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stages, stre
 
 def pgemm_gemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stages, opts=None, stream=None):
     if isinstance(opts, dict):
-        opts = _opts(opts.get("producer"), opts.get("tile"), opts.get("skew", 0))
+        opts = _opts_from(opts)
     p = ctypes.byref(opts) if opts is not None else None
     return _lib.pgemm_gemm_ex(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc,
                               DTYPE_CODE.get(dtype, dtype), stages, p, _stream(stream))
@@ -127,7 +133,7 @@ def pgemm_gemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stages, o
 def pgemm_plan(M, N, K, dtype, stages=0, aligned=1, opts=None):
     """Returns (status, plan dict or None)."""
     if isinstance(opts, dict):
-        opts = _opts(opts.get("producer"), opts.get("tile"))
+        opts = _opts_from(opts)
     info = pgemm_plan_info()
     r = _lib.pgemm_plan(M, N, K, DTYPE_CODE.get(dtype, dtype), stages, int(aligned),
                         ctypes.byref(opts) if opts is not None else None, ctypes.byref(info))

@@ -155,6 +155,30 @@ double staged_efficiency(const VariantDesc& d) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Workgroups to launch: one per output tile (default), or, on request
+// (pgemm_opts.workgroups), fewer persistent ones that loop over the tiles
+// with one K-tile ring across tile boundaries.  Always a multiple of 8 (the
+// kernel splits the tiles into one contiguous range per XCD); surplus
+// workgroups find no tile and exit.
+//
+// Persistence is not the default.  Measured on MI355X (bf16): 2-7 % faster
+// on 128 x 128 tiles at 4096^2 with K <= 1024 and 4 % at 8192^2 x 1024, but
+// 9 % slower at 8192^2 x 4096.  The C stores count in the same vmcnt as the
+// ring's loads, so a persistent workgroup's next ready barrier also waits for
+// its own stores; with one workgroup per tile a retiring workgroup's stores
+// drain while a fresh one (with its own counters) starts on the CU.  A
+// persistent grid must also match residency exactly: the dispatcher packs
+// workgroups onto CUs, so a smaller grid leaves CUs idle.
+int launch_grid(int64_t M, int64_t N, const VariantDesc& d, const pgemm_opts* opts) {
+    const int64_t tiles = ceil_div(M, d.bm) * ceil_div(N, d.bn);
+    int64_t grid = ceil_div(tiles, 8) * 8;
+    if (opts && opts->workgroups > 0) {
+        const int64_t want = ceil_div(opts->workgroups, 8) * 8;
+        if (want < grid) grid = want;
+    }
+    return grid < 8 ? 8 : (int)grid;
+}
+
 bool producer_matches(const VariantDesc& d, int want) { return d.producer == want; }
 
 struct Choice {
@@ -176,7 +200,9 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligne
         want_prod = opts->producer;
     }
     const bool force_tile = opts && (opts->tile_m || opts->tile_n || opts->tile_k);
-    if (opts && (opts->reserved[0] < 0 || opts->reserved[0] > 64)) return PGEMM_ERR_INVALID_ARG;
+    if (opts && (opts->skew < 0 || opts->skew > 64 || opts->workgroups < 0 || opts->reserved[0] != 0 ||
+                 opts->reserved[1] != 0))
+        return PGEMM_ERR_INVALID_ARG;
 
     // Register-staged producers: the (tile, depth) pair with the best measured
     // time; an explicit depth restricts the choice to variants of that depth.
@@ -272,7 +298,7 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligne
 }
 
 void fill_info(int dtype, const VariantDesc& d, int idx, int64_t M, int64_t N, int64_t K, double uncovered,
-               pgemm_plan_info* info) {
+               const pgemm_opts* opts, pgemm_plan_info* info) {
     std::memset(info, 0, sizeof(*info));
     info->tile_m = d.bm;
     info->tile_n = d.bn;
@@ -287,7 +313,7 @@ void fill_info(int dtype, const VariantDesc& d, int idx, int64_t M, int64_t N, i
     info->waves_n = d.wgn;
     info->lds_bytes = d.lds_bytes;
     info->wg_per_cu = wg_per_cu(d);
-    info->grid = (int)(ceil_div(M, d.bm) * ceil_div(N, d.bn));
+    info->grid = launch_grid(M, N, d, opts);
     int base = 0;  // global index: variants of lower dtypes come first
     for (int t = 0; t < dtype; ++t) base += table_for(t).n;
     info->variant = base + idx;
@@ -344,7 +370,7 @@ int pgemm_variant_info(int index, pgemm_plan_info* out, int* dtype) {
     for (int d = 0; d < 4; ++d) {
         Table t = table_for(d);
         if (index < t.n) {
-            fill_info(d, t.v[index], index, t.v[index].bm, t.v[index].bn, t.v[index].bk, 0.0, out);
+            fill_info(d, t.v[index], index, t.v[index].bm, t.v[index].bn, t.v[index].bk, 0.0, nullptr, out);
             if (dtype) *dtype = d;
             return PGEMM_OK;
         }
@@ -362,7 +388,7 @@ int pgemm_plan(int64_t M, int64_t N, int64_t K, int dtype, int stages, int align
     int r = plan_impl(M, N, K, dtype, stages, aligned, opts, c);
     if (r != PGEMM_OK) return r;
     Table t = table_for(dtype);
-    fill_info(dtype, t.v[c.index], c.index, M, N, K, c.uncovered, out);
+    fill_info(dtype, t.v[c.index], c.index, M, N, K, c.uncovered, opts, out);
     return PGEMM_OK;
 }
 
@@ -386,9 +412,10 @@ int pgemm_gemm_ex(int64_t M, int64_t N, int64_t K, double alpha, const void* A, 
     const int epc = 16 / es;
     // 32-bit tile addressing: byte offsets inside one tile must stay below 2^31.
     if (M > 0x7fffffff || N > 0x7fffffff || K > 0x7fffffff) return PGEMM_ERR_TOO_LARGE;
-    if ((double)lda * es * 256.0 >= 2147483648.0 || (double)ldb * es * 128.0 >= 2147483648.0)
+    if ((double)lda * es * 256.0 >= 2147483648.0 || (double)ldb * es * 128.0 >= 2147483648.0 ||
+        (double)ldc * 4.0 * 256.0 >= 2147483648.0)
         return PGEMM_ERR_TOO_LARGE;
-    if (ceil_div(M, 128) * ceil_div(N, 64) > 0x7fffffff) return PGEMM_ERR_TOO_LARGE;
+    if (ceil_div(M, 128) * ceil_div(N, 64) > 0x7ffffff0) return PGEMM_ERR_TOO_LARGE;
     // Element alignment is required; 16-byte alignment selects the vector producers.
     if (((uintptr_t)A % es) || ((uintptr_t)B % es) || ((uintptr_t)C % 4)) return PGEMM_ERR_INVALID_ARG;
     const int aligned = K == 0 || (is_aligned16(A) && is_aligned16(B) && (lda * es) % 16 == 0 &&
@@ -418,8 +445,8 @@ int pgemm_gemm_ex(int64_t M, int64_t N, int64_t K, double alpha, const void* A, 
     a.ialpha = dtype == PGEMM_I8 ? (int)(int64_t)alpha : 0;
     a.ibeta = dtype == PGEMM_I8 ? (int)(int64_t)beta : 0;
     a.beta_nonzero = beta != 0.0;
-    a.dbg_sleep = opts ? opts->reserved[0] : 0;
-    const int grid = a.tiles_m * a.tiles_n;
+    a.dbg_sleep = opts ? opts->skew : 0;
+    const int grid = launch_grid(M, N, d, opts);
     hipError_t e = d.launch(a, grid, (hipStream_t)stream);
     return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_HIP;
 }

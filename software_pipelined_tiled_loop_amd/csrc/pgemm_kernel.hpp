@@ -91,18 +91,22 @@ template <> struct Traits<DT_F32> {
     static constexpr int EPC = 4;      // elements per 16-byte chunk
     static constexpr int KSTEP = 16;   // K covered when each lane reads one A chunk
     typedef f32x4 Acc;
+    typedef float Out;                 // element type of C
 };
 template <> struct Traits<DT_F16> {
     static constexpr int ES = 2, EPC = 8, KSTEP = 32;
     typedef f32x4 Acc;
+    typedef float Out;
 };
 template <> struct Traits<DT_BF16> {
     static constexpr int ES = 2, EPC = 8, KSTEP = 32;
     typedef f32x4 Acc;
+    typedef float Out;
 };
 template <> struct Traits<DT_I8> {
     static constexpr int ES = 1, EPC = 16, KSTEP = 64;
     typedef i32x4 Acc;
+    typedef int Out;
 };
 
 // Buffer resource covering [base, base + 2^31): the kernel decides validity
@@ -626,16 +630,88 @@ __device__ __forceinline__ void sync_ring() {
     }
 }
 
+// Work of one workgroup and the K-tile slots it streams through the ring.
+//
+// Workgroups are dealt round-robin over the 8 XCDs (workgroup b runs on XCD
+// b % 8, each XCD with its own L2).  The grid is a multiple of 8.  XCD x owns
+// a contiguous range of logical tiles; its nl workgroups take tiles start+lb,
+// start+lb+nl, ... of that range, and a grouped raster turns the range into a
+// compact block of tile-rows x tile-columns, so the XCD's L2 serves the
+// shared A and B panels.  With one workgroup per tile every workgroup gets one
+// tile; with fewer (persistent workgroups) each one loops over its tiles.
+struct WgTiles {
+    int start, lb, nl, count;
+};
+
+// Tiles of workgroup b of a grid of `nb` workgroups (nb a multiple of 8) over
+// G logical tiles.
+PGEMM_HD WgTiles wg_tiles_of(int G, int b, int nb) {
+    const int x = b & 7, lb = b >> 3, nl = nb >> 3;
+    const int per = G >> 3, rem = G & 7;
+    const int start = x * per + (x < rem ? x : rem);
+    const int size = per + (x < rem ? 1 : 0);
+    return WgTiles{start, lb, nl, lb < size ? (size - lb + nl - 1) / nl : 0};
+}
+
+// Logical tile L -> (tile row, tile column): grouped raster, group_m tile-rows
+// per group, column-major inside a group.
+PGEMM_HD void raster(int L, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+    const int width = group_m * tiles_n;
+    const int grp = L / width;
+    const int first = grp * group_m;
+    const int gm = (tiles_m - first < group_m) ? tiles_m - first : group_m;
+    const int r = L - grp * width;
+    tm = first + r % gm;
+    tn = r / gm;
+}
+
+__device__ __forceinline__ WgTiles wg_tiles(const KernelArgs& g) {
+    return wg_tiles_of(g.tiles_m * g.tiles_n, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// Origin of this workgroup's i-th tile; past its last tile the origin is
+// (M, N), so every chunk of such a slot lies outside the matrices and loads
+// nothing.
+template <class C>
+__device__ __forceinline__ void wg_tile_origin(const KernelArgs& g, const WgTiles& w, int i, int& m0, int& n0) {
+    if (i >= w.count) {
+        m0 = g.M;
+        n0 = g.N;
+        return;
+    }
+    int tm, tn;
+    raster(w.start + w.lb + i * w.nl, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+    m0 = tm * C::BM;
+    n0 = tn * C::BN;
+}
+
+// The next K-tile slot to load: K tile kt of the workgroup's i-th output
+// tile.  Slots run through all K tiles of one output tile, then the next.
+struct Cursor {
+    int i, kt, m0, n0;
+};
+
+template <class C>
+__device__ __forceinline__ void cursor_next(const KernelArgs& g, const WgTiles& w, int nK, Cursor& c) {
+    if (++c.kt == nK) {
+        c.kt = 0;
+        ++c.i;
+        wg_tile_origin<C>(g, w, c.i, c.m0, c.n0);
+    }
+}
+
 // One K tile of the S >= 2 pipeline.  Fragments for K step ks+1 are read
 // while the MFMAs of step ks run; for the tile's last step the next reads
-// belong to tile t+1, so barrier B_{t+1} and the producer's issue sit right
-// before them -- after the last LDS reads of tile t and before its last
-// MFMAs.  The body is the same for every t: slots past the last K tile load
-// nothing (every lane out of range, zeros land in a stage nobody reads), so
-// the loop has no drain branches and the wait count is a constant.
-// PAR is the fragment buffer holding step 0 of this tile.
+// belong to the next slot, so barrier B_{s+1} and the producer's issue sit
+// right before them -- after the last LDS reads of slot s and before its last
+// MFMAs.  The body is the same for every slot: slots past the workgroup's
+// last K tile load nothing (every lane out of range, zeros land in a stage
+// nobody reads), so the loop has no drain branches and the wait count is a
+// constant.  `lc` is the slot to load (DIRECT: s+S; register producers:
+// s+S+1, one more being in flight in registers).  PAR is the fragment buffer
+// holding step 0 of this slot.
 template <class C, int PAR>
-__device__ __forceinline__ void tile_body(const KernelArgs& g, int m0, int n0, int t, char PGEMM_LDS* smem, int& cur,
+__device__ __forceinline__ void tile_body(const KernelArgs& g, const Cursor& lc, int s, char PGEMM_LDS* smem, int& cur,
                                           Staging<C>& st, Frags<C> (&f)[2],
                                           typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane, int wm0,
                                           int wn0) {
@@ -650,16 +726,16 @@ __device__ __forceinline__ void tile_body(const KernelArgs& g, int m0, int n0, i
         if (ks + 1 < NKS) {
             mfma_step<C, true, false>(acc, use, nxt, cstage, ks + 1, g, none, wave, lane, wm0, wn0);
         } else {
-            sync_ring<C>();  // B_{t+1}: tile t+1 ready, stage of tile t free
-            debug_skew(g, t, wave, C::NW);
+            sync_ring<C>();  // B_{s+1}: slot s+1 ready, stage of slot s free
+            debug_skew(g, s, wave, C::NW);
             const char PGEMM_LDS* rstage = smem + nstage * C::STAGE_BYTES;
             char PGEMM_LDS* freed = smem + cur * C::STAGE_BYTES;
             if constexpr (C::P == PROD_DIRECT) {
-                const DmaTile d = dma_setup<C>(g, m0, n0, t + C::S, freed, wave);  // tile t+S (maybe none)
+                const DmaTile d = dma_setup<C>(g, lc.m0, lc.n0, lc.kt, freed, wave);  // slot s+S (maybe none)
                 mfma_step<C, true, true>(acc, use, nxt, rstage, 0, g, d, wave, lane, wm0, wn0);
             } else {
-                store_tile<C>(freed, st, wave, lane);                      // tile t+S, loaded since B_t
-                issue_tile<C>(g, m0, n0, t + C::S + 1, freed, st, wave, lane);  // tile t+S+1 into registers
+                store_tile<C>(freed, st, wave, lane);                          // slot s+S, loaded since B_s
+                issue_tile<C>(g, lc.m0, lc.n0, lc.kt, freed, st, wave, lane);  // slot s+S+1 into registers
                 mfma_step<C, true, false>(acc, use, nxt, rstage, 0, g, none, wave, lane, wm0, wn0);
             }
         }
@@ -668,38 +744,93 @@ __device__ __forceinline__ void tile_body(const KernelArgs& g, int m0, int n0, i
 }
 
 template <class C>
-__device__ __forceinline__ void pipelined_loop(const KernelArgs& g, int m0, int n0, int nK, char PGEMM_LDS* smem,
-                                               typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane, int wm0,
-                                               int wn0) {
+__device__ __forceinline__ void zero_acc(typename C::T::Acc (&acc)[C::FM][C::FN]) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::T::Acc{0, 0, 0, 0};
+}
+
+template <class C>
+__device__ __forceinline__ void store_c(const KernelArgs& g, int m0, int n0, int wm0, int wn0, int lane,
+                                        typename C::T::Acc (&acc)[C::FM][C::FN]);
+
+// Compute-side bookkeeping after slot s: when it was the last K tile of an
+// output tile, write that tile (fused alpha/beta epilogue) and start the
+// next one from zero.  The loads of the following slots are already in
+// flight, so the store overlaps them (the next tile's prologue).
+template <class C>
+__device__ __forceinline__ void after_slot(const KernelArgs& g, const WgTiles& w, int nK, Cursor& cc,
+                                           typename C::T::Acc (&acc)[C::FM][C::FN], int wm0, int wn0, int lane) {
+    if (++cc.kt == nK) {
+        store_c<C>(g, cc.m0, cc.n0, wm0, wn0, lane, acc);
+        zero_acc<C>(acc);
+        cc.kt = 0;
+        ++cc.i;
+        wg_tile_origin<C>(g, w, cc.i, cc.m0, cc.n0);
+    }
+}
+
+// The S >= 2 pipeline over all K-tile slots of the workgroup's tiles: one
+// ring, one prologue, one drain.  A workgroup with one tile runs exactly the
+// per-tile pipeline; with several, tile j+1's first K tiles load while tile
+// j's last ones are multiplied and stored.
+template <class C>
+__device__ __forceinline__ void stream_loop(const KernelArgs& g, const WgTiles& w, int nK, char PGEMM_LDS* smem,
+                                            typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane, int wm0,
+                                            int wn0) {
     constexpr int NKS = C::BK / C::KSTEP;
     Staging<C> st;
     Frags<C> f[2];
-    // Prologue: K-tile slots 0 .. S-2 into stages 0 .. S-2 (slots >= nK load nothing).
+    Cursor lc{0, 0, 0, 0};
+    wg_tile_origin<C>(g, w, 0, lc.m0, lc.n0);
+    Cursor cc = lc;
+    // Prologue: slots 0 .. S-2 into stages 0 .. S-2.
 #pragma unroll
     for (int p = 0; p < C::S - 1; ++p) {
-        issue_tile<C>(g, m0, n0, p, smem + p * C::STAGE_BYTES, st, wave, lane);
+        issue_tile<C>(g, lc.m0, lc.n0, lc.kt, smem + p * C::STAGE_BYTES, st, wave, lane);
         if constexpr (C::P != PROD_DIRECT) store_tile<C>(smem + p * C::STAGE_BYTES, st, wave, lane);
+        cursor_next<C>(g, w, nK, lc);
     }
-    if constexpr (C::P != PROD_DIRECT) issue_tile<C>(g, m0, n0, C::S - 1, smem, st, wave, lane);
+    if constexpr (C::P != PROD_DIRECT) {
+        issue_tile<C>(g, lc.m0, lc.n0, lc.kt, smem, st, wave, lane);  // slot S-1 into registers
+        cursor_next<C>(g, w, nK, lc);
+    }
     sync_ring<C>();  // B_0
     // Stage S-1 has never been used: slot S-1 goes there now.
     if constexpr (C::P == PROD_DIRECT) {
-        issue_tile<C>(g, m0, n0, C::S - 1, smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
+        issue_tile<C>(g, lc.m0, lc.n0, lc.kt, smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
     } else {
         store_tile<C>(smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
-        issue_tile<C>(g, m0, n0, C::S, smem, st, wave, lane);
+        issue_tile<C>(g, lc.m0, lc.n0, lc.kt, smem, st, wave, lane);  // slot S into registers
     }
+    cursor_next<C>(g, w, nK, lc);
     read_frags<C>(smem, 0, wm0, wn0, lane, f[0]);
     int cur = 0;
+    const int total = w.count * nK;
     if constexpr (NKS % 2 == 0) {
-        for (int t = 0; t < nK; ++t) tile_body<C, 0>(g, m0, n0, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
-    } else {
-        int t = 0;
-        for (; t + 1 < nK; t += 2) {
-            tile_body<C, 0>(g, m0, n0, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
-            tile_body<C, 1>(g, m0, n0, t + 1, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+        for (int s = 0; s < total; ++s) {
+            tile_body<C, 0>(g, lc, s, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+            cursor_next<C>(g, w, nK, lc);
+            after_slot<C>(g, w, nK, cc, acc, wm0, wn0, lane);
         }
-        if (t < nK) tile_body<C, 0>(g, m0, n0, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+    } else {
+        // Pairs of slots keep the fragment buffers' roles fixed at the back
+        // edge (one buffer live between slots); an odd last slot follows.
+        int s = 0;
+        for (; s + 1 < total; s += 2) {
+            tile_body<C, 0>(g, lc, s, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+            cursor_next<C>(g, w, nK, lc);
+            after_slot<C>(g, w, nK, cc, acc, wm0, wn0, lane);
+            tile_body<C, 1>(g, lc, s + 1, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+            cursor_next<C>(g, w, nK, lc);
+            after_slot<C>(g, w, nK, cc, acc, wm0, wn0, lane);
+        }
+        if (s < total) {
+            tile_body<C, 0>(g, lc, s, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+            cursor_next<C>(g, w, nK, lc);
+            after_slot<C>(g, w, nK, cc, acc, wm0, wn0, lane);
+        }
     }
     // No load may still be writing LDS when the workgroup retires.
     __builtin_amdgcn_s_waitcnt(0);
@@ -752,56 +883,77 @@ __device__ __forceinline__ void single_buffer_loop(const KernelArgs& g, int m0, 
     }
 }
 
-// Workgroup -> output tile.  Workgroups are dealt round-robin over the 8 XCDs
-// (each with its own L2); the remap gives every XCD a contiguous range of
-// logical tiles, and the grouped raster makes that range a compact block of
-// tile-rows x tile-columns so the XCD's L2 serves shared A and B panels.
-__device__ __forceinline__ void tile_of(const KernelArgs& g, int& tm, int& tn) {
-    const int G = g.tiles_m * g.tiles_n;
-    const int w = blockIdx.x;
-    const int per = G >> 3;
-    const int G8 = per << 3;
-    const int L = (w < G8) ? (w & 7) * per + (w >> 3) : w;
-    const int width = g.group_m * g.tiles_n;
-    const int grp = L / width;
-    const int first = grp * g.group_m;
-    const int gm = min(g.tiles_m - first, g.group_m);
-    const int r = L - grp * width;
-    tm = first + r % gm;
-    tn = r / gm;
-}
-
 // ---- epilogue: C = alpha*acc + beta*C (fused, as in the pages' kernel) -------------
+
+// The wave's block of C starts at a uniform address; a lane's element sits at
+// a 32-bit offset from it (row 4*lg + 16*i + r, column li + 16*j), split into
+// a uniform row part, one per-lane part and an immediate column part, so the
+// epilogue holds one address register per lane rather than one per row.
+// Byte offsets stay below 2^31 because ldc * 4 * 256 < 2^31 (checked on the
+// host).
+//
+// With beta != 0 the old C is read one 16-row block (i) at a time: all reads
+// of a block in flight together, then the block is combined and written.  A
+// bounded number of registers (the next tile's fragments may be live here)
+// and no serialised read-wait-write per element.  MASK: the tile is cut by the edge
+// of C; the bounds are compared in a lane-invariant form (4*lg against a
+// uniform limit) so no per-row lane values have to stay live.
+template <class C, bool MASK, bool BETA>
+__device__ __forceinline__ void store_c_impl(const KernelArgs& g, int m0, int n0, int wm0, int wn0, int lane,
+                                             typename C::T::Acc (&acc)[C::FM][C::FN]) {
+    using E = typename C::T::Out;
+    const int li = lane & 15, lg4 = 4 * (lane >> 4);
+    const int rows_left = g.M - m0 - wm0, n_left = g.N - n0 - wn0;
+    const int ldc4 = (int)g.ldc * 4;
+    char* cw = (char*)g.C + ((int64_t)(m0 + wm0) * g.ldc + n0 + wn0) * 4;
+    const uint32_t voff = (uint32_t)(lg4 * ldc4 + 4 * li);
+    auto at = [&](int i, int r, int j) -> E* { return (E*)(cw + (uint32_t)((16 * i + r) * ldc4) + voff) + 16 * j; };
+    auto inside = [&](int i, int r, int j) -> bool {
+        return !MASK || (lg4 < rows_left - 16 * i - r && li < n_left - 16 * j);
+    };
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        E old[4][C::FN];
+        if constexpr (BETA) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j) old[r][j] = inside(i, r, j) ? *at(i, r, j) : E(0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                if (!inside(i, r, j)) continue;
+                if constexpr (C::Dt == DT_I8) {
+                    uint32_t v = (uint32_t)g.ialpha * (uint32_t)acc[i][j][r];
+                    if constexpr (BETA) v += (uint32_t)g.ibeta * (uint32_t)old[r][j];
+                    *at(i, r, j) = (int)v;
+                } else {
+                    float v = g.alpha * acc[i][j][r];
+                    if constexpr (BETA) v = fmaf(g.beta, old[r][j], v);
+                    *at(i, r, j) = v;
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
 
 template <class C>
 __device__ __forceinline__ void store_c(const KernelArgs& g, int m0, int n0, int wm0, int wn0, int lane,
                                         typename C::T::Acc (&acc)[C::FM][C::FN]) {
-    const int li = lane & 15, lg = lane >> 4;
-    const int rows_left = g.M - m0, n_left = g.N - n0;
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = wm0 + 16 * i + 4 * lg + r;
-            if (row >= rows_left) continue;
-            const int64_t base = (int64_t)(m0 + row) * g.ldc + n0;
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
-                const int col = wn0 + 16 * j + li;
-                if (col >= n_left) continue;
-                if constexpr (C::Dt == DT_I8) {
-                    int* cp = (int*)g.C + base + col;
-                    uint32_t v = (uint32_t)g.ialpha * (uint32_t)acc[i][j][r];
-                    if (g.beta_nonzero) v += (uint32_t)g.ibeta * (uint32_t)(*cp);
-                    *cp = (int)v;
-                } else {
-                    float* cp = (float*)g.C + base + col;
-                    float v = g.alpha * acc[i][j][r];
-                    if (g.beta_nonzero) v = fmaf(g.beta, *cp, v);
-                    *cp = v;
-                }
-            }
-        }
+    const bool full = m0 + C::BM <= g.M && n0 + C::BN <= g.N;
+    if (g.beta_nonzero) {
+        if (full)
+            store_c_impl<C, false, true>(g, m0, n0, wm0, wn0, lane, acc);
+        else
+            store_c_impl<C, true, true>(g, m0, n0, wm0, wn0, lane, acc);
+    } else {
+        if (full)
+            store_c_impl<C, false, false>(g, m0, n0, wm0, wn0, lane, acc);
+        else
+            store_c_impl<C, true, false>(g, m0, n0, wm0, wn0, lane, acc);
     }
 }
 
@@ -812,29 +964,33 @@ __global__ void __launch_bounds__(C::NT) gemm_kernel(KernelArgs g) {
     __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_BYTES];
     char PGEMM_LDS* smem = (char PGEMM_LDS*)smem_raw;
 
+    const WgTiles w = wg_tiles(g);
+    if (w.count == 0) return;  // more workgroups than tiles in this XCD's range
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm0 = (wave / C::WGN) * C::WM;
     const int wn0 = (wave % C::WGN) * C::WN;
-    int tm, tn;
-    tile_of(g, tm, tn);
-    const int m0 = tm * C::BM, n0 = tn * C::BN;
     const int nK = (g.K + C::BK - 1) / C::BK;
 
     typename C::T::Acc acc[C::FM][C::FN];
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::T::Acc{0, 0, 0, 0};
+    zero_acc<C>(acc);
 
-    if (nK > 0) {
-        if constexpr (C::S == 1) {
-            single_buffer_loop<C>(g, m0, n0, nK, smem, acc, wave, lane, wm0, wn0);
-        } else {
-            pipelined_loop<C>(g, m0, n0, nK, smem, acc, wave, lane, wm0, wn0);
+    if constexpr (C::S > 1) {
+        if (nK > 0) {
+            stream_loop<C>(g, w, nK, smem, acc, wave, lane, wm0, wn0);
+            return;
         }
     }
-    store_c<C>(g, m0, n0, wm0, wn0, lane, acc);
+    // One ring slot (S = 1), or K = 0: tile by tile.
+    for (int i = 0; i < w.count; ++i) {
+        int m0, n0;
+        wg_tile_origin<C>(g, w, i, m0, n0);
+        if constexpr (C::S == 1) {
+            if (nK > 0) single_buffer_loop<C>(g, m0, n0, nK, smem, acc, wave, lane, wm0, wn0);
+        }
+        store_c<C>(g, m0, n0, wm0, wn0, lane, acc);
+        zero_acc<C>(acc);
+    }
 }
 
 }  // namespace pgemm

@@ -213,6 +213,50 @@ static int check_chunk_fits() {
     return cases;
 }
 
+// Work split: for every tile count and grid (a multiple of 8, at most one
+// workgroup per tile rounded up to 8, as the host launches), each logical tile
+// goes to exactly one workgroup, each XCD (b % 8) gets a contiguous range,
+// and the grouped raster maps the logical tiles onto the tile grid one to one.
+static int check_work_split() {
+    const char* name = "work_split";
+    int cases = 0;
+    for (int G = 1; G <= 300; G += (G < 40 ? 1 : 7)) {
+        const int full = (G + 7) / 8 * 8;
+        for (int nb = 8; nb <= full; nb += 8) {
+            std::vector<int> owner(G, -1);
+            for (int b = 0; b < nb; ++b) {
+                const WgTiles w = wg_tiles_of(G, b, nb);
+                for (int i = 0; i < w.count; ++i) {
+                    const int L = w.start + w.lb + i * w.nl;
+                    if (L < 0 || L >= G) FAIL("G %d grid %d: wg %d tile %d out of range", G, nb, b, L);
+                    if (owner[L] >= 0) FAIL("G %d grid %d: tile %d owned twice", G, nb, L);
+                    if ((owner[L] = b) % 8 != (b & 7)) FAIL("bad XCD");
+                }
+            }
+            for (int L = 0; L < G; ++L)
+                if (owner[L] < 0) FAIL("G %d grid %d: tile %d unowned", G, nb, L);
+            for (int L = 1; L < G; ++L)
+                if ((owner[L] & 7) < (owner[L - 1] & 7)) FAIL("G %d grid %d: XCD ranges not contiguous", G, nb);
+            ++cases;
+        }
+    }
+    for (int tm = 1; tm <= 20; ++tm)
+        for (int tn = 1; tn <= 20; ++tn)
+            for (int gm = 1; gm <= 6; ++gm) {
+                std::vector<int> hit(tm * tn, 0);
+                for (int L = 0; L < tm * tn; ++L) {
+                    int a, b;
+                    raster(L, tm, tn, gm, a, b);
+                    if (a < 0 || a >= tm || b < 0 || b >= tn) FAIL("raster %d of %dx%d out of range", L, tm, tn);
+                    hit[a * tn + b]++;
+                }
+                for (int x : hit)
+                    if (x != 1) FAIL("raster %dx%d group %d not a bijection", tm, tn, gm);
+                ++cases;
+            }
+    return cases;
+}
+
 #define CHECK(D, BM, BN, BK, WGM, WGN)                                              \
     do {                                                                           \
         emulate<Cfg<D, BM, BN, BK, 2, WGM, WGN, PROD_DIRECT>>(#D " " #BM "x" #BN "x" #BK); \
@@ -235,6 +279,7 @@ int main() {
     CHECK(DT_F32, 256, 256, 32, 2, 4);
     CHECK(DT_F32, 128, 128, 32, 2, 2);
     printf("chunk_fits %d cases\n", check_chunk_fits());
+    printf("work_split %d cases\n", check_work_split());
     printf("OK %d\n", n);
     return 0;
 }

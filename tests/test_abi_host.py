@@ -74,6 +74,33 @@ def test_argument_errors_before_any_launch(args, code):
     assert r == code, (args, r, lib.pgemm_strerror(r))
 
 
+@pytest.mark.parametrize("opts", [dict(skew=65), dict(skew=-1), dict(workgroups=-8)])
+def test_option_errors_before_any_launch(opts):
+    o = lib._opts(tile=(128, 128, 64), skew=opts.get("skew", 0), workgroups=opts.get("workgroups", 0))
+    r = lib.pgemm_gemm_ex(8, 8, 8, 1.0, FAKE, 8, FAKE, 8, 0.0, FAKE, 8, "bf16", 0, o, 0)
+    assert r == -1, lib.pgemm_strerror(r)
+    o = lib._opts(tile=(128, 128, 64))
+    o.reserved[1] = 3
+    assert lib.pgemm_gemm_ex(8, 8, 8, 1.0, FAKE, 8, FAKE, 8, 0.0, FAKE, 8, "bf16", 0, o, 0) == -1
+
+
+def test_ldc_beyond_32_bit_tile_addressing_is_rejected():
+    r = lib._lib.pgemm_gemm(8, 8, 8, 1.0, FAKE, 8, FAKE, 8, 0.0, FAKE, 1 << 21, 2, 0, None)
+    assert r == -7
+
+
+def test_grid_is_a_multiple_of_8_and_persistent_workgroups_are_capped():
+    # one workgroup per tile, rounded up to a multiple of 8
+    r, p = lib.pgemm_plan(4096, 4096, 4096, "bf16", 0, 1, {"tile": (256, 256, 64)})
+    assert r == 0 and p["grid"] == 256
+    r, p = lib.pgemm_plan(300, 300, 64, "bf16", 0, 1, {"tile": (128, 128, 64)})
+    assert r == 0 and p["grid"] == 16          # 9 tiles -> 16 workgroups, 7 find no tile
+    # persistent: the requested count, rounded up to 8, never more than the default grid
+    for want, got in ((1, 8), (8, 8), (20, 24), (256, 256), (100000, 1024)):
+        r, p = lib.pgemm_plan(4096, 4096, 256, "bf16", 0, 1, {"tile": (128, 128, 64), "workgroups": want})
+        assert r == 0 and p["grid"] == got, (want, p["grid"])
+
+
 def test_empty_problems_are_noops():
     assert lib._lib.pgemm_gemm(0, 8, 8, 1.0, None, 8, None, 8, 0.0, None, 8, 2, 0, None) == 0
     assert lib._lib.pgemm_gemm(8, 0, 8, 1.0, None, 8, None, 8, 0.0, None, 8, 2, 0, None) == 0

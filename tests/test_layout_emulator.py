@@ -31,6 +31,7 @@ def test_emulated_data_path_matches_naive_gemm(tmp_path):
     out = subprocess.run([exe], stdout=subprocess.PIPE, text=True, timeout=600).stdout
     assert out.strip().splitlines()[-1].startswith("OK"), out[-2000:]
     assert re.search(r"^chunk_fits \d+ cases$", out, re.M), out[-2000:]
+    assert re.search(r"^work_split \d+ cases$", out, re.M), out[-2000:]
     emulated = set(tuple(int(x) for x in m) for m in re.findall(r"^class (\d+) (\d+) (\d+) (\d+) (\d+) (\d+)$", out, re.M))
     # every tile class the library compiles is emulated
     for i in range(lib.pgemm_num_variants()):

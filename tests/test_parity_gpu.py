@@ -34,12 +34,12 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
-def run_gpu(lib, op, stages=0, producer=None, tile=None, expect=0):
+def run_gpu(lib, op, stages=0, producer=None, tile=None, expect=0, workgroups=0):
     dev = torch.device("cuda:0")
     A = op.A.to(dev)
     B = op.B.to(dev)
     C = op.C.to(dev)
-    o = lib._opts(producer, tile)
+    o = lib._opts(producer, tile, workgroups=workgroups)
     r = lib.pgemm_gemm_ex(op.M, op.N, op.K, op.alpha, A if op.M and op.K else 0, max(op.lda, 1),
                           B if op.K and op.N else 0, max(op.ldb, 1), op.beta, C if op.M else 0, max(op.ldc, 1),
                           op.dtype, stages, o, None)
@@ -144,6 +144,48 @@ def test_bit_identical_across_stages_and_producers(lib, dtype):
         check(op, outs[0][1])
         for key, o in outs[1:]:
             assert torch.equal(o.view(torch.int32), outs[0][1].view(torch.int32)), (tile, key, outs[0][0])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_persistent_workgroups_bit_identical(lib, dtype):
+    """Persistent workgroups stream the K tiles of several output tiles through
+    one ring (the next tile's loads overlap this tile's last K tiles and its
+    C store).  Each output tile's arithmetic is unchanged, so C must be
+    bit-identical to one workgroup per tile: every tile class, depth and
+    producer, ragged edges, beta != 0, and grids that leave workgroups idle."""
+    alpha, beta = (2, -3) if dtype == "i8" else (1.5, -0.5)
+    classes = {}
+    for i in range(lib.pgemm_num_variants()):
+        v = lib.pgemm_variant_info(i)
+        if v["dtype"] == dtype:
+            classes.setdefault((v["tile_m"], v["tile_n"], v["tile_k"]), []).append((v["stages"], v["producer"]))
+    for tile, variants in sorted(classes.items()):
+        M, N, K = 3 * tile[0] - 37, 2 * tile[1] + 32, 2 * tile[2] + 16  # 16-byte rows: every producer
+        op = inputs.make_operands(dtype, M, N, K, seed=606, alpha=alpha, beta=beta)
+        for stages, producer in sorted(variants):
+            say("persistent", dtype, tile, stages, producer, (M, N, K))
+            ref = run_gpu(lib, op, stages=stages, producer=producer, tile=tile)
+            for wg in (8, 16):
+                got = run_gpu(lib, op, stages=stages, producer=producer, tile=tile, workgroups=wg)
+                assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), (tile, stages, producer, wg)
+        check(op, ref)
+        padding_untouched(op, ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+def test_persistent_workgroups_short_k_and_k0(lib, dtype):
+    """Fewer K tiles than stages, one K tile, and K = 0 (C = beta*C) with
+    several output tiles per workgroup."""
+    bk = {"f32": 32, "bf16": 64, "i8": 128}[dtype]
+    alpha, beta = (1, 2) if dtype == "i8" else (1.0, 0.25)
+    for K in (0, 1, bk, bk + 16, 3 * bk):
+        for stages in (1, 2, 4):
+            say("persistent short K", dtype, K, "stages", stages)
+            op = inputs.make_operands(dtype, 520, 390, K, seed=K + 7, alpha=alpha, beta=beta)
+            ref = run_gpu(lib, op, stages=stages)
+            got = run_gpu(lib, op, stages=stages, workgroups=8)
+            assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), (K, stages)
+            check(op, got)
 
 
 @pytest.mark.parametrize("stages", [1, 2, 3, 4])
@@ -287,6 +329,19 @@ def test_full_size_sampled(lib, name, dtype, M, N, K, alpha, beta, cfg):
     got = run_gpu(lib, op, stages=0)
     rows = sampled_rows(M, seed=cfg)
     check(op, got, rows=rows)
+
+
+def test_persistent_workgroups_full_size(lib):
+    """8192 x 4096 outputs (512 tiles of 256 x 256) on one round of 256
+    persistent workgroups, two tiles each: sampled rows against the oracle,
+    and bit-identical to one workgroup per tile."""
+    M, N, K = 8192, 4096, 1024
+    say("persistent full size", (M, N, K))
+    op = inputs.make_operands("bf16", M, N, K, seed=4321, alpha=1.0, beta=0.0)
+    ref = run_gpu(lib, op)
+    got = run_gpu(lib, op, workgroups=256)
+    check(op, got, rows=sampled_rows(M, n=36, seed=5))
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
 
 
 @pytest.mark.parametrize("K", [32, 64, 256, 1024])

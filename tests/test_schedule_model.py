@@ -8,22 +8,25 @@ finishes reading it, the producer may overwrite it (reuse).  Section
 past K and the epilogue must not consume a stage whose load was not waited
 for.
 
-This test replays the event sequence of the kernel's K loop (the functions
-pipelined_loop / tile_body / single_buffer_loop of pgemm_kernel.hpp) for
-every producer, ring depth S = 1..4, K steps per tile NKS = 1..2 and number of
-K tiles nK = 0..12, and checks, for a workgroup of waves that all run the
-same program and meet only at barriers:
+This test replays the event sequence of the kernel's K loop (stream_loop /
+tile_body / after_slot / single_buffer_loop of pgemm_kernel.hpp) for every
+producer, ring depth S = 1..4, K steps per tile NKS = 1..2, number of K tiles
+nK = 0..12 and 1..3 output tiles per workgroup (a persistent workgroup streams
+the K tiles of all its output tiles through one ring), and checks, for a
+workgroup of waves that all run the same program and meet only at barriers:
 
-  ready   every read of a stage sees the tile the step expects; that tile's
+  ready   every read of a stage sees the slot the step expects; that slot's
           load was waited for (vector loads retire in issue order, so a wait
           with P pending groups completes all but the last P) or written by
           ds_write, and a barrier lies between that and the read;
   reuse   between any read of a stage and a later load into it there is a
           barrier (our barriers drain LDS reads first), and the stage's
           previous load had completed (no two loads race into one stage);
-  order   every K tile is multiplied exactly once, its steps in order, from
-          fragments read after its ready edge; no real load targets a tile
-          >= nK; nothing is in flight when the workgroup ends.
+  order   every K tile of every output tile is multiplied exactly once, its
+          steps in order, from fragments read after its ready edge; each
+          output tile is stored once, after its last MFMA and before the next
+          tile's first; no real load targets a slot past the workgroup's
+          work; nothing is in flight when the workgroup ends.
 """
 import itertools
 
@@ -54,14 +57,19 @@ class Trace:
     def mfma(self, tile, ks):
         self.ev.append(("mfma", tile, ks))
 
+    def store(self, out_tile):
+        self.ev.append(("store", out_tile))
+
     def waitall(self):
         self.ev.append(("wait", 0))
 
 
 # ---- the kernel's control flow, event by event -------------------------------
+# A "slot" is one K tile of one output tile: slot s = tile s // nK, K tile s % nK.
 
-def pipelined_loop(S, NKS, nK, direct):
-    tr = Trace(nK)
+def stream_loop(S, NKS, nK, ntiles, direct):
+    total = ntiles * nK
+    tr = Trace(total)
     for p in range(S - 1):                       # prologue slots 0..S-2
         tr.issue(p, p, direct)
         if not direct:
@@ -76,21 +84,23 @@ def pipelined_loop(S, NKS, nK, direct):
         tr.issue(S, None, False)
     tr.read(0, 0, 0)
     cur = 0
-    for t in range(nK):
+    for s in range(total):
         nstage = (cur + 1) % S
         for ks in range(NKS):
             if ks + 1 < NKS:
-                tr.read(cur, t, ks + 1)
+                tr.read(cur, s, ks + 1)
             else:
-                sync_ring(tr, S, direct)         # B_{t+1}
+                sync_ring(tr, S, direct)         # B_{s+1}
                 if direct:
-                    tr.issue(t + S, cur, True)
+                    tr.issue(s + S, cur, True)
                 else:
-                    tr.write(t + S, cur)
-                    tr.issue(t + S + 1, None, False)
-                tr.read(nstage, t + 1, 0)
-            tr.mfma(t, ks)
+                    tr.write(s + S, cur)
+                    tr.issue(s + S + 1, None, False)
+                tr.read(nstage, s + 1, 0)
+            tr.mfma(s, ks)
         cur = nstage
+        if (s + 1) % nK == 0:                    # after_slot: last K tile of an output tile
+            tr.store(s // nK)
     tr.waitall()
     return tr
 
@@ -101,42 +111,46 @@ def sync_ring(tr, S, direct):
     tr.barrier()
 
 
-def single_buffer_loop(NKS, nK, direct):
-    tr = Trace(nK)
+def single_buffer_tile(tr, base, NKS, nK, direct):
+    """One output tile with one LDS buffer; slots base .. base+nK-1."""
     if direct:
         for t in range(nK):
-            tr.issue(t, 0, True)
+            tr.issue(base + t, 0, True)
             tr.wait(0)
             tr.barrier()
             for ks in range(NKS):
-                tr.read(0, t, ks)
-                tr.mfma(t, ks)
+                tr.read(0, base + t, ks)
+                tr.mfma(base + t, ks)
             tr.barrier()
     else:
         if nK > 0:
-            tr.issue(0, None, False)
-            tr.write(0, 0)
+            tr.issue(base, None, False)
+            tr.write(base, 0)
         for t in range(nK):
             tr.barrier()
             more = t + 1 < nK
             if more:
-                tr.issue(t + 1, None, False)
+                tr.issue(base + t + 1, None, False)
             for ks in range(NKS):
-                tr.read(0, t, ks)
-                tr.mfma(t, ks)
+                tr.read(0, base + t, ks)
+                tr.mfma(base + t, ks)
             tr.barrier()
             if more:
-                tr.write(t + 1, 0)
-    tr.waitall()
+                tr.write(base + t + 1, 0)
+
+
+def kernel_trace(S, NKS, nK, direct, ntiles=1):
+    if nK > 0 and S > 1:
+        tr = stream_loop(S, NKS, nK, ntiles, direct)
+    else:
+        tr = Trace(ntiles * nK)                  # tile by tile (S = 1, or K = 0)
+        for j in range(ntiles):
+            if S == 1:
+                single_buffer_tile(tr, j * nK, NKS, nK, direct)
+            tr.store(j)
+        tr.waitall()
+    tr.k_tiles, tr.ntiles = nK, ntiles
     return tr
-
-
-def kernel_trace(S, NKS, nK, direct):
-    if nK == 0:
-        return Trace(0)                          # the kernel skips the loop
-    if S == 1:
-        return single_buffer_loop(NKS, nK, direct)
-    return pipelined_loop(S, NKS, nK, direct)
 
 
 # ---- the checker ----------------------------------------------------------------
@@ -150,6 +164,7 @@ def check(tr, S, NKS):
     last_barrier = -1
     read_ok = {}             # (tile, ks) -> position of a valid read
     consumed = []
+    stores = []
     for pos, e in enumerate(ev):
         kind = e[0]
         if kind == "barrier":
@@ -193,8 +208,16 @@ def check(tr, S, NKS):
             tile, ks = e[1], e[2]
             assert (tile, ks) in read_ok and read_ok[(tile, ks)] < pos, "MFMA on unread fragments %s" % ((tile, ks),)
             consumed.append((tile, ks))
-    # order: each tile once, steps in order
+        elif kind == "store":
+            # output tile e[1] is complete: every MFMA of its slots done, none of a later tile's
+            j = e[1]
+            mine = [(j * tr.k_tiles + t, k) for t in range(tr.k_tiles) for k in range(NKS)]
+            assert all(m in consumed for m in mine), "output tile %d stored before its last MFMA" % j
+            assert all(c[0] < (j + 1) * tr.k_tiles for c in consumed), "output tile %d stored late" % j
+            stores.append(j)
+    # order: each slot once, steps in order; each output tile stored once, in order
     assert consumed == [(t, k) for t in range(tr.nK) for k in range(NKS)]
+    assert stores == list(range(tr.ntiles))
     # nothing in flight at the end
     assert len(completed) == len(dma)
     # no real load targets a tile >= nK
@@ -206,9 +229,10 @@ def check(tr, S, NKS):
 @pytest.mark.parametrize("direct", [True, False], ids=["direct", "register"])
 @pytest.mark.parametrize("S", [1, 2, 3, 4])
 @pytest.mark.parametrize("NKS", [1, 2])
-def test_stage_protocol(direct, S, NKS):
+@pytest.mark.parametrize("ntiles", [1, 2, 3])
+def test_stage_protocol(direct, S, NKS, ntiles):
     for nK in range(0, 13):
-        check(kernel_trace(S, NKS, nK, direct), S, NKS)
+        check(kernel_trace(S, NKS, nK, direct, ntiles), S, NKS)
 
 
 def test_checker_catches_a_missing_reuse_barrier():
@@ -238,3 +262,24 @@ def test_checker_catches_a_forgotten_epilogue_tile():
     tr.ev = [e for e in tr.ev if not (e[0] == "mfma" and e[1] == 4)]
     with pytest.raises(AssertionError):
         check(tr, 2, 2)
+
+
+def test_checker_catches_a_store_before_the_last_k_tile():
+    """Sensitivity: storing an output tile one slot early (the last K tile
+    not yet multiplied) is caught."""
+    tr = kernel_trace(2, 1, 4, True, ntiles=2)
+    ev = tr.ev
+    st = [i for i, e in enumerate(ev) if e[0] == "store"][0]
+    last_mfma = max(i for i, e in enumerate(ev) if e[0] == "mfma" and e[1] == 3)
+    ev.insert(last_mfma, ev.pop(st))
+    with pytest.raises(AssertionError):
+        check(tr, 2, 1)
+
+
+def test_checker_catches_a_ring_that_restarts_per_tile_without_a_wait():
+    """Sensitivity: a streamed ring whose next tile's first slot is read
+    before its load's wait (the cross-tile prologue overlap done wrong)."""
+    tr = kernel_trace(3, 1, 2, True, ntiles=2)
+    tr.ev = [("wait", e[1] + 1) if e[0] == "wait" and e[1] > 0 else e for e in tr.ev]
+    with pytest.raises(AssertionError):
+        check(tr, 3, 1)
