@@ -447,7 +447,8 @@ int pgemm_gemm_ex(int64_t M, int64_t N, int64_t K, double alpha, const void* A, 
     a.beta_nonzero = beta != 0.0;
     a.dbg_sleep = opts ? opts->skew : 0;
     const int grid = launch_grid(M, N, d, opts);
-    hipError_t e = d.launch(a, grid, (hipStream_t)stream);
+    const bool persistent = grid < ceil_div((int64_t)a.tiles_m * a.tiles_n, 8) * 8;
+    hipError_t e = (persistent ? d.launch_persistent : d.launch)(a, grid, (hipStream_t)stream);
     return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_HIP;
 }
 

@@ -405,6 +405,14 @@ __device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, 
 #pragma unroll
         for (int q = 0; q < C::LPS; ++q) dma_piece<C>(g, d, q, wave, lane);
     } else {
+        // With a ring (S >= 2) the chunk offsets are recomputed from an opaque
+        // copy of the lane id at every issue: hoisted out of the K loop they
+        // would hold a dozen registers for the whole loop next to the doubled
+        // fragment set and, at the register limit, spill.
+        if constexpr (C::S > 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" : "+v"(lane));
+        }
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base);
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base);
 #pragma unroll
@@ -413,7 +421,10 @@ __device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, 
             a_chunk<C>(wave, lane, q, row, kel);
             const bool ok = row < rows_left && kel < k_left;
             const uint32_t off = (uint32_t)(row * (int)g.lda + kel) * ES;
-            if constexpr (C::P == PROD_REGISTER) {
+            if (C::P == PROD_REGISTER || k_left >= C::BK || k_left % C::EPC == 0) {
+                // chunks start at multiples of EPC, so when the K tile is whole or
+                // K - k0 is a multiple of EPC no chunk straddles the end of a row:
+                // every in-range chunk is 16 whole bytes
                 st.a[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? off : OOB, 0, 0);
             } else {
                 const bool vec_ok = chunk_fits(row, kel, g.lda, rows_left, k_left, C::EPC);
@@ -426,7 +437,8 @@ __device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, 
             b_chunk<C>(wave, lane, q, krow, nel);
             const bool ok = krow < k_left && nel < n_left;
             const uint32_t off = (uint32_t)(krow * (int)g.ldb + nel) * ES;
-            if constexpr (C::P == PROD_REGISTER) {
+            if (C::P == PROD_REGISTER || n_left >= C::BN || n_left % C::EPC == 0) {
+                // likewise for the end of B's rows
                 st.b[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? off : OOB, 0, 0);
             } else {
                 const bool vec_ok = chunk_fits(krow, nel, g.ldb, k_left, n_left, C::EPC);
@@ -685,19 +697,22 @@ __device__ __forceinline__ void wg_tile_origin(const KernelArgs& g, const WgTile
     n0 = tn * C::BN;
 }
 
-// The next K-tile slot to load: K tile kt of the workgroup's i-th output
-// tile.  Slots run through all K tiles of one output tile, then the next.
+// A K-tile slot to load: K tile kt of the workgroup's i-th output tile, at
+// tile origin (m0, n0).  Slots run through all K tiles of one output tile,
+// then the next.
 struct Cursor {
-    int i, kt, m0, n0;
+    int kt, m0, n0;
 };
 
+// Cursor of absolute slot `slot` (uniform; one division, so it stays out of
+// the hot loop).
 template <class C>
-__device__ __forceinline__ void cursor_next(const KernelArgs& g, const WgTiles& w, int nK, Cursor& c) {
-    if (++c.kt == nK) {
-        c.kt = 0;
-        ++c.i;
-        wg_tile_origin<C>(g, w, c.i, c.m0, c.n0);
-    }
+__device__ __forceinline__ Cursor cursor_at(const KernelArgs& g, const WgTiles& w, int nK, int slot) {
+    Cursor c;
+    const int i = slot / nK;
+    c.kt = slot - i * nK;
+    wg_tile_origin<C>(g, w, i, c.m0, c.n0);
+    return c;
 }
 
 // One K tile of the S >= 2 pipeline.  Fragments for K step ks+1 are read
@@ -755,82 +770,126 @@ template <class C>
 __device__ __forceinline__ void store_c(const KernelArgs& g, int m0, int n0, int wm0, int wn0, int lane,
                                         typename C::T::Acc (&acc)[C::FM][C::FN]);
 
-// Compute-side bookkeeping after slot s: when it was the last K tile of an
-// output tile, write that tile (fused alpha/beta epilogue) and start the
-// next one from zero.  The loads of the following slots are already in
-// flight, so the store overlaps them (the next tile's prologue).
+// The S >= 2 pipeline of one output tile: prologue, steady state, drain.
+// The slot to load is LA K tiles ahead (S for DIRECT, S+1 for the register
+// producers); past the last K tile that lies beyond K, so every lane is out
+// of range and the slot loads nothing.
 template <class C>
-__device__ __forceinline__ void after_slot(const KernelArgs& g, const WgTiles& w, int nK, Cursor& cc,
-                                           typename C::T::Acc (&acc)[C::FM][C::FN], int wm0, int wn0, int lane) {
-    if (++cc.kt == nK) {
-        store_c<C>(g, cc.m0, cc.n0, wm0, wn0, lane, acc);
-        zero_acc<C>(acc);
-        cc.kt = 0;
-        ++cc.i;
-        wg_tile_origin<C>(g, w, cc.i, cc.m0, cc.n0);
+__device__ __forceinline__ void pertile_loop(const KernelArgs& g, int m0, int n0, int nK, char PGEMM_LDS* smem,
+                                             typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane, int wm0,
+                                             int wn0) {
+    constexpr int NKS = C::BK / C::KSTEP;
+    constexpr int LA = C::P == PROD_DIRECT ? C::S : C::S + 1;
+    Staging<C> st;
+    Frags<C> f[2];
+    // Prologue: K tiles 0 .. S-2 into stages 0 .. S-2.
+#pragma unroll
+    for (int p = 0; p < C::S - 1; ++p) {
+        issue_tile<C>(g, m0, n0, p, smem + p * C::STAGE_BYTES, st, wave, lane);
+        if constexpr (C::P != PROD_DIRECT) store_tile<C>(smem + p * C::STAGE_BYTES, st, wave, lane);
     }
+    if constexpr (C::P != PROD_DIRECT) issue_tile<C>(g, m0, n0, C::S - 1, smem, st, wave, lane);
+    sync_ring<C>();  // B_0
+    // Stage S-1 has never been used: K tile S-1 goes there now.
+    if constexpr (C::P == PROD_DIRECT) {
+        issue_tile<C>(g, m0, n0, C::S - 1, smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
+    } else {
+        store_tile<C>(smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
+        issue_tile<C>(g, m0, n0, C::S, smem, st, wave, lane);
+    }
+    read_frags<C>(smem, 0, wm0, wn0, lane, f[0]);
+    int cur = 0;
+    if constexpr (NKS % 2 == 0) {
+        for (int t = 0; t < nK; ++t)
+            tile_body<C, 0>(g, Cursor{t + LA, m0, n0}, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+    } else {
+        int t = 0;
+        for (; t + 1 < nK; t += 2) {
+            tile_body<C, 0>(g, Cursor{t + LA, m0, n0}, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+            tile_body<C, 1>(g, Cursor{t + 1 + LA, m0, n0}, t + 1, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+        }
+        if (t < nK) tile_body<C, 0>(g, Cursor{t + LA, m0, n0}, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+    }
+    // No load may still be writing LDS when the workgroup retires.
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 // The S >= 2 pipeline over all K-tile slots of the workgroup's tiles: one
 // ring, one prologue, one drain.  A workgroup with one tile runs exactly the
 // per-tile pipeline; with several, tile j+1's first K tiles load while tile
 // j's last ones are multiplied and stored.
+//
+// Each output tile's K loop has two phases.  In phase A the slot to load
+// (LA slots ahead: S for DIRECT, S+1 for the register producers, which hold
+// one more in registers) lies in the same output tile, so its cursor is
+// plain arithmetic: this is the hot loop.  Phase B covers the last LA slots,
+// whose loads belong to later tiles.
 template <class C>
 __device__ __forceinline__ void stream_loop(const KernelArgs& g, const WgTiles& w, int nK, char PGEMM_LDS* smem,
                                             typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane, int wm0,
                                             int wn0) {
     constexpr int NKS = C::BK / C::KSTEP;
+    constexpr int LA = C::P == PROD_DIRECT ? C::S : C::S + 1;
     Staging<C> st;
     Frags<C> f[2];
-    Cursor lc{0, 0, 0, 0};
-    wg_tile_origin<C>(g, w, 0, lc.m0, lc.n0);
-    Cursor cc = lc;
     // Prologue: slots 0 .. S-2 into stages 0 .. S-2.
 #pragma unroll
     for (int p = 0; p < C::S - 1; ++p) {
-        issue_tile<C>(g, lc.m0, lc.n0, lc.kt, smem + p * C::STAGE_BYTES, st, wave, lane);
+        const Cursor c = cursor_at<C>(g, w, nK, p);
+        issue_tile<C>(g, c.m0, c.n0, c.kt, smem + p * C::STAGE_BYTES, st, wave, lane);
         if constexpr (C::P != PROD_DIRECT) store_tile<C>(smem + p * C::STAGE_BYTES, st, wave, lane);
-        cursor_next<C>(g, w, nK, lc);
     }
     if constexpr (C::P != PROD_DIRECT) {
-        issue_tile<C>(g, lc.m0, lc.n0, lc.kt, smem, st, wave, lane);  // slot S-1 into registers
-        cursor_next<C>(g, w, nK, lc);
+        const Cursor c = cursor_at<C>(g, w, nK, C::S - 1);
+        issue_tile<C>(g, c.m0, c.n0, c.kt, smem, st, wave, lane);  // slot S-1 into registers
     }
     sync_ring<C>();  // B_0
     // Stage S-1 has never been used: slot S-1 goes there now.
     if constexpr (C::P == PROD_DIRECT) {
-        issue_tile<C>(g, lc.m0, lc.n0, lc.kt, smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
+        const Cursor c = cursor_at<C>(g, w, nK, C::S - 1);
+        issue_tile<C>(g, c.m0, c.n0, c.kt, smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
     } else {
+        const Cursor c = cursor_at<C>(g, w, nK, C::S);
         store_tile<C>(smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
-        issue_tile<C>(g, lc.m0, lc.n0, lc.kt, smem, st, wave, lane);  // slot S into registers
+        issue_tile<C>(g, c.m0, c.n0, c.kt, smem, st, wave, lane);  // slot S into registers
     }
-    cursor_next<C>(g, w, nK, lc);
     read_frags<C>(smem, 0, wm0, wn0, lane, f[0]);
     int cur = 0;
-    const int total = w.count * nK;
-    if constexpr (NKS % 2 == 0) {
-        for (int s = 0; s < total; ++s) {
-            tile_body<C, 0>(g, lc, s, smem, cur, st, f, acc, wave, lane, wm0, wn0);
-            cursor_next<C>(g, w, nK, lc);
-            after_slot<C>(g, w, nK, cc, acc, wm0, wn0, lane);
+    // Outer loop: the workgroup's output tiles (epilogue between them); the
+    // ring and the look-ahead fragments carry over from tile to tile.
+    for (int i = 0; i < w.count; ++i) {
+        const int s0 = i * nK;
+        int m0, n0;
+        wg_tile_origin<C>(g, w, i, m0, n0);
+        const int nA = nK > LA ? nK - LA : 0;
+        int kt = 0;
+        if constexpr (NKS % 2 == 0) {
+            for (; kt < nA; ++kt)
+                tile_body<C, 0>(g, Cursor{kt + LA, m0, n0}, s0 + kt, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+            for (; kt < nK; ++kt)
+                tile_body<C, 0>(g, cursor_at<C>(g, w, nK, s0 + kt + LA), s0 + kt, smem, cur, st, f, acc, wave, lane,
+                                wm0, wn0);
+        } else {
+            // Pairs of slots keep the fragment buffers' roles fixed at the
+            // back edge of the hot loop (one buffer live between slots).
+            for (; kt + 1 < nA; kt += 2) {
+                tile_body<C, 0>(g, Cursor{kt + LA, m0, n0}, s0 + kt, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+                tile_body<C, 1>(g, Cursor{kt + 1 + LA, m0, n0}, s0 + kt + 1, smem, cur, st, f, acc, wave, lane, wm0,
+                                wn0);
+            }
+            // The rest (at most LA + 1 slots): one slot at a time, the look-ahead
+            // fragments moved back to buffer 0 after each, so a single buffer
+            // is live at every join.
+            for (; kt < nK; ++kt) {
+                const Cursor c = kt < nA ? Cursor{kt + LA, m0, n0} : cursor_at<C>(g, w, nK, s0 + kt + LA);
+                tile_body<C, 0>(g, c, s0 + kt, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+                f[0] = f[1];
+            }
         }
-    } else {
-        // Pairs of slots keep the fragment buffers' roles fixed at the back
-        // edge (one buffer live between slots); an odd last slot follows.
-        int s = 0;
-        for (; s + 1 < total; s += 2) {
-            tile_body<C, 0>(g, lc, s, smem, cur, st, f, acc, wave, lane, wm0, wn0);
-            cursor_next<C>(g, w, nK, lc);
-            after_slot<C>(g, w, nK, cc, acc, wm0, wn0, lane);
-            tile_body<C, 1>(g, lc, s + 1, smem, cur, st, f, acc, wave, lane, wm0, wn0);
-            cursor_next<C>(g, w, nK, lc);
-            after_slot<C>(g, w, nK, cc, acc, wm0, wn0, lane);
-        }
-        if (s < total) {
-            tile_body<C, 0>(g, lc, s, smem, cur, st, f, acc, wave, lane, wm0, wn0);
-            cursor_next<C>(g, w, nK, lc);
-            after_slot<C>(g, w, nK, cc, acc, wm0, wn0, lane);
-        }
+        // Fused alpha/beta epilogue; the loads of the next tile's first slots
+        // are already in flight.
+        store_c<C>(g, m0, n0, wm0, wn0, lane, acc);
+        zero_acc<C>(acc);
     }
     // No load may still be writing LDS when the workgroup retires.
     __builtin_amdgcn_s_waitcnt(0);
@@ -959,7 +1018,10 @@ __device__ __forceinline__ void store_c(const KernelArgs& g, int m0, int n0, int
 
 // ---- the kernel -------------------------------------------------------------------------
 
-template <class C>
+// STREAM = false: one output tile per workgroup (the launch gives every
+// workgroup at most one tile), the per-tile pipeline with the epilogue after
+// it.  STREAM = true: persistent workgroups, one ring across all their tiles.
+template <class C, bool STREAM>
 __global__ void __launch_bounds__(C::NT) gemm_kernel(KernelArgs g) {
     __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_BYTES];
     char PGEMM_LDS* smem = (char PGEMM_LDS*)smem_raw;
@@ -975,21 +1037,33 @@ __global__ void __launch_bounds__(C::NT) gemm_kernel(KernelArgs g) {
     typename C::T::Acc acc[C::FM][C::FN];
     zero_acc<C>(acc);
 
-    if constexpr (C::S > 1) {
+    if constexpr (STREAM && C::S > 1) {
         if (nK > 0) {
             stream_loop<C>(g, w, nK, smem, acc, wave, lane, wm0, wn0);
             return;
         }
     }
-    // One ring slot (S = 1), or K = 0: tile by tile.
-    for (int i = 0; i < w.count; ++i) {
+    if constexpr (!STREAM) {
         int m0, n0;
-        wg_tile_origin<C>(g, w, i, m0, n0);
-        if constexpr (C::S == 1) {
-            if (nK > 0) single_buffer_loop<C>(g, m0, n0, nK, smem, acc, wave, lane, wm0, wn0);
+        wg_tile_origin<C>(g, w, 0, m0, n0);
+        if (nK > 0) {
+            if constexpr (C::S == 1)
+                single_buffer_loop<C>(g, m0, n0, nK, smem, acc, wave, lane, wm0, wn0);
+            else
+                pertile_loop<C>(g, m0, n0, nK, smem, acc, wave, lane, wm0, wn0);
         }
         store_c<C>(g, m0, n0, wm0, wn0, lane, acc);
-        zero_acc<C>(acc);
+    } else {
+        // Persistent with one ring slot (S = 1), or K = 0: tile by tile.
+        for (int i = 0; i < w.count; ++i) {
+            int m0, n0;
+            wg_tile_origin<C>(g, w, i, m0, n0);
+            if constexpr (C::S == 1) {
+                if (nK > 0) single_buffer_loop<C>(g, m0, n0, nK, smem, acc, wave, lane, wm0, wn0);
+            }
+            store_c<C>(g, m0, n0, wm0, wn0, lane, acc);
+            zero_acc<C>(acc);
+        }
     }
 }
 

@@ -11,12 +11,13 @@ typedef hipError_t (*LaunchFn)(const KernelArgs&, int grid, hipStream_t);
 struct VariantDesc {
     int dtype, bm, bn, bk, stages, wgm, wgn, producer;
     int threads, lds_bytes;
-    LaunchFn launch;
+    LaunchFn launch;             // one workgroup per output tile
+    LaunchFn launch_persistent;  // fewer workgroups, each looping over its tiles
 };
 
-template <class C>
+template <class C, bool STREAM>
 hipError_t launch_variant(const KernelArgs& a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL(gemm_kernel<C>, dim3(grid), dim3(C::NT), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<C, STREAM>), dim3(grid), dim3(C::NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -24,7 +25,8 @@ hipError_t launch_variant(const KernelArgs& a, int grid, hipStream_t s) {
     VariantDesc {                                                                         \
         D, BM, BN, BK, S, WGM, WGN, P, Cfg<D, BM, BN, BK, S, WGM, WGN, P>::NT,             \
             Cfg<D, BM, BN, BK, S, WGM, WGN, P>::LDS_BYTES,                                 \
-            &launch_variant<Cfg<D, BM, BN, BK, S, WGM, WGN, P>>                            \
+            &launch_variant<Cfg<D, BM, BN, BK, S, WGM, WGN, P>, false>,                    \
+            &launch_variant<Cfg<D, BM, BN, BK, S, WGM, WGN, P>, true>                      \
     }
 
 // Per-dtype tables, each defined in its own translation unit.

@@ -226,6 +226,7 @@ static int check_work_split() {
             std::vector<int> owner(G, -1);
             for (int b = 0; b < nb; ++b) {
                 const WgTiles w = wg_tiles_of(G, b, nb);
+                if (nb == full && w.count > 1) FAIL("G %d: default grid gives wg %d %d tiles", G, b, w.count);
                 for (int i = 0; i < w.count; ++i) {
                     const int L = w.start + w.lb + i * w.nl;
                     if (L < 0 || L >= G) FAIL("G %d grid %d: wg %d tile %d out of range", G, nb, b, L);

@@ -239,7 +239,7 @@ def test_generic_producer_misaligned(lib, dtype):
     zero every element past K or N; element-wise reads take the chunk at the
     very end of the matrix."""
     for (M, N, K, pa, pb, pc) in [(130, 77, 203, 1, 2, 3), (129, 131, 97, 0, 0, 0), (64, 5, 3, 0, 1, 0),
-                                  (200, 255, 1001, 3, 0, 1)]:
+                                  (200, 255, 1001, 3, 0, 1), (300, 272, 400, 1, 1, 0), (260, 400, 272, 1, 0, 0)]:
         for stages in (1, 2, 3, 4):
             say("misaligned", dtype, (M, N, K), "ld pads", (pa, pb, pc), "stages", stages)
             op = inputs.make_operands(dtype, M, N, K, seed=5 + K, alpha=1.0, beta=0.0, lda=K + pa, ldb=N + pb,
