@@ -116,36 +116,35 @@ double tile_efficiency(const VariantDesc& d) {
 // Register-staged producers (REGISTER, GENERIC): measured efficiency of each
 // (tile class, ring depth) pair, MI355X, seeded inputs (GENERIC on the ragged
 // 4000 x 3968 x 4001 problem with lda = 4001; REGISTER at 4096^3).  For these
-// producers the best depth is set by register pressure, not by latency: the
-// staging registers plus the doubled fragment set exceed the 256 registers a
-// wave of a two-waves-per-SIMD workgroup may hold at S >= 2 on 256 x 256
-// tiles, and the spills cost more than the deeper ring gains.  The planner
-// therefore picks the (tile, depth) pair directly from this table.
+// producers the best depth depends on register pressure as much as on
+// latency (staging registers next to the doubled fragment set, at the 256
+// registers a wave of a two-waves-per-SIMD workgroup may hold), so the
+// planner picks the (tile, depth) pair directly from this table.
 double staged_efficiency(const VariantDesc& d) {
     struct E { int dt, bm, bn, bk, s, p; double e; };
     static const E table[] = {
-        {PGEMM_BF16, 256, 256, 32, 1, PROD_GENERIC, 0.28},  {PGEMM_BF16, 256, 256, 32, 2, PROD_GENERIC, 0.32},
-        {PGEMM_BF16, 128, 128, 64, 1, PROD_GENERIC, 0.21},  {PGEMM_BF16, 128, 128, 64, 2, PROD_GENERIC, 0.21},
-        {PGEMM_BF16, 128, 128, 64, 3, PROD_GENERIC, 0.13},  {PGEMM_BF16, 128, 128, 64, 4, PROD_GENERIC, 0.13},
-        {PGEMM_F16, 256, 256, 32, 1, PROD_GENERIC, 0.28},   {PGEMM_F16, 256, 256, 32, 2, PROD_GENERIC, 0.31},
-        {PGEMM_F16, 128, 128, 64, 1, PROD_GENERIC, 0.20},   {PGEMM_F16, 128, 128, 64, 2, PROD_GENERIC, 0.21},
-        {PGEMM_F16, 128, 128, 64, 3, PROD_GENERIC, 0.13},   {PGEMM_F16, 128, 128, 64, 4, PROD_GENERIC, 0.13},
-        {PGEMM_I8, 256, 256, 64, 1, PROD_GENERIC, 0.246},   {PGEMM_I8, 256, 256, 64, 2, PROD_GENERIC, 0.21},
-        {PGEMM_I8, 128, 128, 128, 1, PROD_GENERIC, 0.11},   {PGEMM_I8, 128, 128, 128, 2, PROD_GENERIC, 0.117},
-        {PGEMM_I8, 128, 128, 128, 3, PROD_GENERIC, 0.118},  {PGEMM_I8, 128, 128, 128, 4, PROD_GENERIC, 0.116},
-        {PGEMM_F32, 256, 256, 32, 1, PROD_GENERIC, 0.745},  {PGEMM_F32, 256, 256, 32, 2, PROD_GENERIC, 0.53},
-        {PGEMM_F32, 128, 64, 16, 1, PROD_GENERIC, 0.69},    {PGEMM_F32, 128, 64, 16, 2, PROD_GENERIC, 0.64},
-        {PGEMM_F32, 128, 128, 32, 1, PROD_GENERIC, 0.67},   {PGEMM_F32, 128, 128, 32, 2, PROD_GENERIC, 0.645},
-        {PGEMM_F32, 128, 128, 32, 3, PROD_GENERIC, 0.49},   {PGEMM_F32, 128, 128, 32, 4, PROD_GENERIC, 0.495},
-        {PGEMM_BF16, 256, 256, 32, 1, PROD_REGISTER, 0.38}, {PGEMM_BF16, 256, 256, 32, 2, PROD_REGISTER, 0.34},
-        {PGEMM_BF16, 256, 256, 32, 3, PROD_REGISTER, 0.25}, {PGEMM_BF16, 256, 256, 32, 4, PROD_REGISTER, 0.256},
-        {PGEMM_BF16, 128, 128, 64, 2, PROD_REGISTER, 0.345},
-        {PGEMM_F16, 256, 256, 32, 1, PROD_REGISTER, 0.37},  {PGEMM_F16, 256, 256, 32, 2, PROD_REGISTER, 0.34},
-        {PGEMM_F16, 256, 256, 32, 3, PROD_REGISTER, 0.25},  {PGEMM_F16, 256, 256, 32, 4, PROD_REGISTER, 0.256},
-        {PGEMM_F16, 128, 128, 64, 2, PROD_REGISTER, 0.335},
-        {PGEMM_I8, 256, 256, 64, 1, PROD_REGISTER, 0.328},  {PGEMM_I8, 256, 256, 64, 2, PROD_REGISTER, 0.288},
-        {PGEMM_I8, 256, 256, 64, 3, PROD_REGISTER, 0.216},  {PGEMM_I8, 256, 256, 64, 4, PROD_REGISTER, 0.221},
-        {PGEMM_F32, 128, 64, 16, 1, PROD_REGISTER, 0.856},  {PGEMM_F32, 128, 64, 16, 2, PROD_REGISTER, 0.858},
+        {PGEMM_BF16, 256, 256, 32, 1, PROD_GENERIC, 0.259}, {PGEMM_BF16, 256, 256, 32, 2, PROD_GENERIC, 0.333},
+        {PGEMM_BF16, 128, 128, 64, 1, PROD_GENERIC, 0.141}, {PGEMM_BF16, 128, 128, 64, 2, PROD_GENERIC, 0.141},
+        {PGEMM_BF16, 128, 128, 64, 3, PROD_GENERIC, 0.071}, {PGEMM_BF16, 128, 128, 64, 4, PROD_GENERIC, 0.070},
+        {PGEMM_F16, 256, 256, 32, 1, PROD_GENERIC, 0.257},  {PGEMM_F16, 256, 256, 32, 2, PROD_GENERIC, 0.329},
+        {PGEMM_F16, 128, 128, 64, 1, PROD_GENERIC, 0.141},  {PGEMM_F16, 128, 128, 64, 2, PROD_GENERIC, 0.141},
+        {PGEMM_F16, 128, 128, 64, 3, PROD_GENERIC, 0.071},  {PGEMM_F16, 128, 128, 64, 4, PROD_GENERIC, 0.070},
+        {PGEMM_I8, 256, 256, 64, 1, PROD_GENERIC, 0.223},   {PGEMM_I8, 256, 256, 64, 2, PROD_GENERIC, 0.308},
+        {PGEMM_I8, 128, 128, 128, 1, PROD_GENERIC, 0.067},  {PGEMM_I8, 128, 128, 128, 2, PROD_GENERIC, 0.127},
+        {PGEMM_I8, 128, 128, 128, 3, PROD_GENERIC, 0.065},  {PGEMM_I8, 128, 128, 128, 4, PROD_GENERIC, 0.064},
+        {PGEMM_F32, 256, 256, 32, 1, PROD_GENERIC, 0.728},  {PGEMM_F32, 256, 256, 32, 2, PROD_GENERIC, 0.691},
+        {PGEMM_F32, 128, 64, 16, 1, PROD_GENERIC, 0.737},   {PGEMM_F32, 128, 64, 16, 2, PROD_GENERIC, 0.683},
+        {PGEMM_F32, 128, 128, 32, 1, PROD_GENERIC, 0.637},  {PGEMM_F32, 128, 128, 32, 2, PROD_GENERIC, 0.618},
+        {PGEMM_F32, 128, 128, 32, 3, PROD_GENERIC, 0.378},  {PGEMM_F32, 128, 128, 32, 4, PROD_GENERIC, 0.376},
+        {PGEMM_BF16, 256, 256, 32, 1, PROD_REGISTER, 0.400}, {PGEMM_BF16, 256, 256, 32, 2, PROD_REGISTER, 0.414},
+        {PGEMM_BF16, 256, 256, 32, 3, PROD_REGISTER, 0.409}, {PGEMM_BF16, 256, 256, 32, 4, PROD_REGISTER, 0.410},
+        {PGEMM_BF16, 128, 128, 64, 2, PROD_REGISTER, 0.300},
+        {PGEMM_F16, 256, 256, 32, 1, PROD_REGISTER, 0.385},  {PGEMM_F16, 256, 256, 32, 2, PROD_REGISTER, 0.400},
+        {PGEMM_F16, 256, 256, 32, 3, PROD_REGISTER, 0.396},  {PGEMM_F16, 256, 256, 32, 4, PROD_REGISTER, 0.395},
+        {PGEMM_F16, 128, 128, 64, 2, PROD_REGISTER, 0.293},
+        {PGEMM_I8, 256, 256, 64, 1, PROD_REGISTER, 0.326},   {PGEMM_I8, 256, 256, 64, 2, PROD_REGISTER, 0.341},
+        {PGEMM_I8, 256, 256, 64, 3, PROD_REGISTER, 0.338},   {PGEMM_I8, 256, 256, 64, 4, PROD_REGISTER, 0.346},
+        {PGEMM_F32, 128, 64, 16, 1, PROD_REGISTER, 0.858},   {PGEMM_F32, 128, 64, 16, 2, PROD_REGISTER, 0.787},
     };
     for (const E& x : table)
         if (x.dt == d.dtype && x.bm == d.bm && x.bn == d.bn && x.bk == d.bk && x.s == d.stages && x.p == d.producer)
