@@ -63,8 +63,11 @@ def make_device_operands(dtype, M, N, K, seed, alpha, beta, lda=None, ldb=None, 
     return op, op.A.cuda(), op.B.cuda(), op.C.cuda()
 
 
-def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=20, warmup=3):
-    """Average ms per call over `reps` back-to-back launches (HIP events on the launch stream)."""
+def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=20, warmup=3, trials=3):
+    """ms per call: the median over `trials` of the average over `reps`
+    back-to-back launches (HIP events on the launch stream).  The median
+    keeps one disturbed trial (clock ramp, a profiler's buffer flush) out of
+    the reported sweep points."""
     import torch
     stream = torch.cuda.current_stream()
     opts = lib._opts(producer, tile)
@@ -80,12 +83,15 @@ def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=20, war
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        call()
-    e1.record(stream)
-    e1.synchronize()
-    return e0.elapsed_time(e1) / reps
+    times = []
+    for _ in range(trials):
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    return sorted(times)[len(times) // 2]
 
 
 def tflops(M, N, K, ms):
@@ -298,6 +304,9 @@ def run_reports(lib, torch):
                        "pct_of_roof": round(100 * tflops(M, N, Ks, ms) / roof, 1),
                        "roof": "hbm" if roof < PEAK["bf16"] else "mfma",
                        "GBs": round(byts / (ms * 1e-3) / 1e9, 0)}
+        best = max(("s1", "s2", "s3", "s4"), key=lambda k: row[k]["tflops"])
+        row["best_measured"] = {"stages": best, "plan": row[best]["plan"], "tflops": row[best]["tflops"],
+                                "auto_vs_best": round(row["auto"]["tflops"] / row[best]["tflops"], 3)}
         sweep["K%d" % Ks] = row
         del A, B, C
     r = inputs.RAGGED
