@@ -94,7 +94,9 @@ typedef struct pgemm_opts {
                        workgroups (rounded up to a multiple of 8, at most one per
                        output tile), each looping over its share of the tiles
                        with one K-tile ring running across tile boundaries. */
-    int reserved[2]; /* must be 0 */
+    int waves;     /* 0 = planner's choice; else force the workgroup's wave count
+                      (with tile_m/n/k this selects one compiled variant) */
+    int reserved[1]; /* must be 0 */
 } pgemm_opts;
 
 /* What the planner chose (pgemm_plan output). */

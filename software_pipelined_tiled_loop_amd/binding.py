@@ -34,7 +34,7 @@ STATUS = {0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED_DTYPE", -3: "BAD_STAGES",
 class pgemm_opts(ctypes.Structure):
     _fields_ = [("producer", ctypes.c_int), ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int),
                 ("tile_k", ctypes.c_int), ("skew", ctypes.c_int), ("workgroups", ctypes.c_int),
-                ("reserved", ctypes.c_int * 2)]
+                ("waves", ctypes.c_int), ("reserved", ctypes.c_int * 1)]
 
 
 class pgemm_plan_info(ctypes.Structure):
@@ -101,8 +101,8 @@ def _stream(s):
     return s.cuda_stream
 
 
-def _opts(producer=None, tile=None, skew=0, workgroups=0):
-    if producer is None and tile is None and not skew and not workgroups:
+def _opts(producer=None, tile=None, skew=0, workgroups=0, waves=0):
+    if producer is None and tile is None and not skew and not workgroups and not waves:
         return None
     o = pgemm_opts()
     o.producer = PRODUCER[producer] if isinstance(producer, str) else int(producer or 0)
@@ -110,11 +110,12 @@ def _opts(producer=None, tile=None, skew=0, workgroups=0):
         o.tile_m, o.tile_n, o.tile_k = (int(v) for v in tile)
     o.skew = int(skew)
     o.workgroups = int(workgroups)
+    o.waves = int(waves)
     return o
 
 
 def _opts_from(d):
-    return _opts(d.get("producer"), d.get("tile"), d.get("skew", 0), d.get("workgroups", 0))
+    return _opts(d.get("producer"), d.get("tile"), d.get("skew", 0), d.get("workgroups", 0), d.get("waves", 0))
 
 
 def pgemm_gemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stages, stream=None):

@@ -199,9 +199,10 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligne
         want_prod = opts->producer;
     }
     const bool force_tile = opts && (opts->tile_m || opts->tile_n || opts->tile_k);
-    if (opts && (opts->skew < 0 || opts->skew > 64 || opts->workgroups < 0 || opts->reserved[0] != 0 ||
-                 opts->reserved[1] != 0))
+    if (opts && (opts->skew < 0 || opts->skew > 64 || opts->workgroups < 0 || opts->waves < 0 ||
+                 opts->reserved[0] != 0))
         return PGEMM_ERR_INVALID_ARG;
+    const int force_waves = opts ? opts->waves : 0;
 
     // Register-staged producers: the (tile, depth) pair with the best measured
     // time; an explicit depth restricts the choice to variants of that depth.
@@ -212,6 +213,7 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligne
             const VariantDesc& d = t.v[i];
             if (!producer_matches(d, want_prod)) continue;
             if (force_tile && (d.bm != opts->tile_m || d.bn != opts->tile_n || d.bk != opts->tile_k)) continue;
+            if (force_waves && d.wgm * d.wgn != force_waves) continue;
             if (stages != 0 && d.stages != stages) continue;
             const int occ = wg_per_cu(d);
             const int64_t tiles = ceil_div(M, d.bm) * ceil_div(N, d.bn);
@@ -238,6 +240,7 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligne
         const VariantDesc& d = t.v[i];
         if (!producer_matches(d, want_prod)) continue;
         if (force_tile && (d.bm != opts->tile_m || d.bn != opts->tile_n || d.bk != opts->tile_k)) continue;
+        if (force_waves && d.wgm * d.wgn != force_waves) continue;
         if (stages != 0) {
             // the tile class must offer the requested depth
             bool has = false;

@@ -80,7 +80,7 @@ def test_option_errors_before_any_launch(opts):
     r = lib.pgemm_gemm_ex(8, 8, 8, 1.0, FAKE, 8, FAKE, 8, 0.0, FAKE, 8, "bf16", 0, o, 0)
     assert r == -1, lib.pgemm_strerror(r)
     o = lib._opts(tile=(128, 128, 64))
-    o.reserved[1] = 3
+    o.reserved[0] = 3
     assert lib.pgemm_gemm_ex(8, 8, 8, 1.0, FAKE, 8, FAKE, 8, 0.0, FAKE, 8, "bf16", 0, o, 0) == -1
 
 
@@ -99,6 +99,15 @@ def test_grid_is_a_multiple_of_8_and_persistent_workgroups_are_capped():
     for want, got in ((1, 8), (8, 8), (20, 24), (256, 256), (100000, 1024)):
         r, p = lib.pgemm_plan(4096, 4096, 256, "bf16", 0, 1, {"tile": (128, 128, 64), "workgroups": want})
         assert r == 0 and p["grid"] == got, (want, p["grid"])
+
+
+def test_waves_option_selects_the_wave_layout():
+    r, p = lib.pgemm_plan(4096, 4096, 4096, "bf16", 0, 1, {"tile": (128, 128, 64), "waves": 4})
+    assert r == 0 and p["waves_m"] * p["waves_n"] == 4
+    r, _ = lib.pgemm_plan(4096, 4096, 4096, "bf16", 0, 1, {"tile": (128, 128, 64), "waves": 8})
+    assert r == -4
+    o = lib._opts(tile=(128, 128, 64), waves=-1)
+    assert lib.pgemm_gemm_ex(8, 8, 8, 1.0, FAKE, 8, FAKE, 8, 0.0, FAKE, 8, "bf16", 0, o, 0) == -1
 
 
 def test_empty_problems_are_noops():
