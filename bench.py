@@ -279,6 +279,34 @@ def run_reports(lib, torch):
                                "variants": variant_sweep(lib, op, A, B, C, M, N, K)}
         del A, B, C
 
+    # fp32 256^3 (alpha=1, beta=0): single vs double buffer on the pages' tile; launch-bound,
+    # so also timed as replays of a HIP graph of 50 calls
+    op, A, B, C = make_device_operands("f32", 256, 256, 256, inputs.seed_for(0), 1.0, 0.0)
+    small = {}
+    for s in (1, 2):
+        eager_ms = time_gemm(lib, op, A, B, C, stages=s, tile=(128, 64, 16), reps=50)
+        opts = lib._opts(None, (128, 64, 16))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(50):
+                lib.pgemm_gemm_ex(256, 256, 256, 1.0, A, 256, B, 256, 0.0, C, 256, "f32", s, opts, None)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            g.replay()
+        e1.record()
+        e1.synchronize()
+        graph_ms = e0.elapsed_time(e1) / 250
+        small["128x64x16 s%d direct" % s] = {"eager_us": round(eager_ms * 1e3, 2), "graph_us": round(graph_ms * 1e3, 2),
+                                             "tflops_graph": round(tflops(256, 256, 256, graph_ms), 2)}
+        del g
+    rep["f32_256_cfg0"] = small
+    del A, B, C
+
     # fp32: the pages' tile class, 1 vs 2 stages, and the planner's choice
     op, A, B, C = make_device_operands("f32", M, N, K, inputs.seed_for(1), 1.0, 0.5)
     d = {}
