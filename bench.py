@@ -47,13 +47,23 @@ WORKLOADS = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank runs: what the compiler sees."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the files that define the kernels (not the host planner)."""
+    """Hash of the code (comments stripped) of the files that define the
+    kernels, not the host planner: HBM traffic measured on one version stays
+    valid while only comments change."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "software_pipelined_tiled_loop_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(_code_only(open(os.path.join(csrc, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

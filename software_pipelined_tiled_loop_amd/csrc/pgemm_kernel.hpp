@@ -1,21 +1,24 @@
 // pgemm_kernel.hpp -- the software-pipelined tiled GEMM kernel for gfx950.
 //
-// One workgroup computes a BM x BN tile of C = alpha*A*B + beta*C.  Its K loop
+// A workgroup computes BM x BN tiles of C = alpha*A*B + beta*C.  Its K loop
 // runs over a ring of S LDS stages, following the prologue / steady state /
 // epilogue structure of page "Software pipelines and asynchronous copies"
 // (section "Prologue, steady state, and epilogue") and the one-barrier
 // double-buffered loop of page "Double Buffering: Software Pipelining the
 // K-Loop" (section "Two Stages, One Barrier"), generalised to S stages:
 //
-//   prologue      issue tiles 0 .. S-2 into stages 0 .. S-2 (never past nK)
-//   iteration t   s_waitcnt: tile t has landed (loads of later tiles may
-//                 still be in flight: vmcnt = loads-per-stage * their count)
-//                 s_barrier: ready edge of stage t%S for every wave, and the
-//                 reuse edge of stage (t-1)%S (every wave finished reading it)
-//                 issue tile t+S-1 into stage (t-1)%S           [if < nK]
-//                 MFMA work on stage t%S
-//   drain         the last S-1 iterations issue nothing; the wait counts
-//                 shrink so only tiles that were issued are waited for.
+//   prologue      issue K tiles 0 .. S-2 into stages 0 .. S-2
+//   iteration t   s_waitcnt: tile t+1 has landed (the loads of the S-2 later
+//                 tiles may still be in flight: vmcnt = loads-per-stage times
+//                 their count); s_barrier: ready edge of tile t+1's stage for
+//                 every wave, and reuse edge of tile t's stage (every wave
+//                 finished reading it); issue tile t+S into that stage; MFMA
+//                 work on tile t (its last K step after the barrier)
+//   drain         the loop body is the same for every t: a slot past the last
+//                 K tile issues the same number of loads with every lane out
+//                 of range (zeros into a stage nobody reads), so the wait
+//                 count is a constant and the loop has no drain branches; the
+//                 workgroup waits for everything before it retires.
 //
 // S == 1 is the single-buffer loop (load, wait, barrier, compute, barrier) of
 // the first page's section on kernel 10; with the REGISTER producer it is the
@@ -29,9 +32,16 @@
 //             stage without registers; completion observed with vmcnt.
 //   REGISTER  buffer_load_dwordx4 into VGPRs at the top of the iteration,
 //             ds_write_b128 into the stage after the MFMA work.
-//   GENERIC   element-wise buffer loads (any alignment), then as REGISTER.
+//   GENERIC   as REGISTER for any element-aligned layout: 16-byte loads at
+//             unaligned addresses, elements past K or N zeroed in registers,
+//             element loads only for a chunk at the very end of a matrix.
 // All three write byte-identical LDS images, so the arithmetic, and hence the
 // result, does not depend on the producer or on S.
+//
+// Launches: one workgroup per output tile (the per-tile pipeline, epilogue
+// after it), or persistent workgroups that stream the K tiles of all their
+// output tiles through one ring, the fused alpha/beta epilogue of each tile
+// between them.
 //
 // LDS layout (per stage): A tile as BM rows of BK elements (K contiguous),
 // B tile as BK rows of BN elements (N contiguous) -- both straight copies of

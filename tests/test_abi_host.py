@@ -4,7 +4,7 @@
 * argument errors come back before anything is launched;
 * planner invariants: LDS ring within 160 KiB, effective depth clipped to the
   number of K tiles, explicit depths honoured or refused, misaligned data
-  routed to the element-wise producer;
+  routed to the generic producer;
 * the planner's models reproduce the figures the pages print
   (tests/golden/page_models.json).
 """

@@ -8,8 +8,8 @@ finishes reading it, the producer may overwrite it (reuse).  Section
 past K and the epilogue must not consume a stage whose load was not waited
 for.
 
-This test replays the event sequence of the kernel's K loop (stream_loop /
-tile_body / after_slot / single_buffer_loop of pgemm_kernel.hpp) for every
+This test replays the event sequence of the kernel's K loop (pertile_loop /
+stream_loop / tile_body / single_buffer_loop of pgemm_kernel.hpp) for every
 producer, ring depth S = 1..4, K steps per tile NKS = 1..2, number of K tiles
 nK = 0..12 and 1..3 output tiles per workgroup (a persistent workgroup streams
 the K tiles of all its output tiles through one ring), and checks, for a
@@ -99,7 +99,7 @@ def stream_loop(S, NKS, nK, ntiles, direct):
                 tr.read(nstage, s + 1, 0)
             tr.mfma(s, ks)
         cur = nstage
-        if (s + 1) % nK == 0:                    # after_slot: last K tile of an output tile
+        if (s + 1) % nK == 0:                    # last K tile of an output tile: its epilogue
             tr.store(s // nK)
     tr.waitall()
     return tr
