@@ -281,6 +281,38 @@ def test_generic_matches_direct_on_zero_padded_copy(lib, dtype):
         check(op, run_gpu(lib, op, stages=min(depths), producer="generic", tile=tile))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_leading_dimensions_at_the_addressing_limit(lib, dtype):
+    """lda, ldb and ldc just below the 32-bit tile addressing limits the ABI
+    enforces (lda*s*256, ldb*s*128, ldc*4*256 < 2^31): the per-tile byte
+    offsets reach their largest values.  The matrices live in a few GiB of
+    device memory; padding is NaN.  One element more is refused."""
+    es = inputs.ELEM_BYTES[dtype]
+    M, N, K = 300, 136, 96
+    lda = (1 << 31) // (es * 256) - 16
+    ldb = (1 << 31) // (es * 128) - 16
+    ldc = (1 << 31) // (4 * 256) - 16
+    say("addressing limit", dtype, (M, N, K), "ld", (lda, ldb, ldc))
+    op = inputs.make_operands(dtype, M, N, K, seed=17, alpha=1.0, beta=0.5)
+    dev = torch.device("cuda:0")
+    A = torch.full((M, lda), float("nan"), dtype=op.A.dtype, device=dev)
+    B = torch.full((K, ldb), float("nan"), dtype=op.B.dtype, device=dev)
+    C = torch.full((M, ldc), float("nan"), dtype=torch.float32, device=dev)
+    A[:, :K] = op.A[:, :K].to(dev)
+    B[:, :N] = op.B[:, :N].to(dev)
+    C[:, :N] = op.C[:, :N].to(dev)
+    r = lib.pgemm_gemm(M, N, K, 1.0, A, lda, B, ldb, 0.5, C, ldc, dtype, 0)
+    assert r == 0, lib.pgemm_strerror(r)
+    torch.cuda.synchronize()
+    got = C[:, :N].cpu()
+    assert torch.isnan(C[:, N:N + 64]).all()       # the caller's memory past N is untouched
+    del A, B, C
+    torch.cuda.empty_cache()
+    check(op, got)
+    big = (1 << 31) // (4 * 256)
+    assert lib.pgemm_gemm(M, N, K, 1.0, 1 << 20, lda, 1 << 20, ldb, 0.5, 1 << 20, big, dtype, 0) == -7
+
+
 def test_beta_zero_ignores_nan_in_C_and_K0(lib):
     op = inputs.make_operands("f32", 64, 64, 0, seed=2, alpha=1.0, beta=0.0)
     got = run_gpu(lib, op)
