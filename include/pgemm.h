@@ -60,7 +60,8 @@ enum pgemm_status {
     PGEMM_ERR_BAD_STAGES = -3,         /* stages outside 0..4 */
     PGEMM_ERR_INFEASIBLE_PLAN = -4,    /* no compiled variant satisfies the forced options */
     PGEMM_ERR_NONINTEGRAL_SCALAR = -5, /* int8 with alpha or beta not an int32 integer */
-    PGEMM_ERR_HIP = -6,                /* the HIP runtime rejected the launch */
+    PGEMM_ERR_HIP = -6,                /* the HIP runtime rejected the launch (its error string is
+                                          printed to stderr) */
     PGEMM_ERR_TOO_LARGE = -7           /* a dimension or byte offset exceeds the 32-bit tile addressing */
 };
 

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdio>
 #include <cstdint>
 #include <cstring>
 
@@ -451,7 +452,14 @@ int pgemm_gemm_ex(int64_t M, int64_t N, int64_t K, double alpha, const void* A, 
     const int grid = launch_grid(M, N, d, opts);
     const bool persistent = grid < ceil_div((int64_t)a.tiles_m * a.tiles_n, 8) * 8;
     hipError_t e = (persistent ? d.launch_persistent : d.launch)(a, grid, (hipStream_t)stream);
-    return e == hipSuccess ? PGEMM_OK : PGEMM_ERR_HIP;
+    if (e != hipSuccess) {
+        // The status code alone cannot say which runtime error it was.
+        std::fprintf(stderr, "pgemm: launch of %s %dx%dx%d S=%d (grid %d) failed: %s (%d)\n",
+                     dtype == PGEMM_F32 ? "f32" : dtype == PGEMM_F16 ? "f16" : dtype == PGEMM_BF16 ? "bf16" : "i8",
+                     d.bm, d.bn, d.bk, d.stages, grid, hipGetErrorString(e), (int)e);
+        return PGEMM_ERR_HIP;
+    }
+    return PGEMM_OK;
 }
 
 int pgemm_gemm(int64_t M, int64_t N, int64_t K, double alpha, const void* A, int64_t lda, const void* B, int64_t ldb,

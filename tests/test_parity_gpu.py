@@ -305,7 +305,8 @@ def test_leading_dimensions_at_the_addressing_limit(lib, dtype):
     assert r == 0, lib.pgemm_strerror(r)
     torch.cuda.synchronize()
     got = C[:, :N].cpu()
-    assert torch.isnan(C[:, N:N + 64]).all()       # the caller's memory past N is untouched
+    untouched = bool(torch.isnan(C[:, N:N + 64]).all())
+    assert untouched                                # the caller's memory past N is untouched
     del A, B, C
     torch.cuda.empty_cache()
     check(op, got)
@@ -327,10 +328,11 @@ def test_argument_errors_before_launch(lib):
     say("errors")
     A = op.A.cuda()
     C = op.C.cuda()
-    assert lib.pgemm_gemm(8, 8, 8, 1.0, A, 4, A, 8, 0.0, C, 8, "bf16", 0) == -1  # lda < K
-    assert lib.pgemm_gemm(8, 8, 8, 1.0, A, 8, A, 8, 0.0, C, 8, 7, 0) == -2
-    assert lib.pgemm_gemm(8, 8, 8, 1.0, A, 8, A, 8, 0.0, C, 8, "bf16", 5) == -3
-    assert lib.pgemm_gemm(8, 8, 8, 0.5, A, 8, A, 8, 0.0, C, 8, "i8", 0) == -5
+    a, c = A.data_ptr(), C.data_ptr()  # plain addresses: a failing assert never prints a device tensor
+    assert lib.pgemm_gemm(8, 8, 8, 1.0, a, 4, a, 8, 0.0, c, 8, "bf16", 0) == -1  # lda < K
+    assert lib.pgemm_gemm(8, 8, 8, 1.0, a, 8, a, 8, 0.0, c, 8, 7, 0) == -2
+    assert lib.pgemm_gemm(8, 8, 8, 1.0, a, 8, a, 8, 0.0, c, 8, "bf16", 5) == -3
+    assert lib.pgemm_gemm(8, 8, 8, 0.5, a, 8, a, 8, 0.0, c, 8, "i8", 0) == -5
     assert lib.pgemm_gemm(0, 8, 8, 1.0, 0, 8, 0, 8, 0.0, 0, 8, "bf16", 0) == 0
 
 
@@ -402,6 +404,8 @@ def test_identity_B_full_size_is_exact(lib):
     A = inputs.draw("bf16", 4096, N, seed=31).cuda()
     B = torch.eye(N, dtype=torch.bfloat16).cuda()
     C = torch.empty(4096, N, dtype=torch.float32).cuda()
-    assert lib.pgemm_gemm(4096, N, N, 1.0, A, N, B, N, 0.0, C, N, "bf16", 0) == 0
+    r = lib.pgemm_gemm(4096, N, N, 1.0, A, N, B, N, 0.0, C, N, "bf16", 0)
+    assert r == 0, lib.pgemm_strerror(r)
     torch.cuda.synchronize()
-    assert torch.equal(C, A.float())
+    same = bool(torch.equal(C, A.float()))
+    assert same

@@ -53,8 +53,8 @@ def test_skewed_waves_many_runs_bit_exact(producer, stages, tile):
         C = torch.empty((M, N), dtype=torch.int32, device="cuda")
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        assert lib.pgemm_gemm_ex(M, N, K, 1, A, K, B, N, 0, C, N, "i8", stages, lib._opts(producer, tile, skew),
-                                 None) == 0
+        r = lib.pgemm_gemm_ex(M, N, K, 1, A, K, B, N, 0, C, N, "i8", stages, lib._opts(producer, tile, skew), None)
+        assert r == 0, lib.pgemm_strerror(r)
         e1.record()
         e1.synchronize()
         return e0.elapsed_time(e1) * 1e3  # us
