@@ -21,6 +21,17 @@ if not os.path.exists(LIB_PATH):
     raise ImportError("libpgemm.so is not built (run __graft_entry__.build() or "
                       "python -m software_pipelined_tiled_loop_amd.build); there is no fallback")
 
+# torch ships its own HIP and HSA runtimes under the same sonames as the ROCm
+# install the library is linked against.  Whichever is loaded first is the one
+# the other binds to; loading libpgemm.so first would leave two HIP runtimes in
+# the process, and the library's would find no device.  So torch, when
+# present, is loaded first and the library shares its runtime, its device
+# memory and its streams.
+try:
+    import torch  # noqa: F401
+except ImportError:  # a caller without torch uses the ROCm runtime directly
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 PGEMM_F32, PGEMM_F16, PGEMM_BF16, PGEMM_I8 = 0, 1, 2, 3

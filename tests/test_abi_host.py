@@ -12,6 +12,7 @@ import json
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -108,6 +109,19 @@ def test_waves_option_selects_the_wave_layout():
     assert r == -4
     o = lib._opts(tile=(128, 128, 64), waves=-1)
     assert lib.pgemm_gemm_ex(8, 8, 8, 1.0, FAKE, 8, FAKE, 8, 0.0, FAKE, 8, "bf16", 0, o, 0) == -1
+
+
+def test_binding_leaves_one_hip_runtime_in_the_process():
+    """torch bundles HIP and HSA runtimes under the sonames the library links
+    against; importing the binding before anything else must still leave one
+    copy of each (two copies made the library's runtime find no device)."""
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from software_pipelined_tiled_loop_amd import binding\n"
+            "import torch\n"
+            "libs = set(l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l or 'libhsa-runtime64' in l)\n"
+            "print(len([x for x in libs if 'amdhip64' in x]), len([x for x in libs if 'hsa-runtime64' in x]))\n" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], stdout=subprocess.PIPE, text=True, check=True).stdout.split()
+    assert out == ["1", "1"], out
 
 
 def test_empty_problems_are_noops():

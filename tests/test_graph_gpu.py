@@ -14,13 +14,7 @@ import torch
 import oracle
 from software_pipelined_tiled_loop_amd import inputs
 
-pytestmark = [
-    pytest.mark.gpu,
-    pytest.mark.skip(reason="kept off the GPU: once, run first in the whole GPU suite, the eager call "
-                            "before the capture returned an error and the process then crashed while "
-                            "printing device tensors; the cause is not found yet (the same file had passed "
-                            "when run alone)"),
-]
+pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("dtype,M,N,K,beta,stages", [
