@@ -73,11 +73,12 @@ def make_device_operands(dtype, M, N, K, seed, alpha, beta, lda=None, ldb=None, 
     return op, op.A.cuda(), op.B.cuda(), op.C.cuda()
 
 
-def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=20, warmup=3, trials=3):
+def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=20, warmup=None, trials=3):
     """ms per call: the median over `trials` of the average over `reps`
     back-to-back launches (HIP events on the launch stream).  The median
     keeps one disturbed trial (clock ramp, a profiler's buffer flush) out of
-    the reported sweep points."""
+    the reported sweep points.  Warm-up runs the kernel for at least ~20 ms
+    first, so the clock has settled whichever point is timed first."""
     import torch
     stream = torch.cuda.current_stream()
     opts = lib._opts(producer, tile)
@@ -88,10 +89,17 @@ def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=20, war
         if r != 0:
             raise lib.PgemmError(r)
 
-    for _ in range(warmup):
-        call()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    if warmup is None:
+        call()
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        e1.synchronize()
+        warmup = max(3, min(200, int(20.0 / max(e0.elapsed_time(e1), 1e-3))))
+    for _ in range(warmup):
+        call()
     torch.cuda.synchronize()
     times = []
     for _ in range(trials):
