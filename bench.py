@@ -55,15 +55,18 @@ def _code_only(text: str) -> str:
     return "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
 
 
+KERNEL_FILES = ("pgemm_kernel.hpp", "kern_f32.hip", "kern_f16.hip", "kern_bf16.hip", "kern_i8.hip")
+
+
 def kernel_source_hash() -> str:
     """Hash of the code (comments stripped) of the files that define the
-    kernels, not the host planner: HBM traffic measured on one version stays
-    valid while only comments change."""
+    kernels and their compiled variants -- not the host launcher or planner:
+    HBM traffic measured on one version stays valid while only comments or
+    host code change."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "software_pipelined_tiled_loop_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(_code_only(open(os.path.join(csrc, f)).read()).encode())
+    for f in KERNEL_FILES:
+        h.update(_code_only(open(os.path.join(csrc, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -15,10 +15,14 @@ struct VariantDesc {
     LaunchFn launch_persistent;  // fewer workgroups, each looping over its tiles
 };
 
+// hipLaunchKernel returns this launch's own status; reading the runtime's
+// last-error slot instead could report an earlier, unrelated failure.
 template <class C, bool STREAM>
 hipError_t launch_variant(const KernelArgs& a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_kernel<C, STREAM>), dim3(grid), dim3(C::NT), 0, s, a);
-    return hipGetLastError();
+    KernelArgs arg = a;
+    void* args[] = {&arg};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_kernel<C, STREAM>), dim3(grid), dim3(C::NT), args, 0,
+                           s);
 }
 
 #define PGEMM_VARIANT(D, BM, BN, BK, S, WGM, WGN, P)                                      \
