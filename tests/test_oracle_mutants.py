@@ -61,7 +61,7 @@ def _enc(dtype, vals):
 
 
 def battery(lib):
-    """True when every pin holds for this build.  Shapes keep N <= K so that a
+    """True when every pin holds for this compiled oracle.  Shapes keep N <= K so that a
     transposed-B mutant still reads inside its arrays."""
     rng = random.Random(5)
     # exact brute force, float kinds
