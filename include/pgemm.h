@@ -71,9 +71,11 @@ enum pgemm_status {
  *               with no register involvement (the cp.async analogue).
  *   REGISTER -- global memory into VGPRs at the top of the iteration, written
  *               to the LDS stage after the iteration's MFMA work.
- *   GENERIC  -- as REGISTER, for any element-aligned layout: 16-byte loads
- *               with the elements past K or N zeroed in registers, element
- *               loads for the last chunk of a matrix. */
+ *   GENERIC  -- as REGISTER, for any element-aligned layout: 16-byte loads;
+ *               in the last K tile the elements past K are zeroed in
+ *               registers and the chunk at the very end of a matrix is loaded
+ *               element by element.  Elements read past N reach only output
+ *               columns that are never stored. */
 enum pgemm_producer {
     PGEMM_PRODUCER_AUTO = 0,
     PGEMM_PRODUCER_DIRECT = 1,
@@ -163,6 +165,49 @@ int pgemm_variant_info(int index, pgemm_plan_info* out, int* dtype);
 double pgemm_model_uncovered_cycles(double latency, double compute_per_tile, int stages);
 int64_t pgemm_model_lds_bytes(int bm, int bn, int bk, int stages, int elem_bytes, int a_pad_elems_per_k);
 double pgemm_model_global_loads_per_output(int bm, int bn, int64_t K);
+
+/* Consume-before-reuse hazard demonstrator (page "Software pipelines and
+ * asynchronous copies", sections "Producer-consumer synchronization" and
+ * "Practice").  Not a GEMM: a two-stage tiled copy-and-reduce that computes
+ *
+ *     row_sums[r] = sum_c X[r*ldx + c]    for 0 <= r < rows, 0 <= c < cols
+ *
+ * in int32 (two's-complement wrap; exact and order-independent, so any
+ * difference from the plain sum is a protocol failure, not rounding).
+ * Each workgroup owns 16 rows and walks the columns in tiles of 16 x 256
+ * through two LDS stages: the loads of tile t+2 are in flight in registers
+ * while the four waves reduce tile t (four rows each) from stage t%2; then
+ * stage t%2 is rewritten with tile t+2.
+ *
+ *   reuse_wait = 1: the correct protocol, two workgroup barriers per tile:
+ *       the reuse barrier (every wave has finished reading stage t%2) before
+ *       the rewrite, the readiness barrier (the rewrite is visible) after it.
+ *   reuse_wait = 0: the same kernel with only the reuse barrier removed.  A
+ *       wave that finishes early may overwrite stage t%2 with tile t+2 while
+ *       another wave still reads tile t from it: the sums of that wave's rows
+ *       come out wrong, intermittently without a delay.  Every remaining
+ *       barrier is still executed by all waves and every address is the same
+ *       as in the correct protocol, so the variant cannot hang or fault.
+ *
+ *   delay_wave (-1 = none, else 0..3) sleeps delay_sleeps x 8128 cycles
+ *   (0..1000) before reading each tile: the artificial consumer delay.
+ *
+ *   trace (optional, NULL = off): for workgroup trace_wg, lane 0 of each wave
+ *   w records six shader-clock stamps per tile t at trace[(w*nT + t)*6 + e]:
+ *   e = 0 top of the iteration (loads of tile t+2 issued), 1 start of the
+ *   reads of stage t%2, 2 reads complete, 3 past the reuse barrier (same as 2
+ *   without it), 4 stage t%2 rewritten, 5 past the readiness barrier;
+ *   nT = cols / 256, trace_len >= 24 * nT.
+ *
+ * Layout: X row-major int32 with leading dimension ldx (elements), device
+ * pointer, 16-byte aligned; rows a multiple of 16, cols a positive multiple
+ * of 256, ldx >= cols and a multiple of 4.  row_sums: device int32[rows].
+ * All buffers belong to the caller; nothing is allocated.  Argument errors
+ * (PGEMM_ERR_INVALID_ARG) are detected before anything is enqueued; a
+ * rejected launch returns PGEMM_ERR_HIP.  Asynchronous on `stream`. */
+int pgemm_hazard_copy_reduce(const int32_t* X, int64_t rows, int64_t cols, int64_t ldx,
+                             int32_t* row_sums, int reuse_wait, int delay_wave, int delay_sleeps,
+                             int64_t* trace, int64_t trace_len, int trace_wg, void* stream);
 
 /* ABI version: major*10000 + minor*100 + patch. */
 int pgemm_version(void);

@@ -1,4 +1,5 @@
-"""The oracle: a plain, slow, obviously correct CPU GEMM (see ``oracle.c``).
+"""The oracle: a plain, slow, obviously correct CPU GEMM (see ``oracle.c``),
+and the row sums of the hazard demonstrator (``row_sums``).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
@@ -191,3 +192,25 @@ def gemm(dtype: str, M: int, N: int, K: int, alpha, A: np.ndarray, B: np.ndarray
 
 
 gemm.last_overflow = (0, 0)
+
+
+def row_sums(X: np.ndarray, rows: int, cols: int, ldx: int | None = None) -> np.ndarray:
+    """Row sums of a row-major int32 array with leading dimension ldx, wrapped
+    to int32 (two's complement).
+
+    This is the deterministic reduction that consumes each stage of the
+    copy-and-reduce of page "Software pipelines and asynchronous copies",
+    section "Practice": every element X[r, c] with c < cols enters the sum of
+    row r exactly once; padding columns (cols <= c < ldx) never do.  Each row
+    is summed exactly in int64 (|sum| < 2^63 for any int32 row shorter than
+    2^32) and then reduced modulo 2^32.
+    """
+    ldx = cols if ldx is None else ldx
+    flat = np.ascontiguousarray(X, dtype=np.int32).reshape(-1)
+    if rows and flat.size < (rows - 1) * ldx + cols:
+        raise ValueError("X holds %d elements, rows/cols/ldx need %d" % (flat.size, (rows - 1) * ldx + cols))
+    out = np.empty(rows, np.int32)
+    for r in range(rows):
+        s = int(flat[r * ldx:r * ldx + cols].astype(np.int64).sum())
+        out[r] = (s + 2 ** 31) % 2 ** 32 - 2 ** 31
+    return out

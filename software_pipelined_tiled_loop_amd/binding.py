@@ -83,10 +83,12 @@ _lib.pgemm_model_lds_bytes.argtypes = [_int, _int, _int, _int, _int, _int]
 _lib.pgemm_model_lds_bytes.restype = _i64
 _lib.pgemm_model_global_loads_per_output.argtypes = [_int, _int, _i64]
 _lib.pgemm_model_global_loads_per_output.restype = _dbl
+_lib.pgemm_hazard_copy_reduce.argtypes = [_vp, _i64, _i64, _i64, _vp, _int, _int, _int, _vp, _i64, _int, _vp]
+_lib.pgemm_hazard_copy_reduce.restype = _int
 
 EXPORTED = ("pgemm_gemm", "pgemm_gemm_ex", "pgemm_plan", "pgemm_strerror", "pgemm_num_variants",
             "pgemm_variant_info", "pgemm_version", "pgemm_model_uncovered_cycles", "pgemm_model_lds_bytes",
-            "pgemm_model_global_loads_per_output")
+            "pgemm_model_global_loads_per_output", "pgemm_hazard_copy_reduce")
 
 
 class PgemmError(RuntimeError):
@@ -207,3 +209,10 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, stages=0, producer=None, tile=None, M=Non
     if r != 0:
         raise PgemmError(r)
     return C
+
+
+def pgemm_hazard_copy_reduce(X, rows, cols, ldx, row_sums, reuse_wait, delay_wave=-1, delay_sleeps=0, trace=None,
+                             trace_len=0, trace_wg=0, stream=None):
+    return _lib.pgemm_hazard_copy_reduce(_ptr(X), rows, cols, ldx, _ptr(row_sums), int(reuse_wait), int(delay_wave),
+                                         int(delay_sleeps), _ptr(trace), int(trace_len), int(trace_wg),
+                                         _stream(stream))

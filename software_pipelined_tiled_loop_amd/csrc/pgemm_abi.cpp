@@ -124,19 +124,19 @@ double tile_efficiency(const VariantDesc& d) {
 double staged_efficiency(const VariantDesc& d) {
     struct E { int dt, bm, bn, bk, s, p; double e; };
     static const E table[] = {
-        {PGEMM_BF16, 256, 256, 32, 1, PROD_GENERIC, 0.259}, {PGEMM_BF16, 256, 256, 32, 2, PROD_GENERIC, 0.333},
-        {PGEMM_BF16, 128, 128, 64, 1, PROD_GENERIC, 0.141}, {PGEMM_BF16, 128, 128, 64, 2, PROD_GENERIC, 0.141},
-        {PGEMM_BF16, 128, 128, 64, 3, PROD_GENERIC, 0.071}, {PGEMM_BF16, 128, 128, 64, 4, PROD_GENERIC, 0.070},
-        {PGEMM_F16, 256, 256, 32, 1, PROD_GENERIC, 0.257},  {PGEMM_F16, 256, 256, 32, 2, PROD_GENERIC, 0.329},
-        {PGEMM_F16, 128, 128, 64, 1, PROD_GENERIC, 0.141},  {PGEMM_F16, 128, 128, 64, 2, PROD_GENERIC, 0.141},
-        {PGEMM_F16, 128, 128, 64, 3, PROD_GENERIC, 0.071},  {PGEMM_F16, 128, 128, 64, 4, PROD_GENERIC, 0.070},
-        {PGEMM_I8, 256, 256, 64, 1, PROD_GENERIC, 0.223},   {PGEMM_I8, 256, 256, 64, 2, PROD_GENERIC, 0.308},
-        {PGEMM_I8, 128, 128, 128, 1, PROD_GENERIC, 0.067},  {PGEMM_I8, 128, 128, 128, 2, PROD_GENERIC, 0.127},
-        {PGEMM_I8, 128, 128, 128, 3, PROD_GENERIC, 0.065},  {PGEMM_I8, 128, 128, 128, 4, PROD_GENERIC, 0.064},
-        {PGEMM_F32, 256, 256, 32, 1, PROD_GENERIC, 0.728},  {PGEMM_F32, 256, 256, 32, 2, PROD_GENERIC, 0.691},
-        {PGEMM_F32, 128, 64, 16, 1, PROD_GENERIC, 0.737},   {PGEMM_F32, 128, 64, 16, 2, PROD_GENERIC, 0.683},
-        {PGEMM_F32, 128, 128, 32, 1, PROD_GENERIC, 0.637},  {PGEMM_F32, 128, 128, 32, 2, PROD_GENERIC, 0.618},
-        {PGEMM_F32, 128, 128, 32, 3, PROD_GENERIC, 0.378},  {PGEMM_F32, 128, 128, 32, 4, PROD_GENERIC, 0.376},
+        {PGEMM_BF16, 256, 256, 32, 1, PROD_GENERIC, 0.343}, {PGEMM_BF16, 256, 256, 32, 2, PROD_GENERIC, 0.376},
+        {PGEMM_BF16, 128, 128, 64, 1, PROD_GENERIC, 0.280}, {PGEMM_BF16, 128, 128, 64, 2, PROD_GENERIC, 0.265},
+        {PGEMM_BF16, 128, 128, 64, 3, PROD_GENERIC, 0.166}, {PGEMM_BF16, 128, 128, 64, 4, PROD_GENERIC, 0.171},
+        {PGEMM_F16, 256, 256, 32, 1, PROD_GENERIC, 0.336},  {PGEMM_F16, 256, 256, 32, 2, PROD_GENERIC, 0.369},
+        {PGEMM_F16, 128, 128, 64, 1, PROD_GENERIC, 0.271},  {PGEMM_F16, 128, 128, 64, 2, PROD_GENERIC, 0.258},
+        {PGEMM_F16, 128, 128, 64, 3, PROD_GENERIC, 0.166},  {PGEMM_F16, 128, 128, 64, 4, PROD_GENERIC, 0.171},
+        {PGEMM_I8, 256, 256, 64, 1, PROD_GENERIC, 0.285},   {PGEMM_I8, 256, 256, 64, 2, PROD_GENERIC, 0.324},
+        {PGEMM_I8, 128, 128, 128, 1, PROD_GENERIC, 0.153},  {PGEMM_I8, 128, 128, 128, 2, PROD_GENERIC, 0.219},
+        {PGEMM_I8, 128, 128, 128, 3, PROD_GENERIC, 0.142},  {PGEMM_I8, 128, 128, 128, 4, PROD_GENERIC, 0.140},
+        {PGEMM_F32, 256, 256, 32, 1, PROD_GENERIC, 0.807},  {PGEMM_F32, 256, 256, 32, 2, PROD_GENERIC, 0.807},
+        {PGEMM_F32, 128, 64, 16, 1, PROD_GENERIC, 0.788},   {PGEMM_F32, 128, 64, 16, 2, PROD_GENERIC, 0.712},
+        {PGEMM_F32, 128, 128, 32, 1, PROD_GENERIC, 0.788},  {PGEMM_F32, 128, 128, 32, 2, PROD_GENERIC, 0.699},
+        {PGEMM_F32, 128, 128, 32, 3, PROD_GENERIC, 0.572},  {PGEMM_F32, 128, 128, 32, 4, PROD_GENERIC, 0.566},
         {PGEMM_BF16, 256, 256, 32, 1, PROD_REGISTER, 0.400}, {PGEMM_BF16, 256, 256, 32, 2, PROD_REGISTER, 0.414},
         {PGEMM_BF16, 256, 256, 32, 3, PROD_REGISTER, 0.409}, {PGEMM_BF16, 256, 256, 32, 4, PROD_REGISTER, 0.410},
         {PGEMM_BF16, 128, 128, 64, 2, PROD_REGISTER, 0.300},

@@ -354,6 +354,24 @@ __device__ __forceinline__ i32x4 load_chunk_any(__amdgpu_buffer_rsrc_t r, uint32
     return load_chunk_elementwise<ES>(r, off, valid);
 }
 
+// GENERIC producer: true when every chunk of the K tile whose remaining
+// extents from the tile origin are k_left and n_left may be read as one whole
+// 16-byte load, so the tile's loads form one straight run with no waits
+// between them.  Chunks start at multiples of EPC, so no A chunk straddles the
+// end of K when the K tile is whole or k_left is a multiple of EPC; likewise
+// for B and N.  A B chunk that does straddle N carries the first elements of
+// B's next row into columns >= N, which feed only outputs that are never
+// stored; before the last K tile (k_left > BK) at least one more row of B lies
+// beyond it, which holds the overrun when ldb >= EPC.  Otherwise (only ever in
+// the last K tile) each chunk is loaded by load_chunk_any.  Past the last K
+// tile (k_left <= 0) every chunk is out of range and loads nothing.
+template <class C>
+PGEMM_HD bool whole_loads(int k_left, int n_left, int64_t ldb) {
+    const bool a_whole = k_left >= C::BK || k_left % C::EPC == 0;
+    const bool b_whole = n_left >= C::BN || n_left % C::EPC == 0;
+    return k_left <= 0 || (a_whole && (b_whole || (k_left > C::BK && ldb >= C::EPC)));
+}
+
 // DIRECT producer state for one K tile: buffer descriptors of the tile's A
 // and B panels, the LDS bases of the stage and the remaining extents.
 struct DmaTile {
@@ -425,32 +443,39 @@ __device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, 
         }
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base);
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base);
+        if (C::P == PROD_REGISTER || whole_loads<C>(k_left, n_left, g.ldb)) {
 #pragma unroll
-        for (int q = 0; q < C::A_INSTR; ++q) {
-            int row, kel;
-            a_chunk<C>(wave, lane, q, row, kel);
-            const bool ok = row < rows_left && kel < k_left;
-            const uint32_t off = (uint32_t)(row * (int)g.lda + kel) * ES;
-            if (C::P == PROD_REGISTER || k_left >= C::BK || k_left % C::EPC == 0) {
-                // chunks start at multiples of EPC, so when the K tile is whole or
-                // K - k0 is a multiple of EPC no chunk straddles the end of a row:
-                // every in-range chunk is 16 whole bytes
-                st.a[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? off : OOB, 0, 0);
-            } else {
+            for (int q = 0; q < C::A_INSTR; ++q) {
+                int row, kel;
+                a_chunk<C>(wave, lane, q, row, kel);
+                const bool ok = row < rows_left && kel < k_left;
+                st.a[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? (uint32_t)(row * (int)g.lda + kel) * ES : OOB,
+                                                                0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < C::B_INSTR; ++q) {
+                int krow, nel;
+                b_chunk<C>(wave, lane, q, krow, nel);
+                const bool ok = krow < k_left && nel < n_left;
+                st.b[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? (uint32_t)(krow * (int)g.ldb + nel) * ES : OOB,
+                                                                0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < C::A_INSTR; ++q) {
+                int row, kel;
+                a_chunk<C>(wave, lane, q, row, kel);
+                const bool ok = row < rows_left && kel < k_left;
+                const uint32_t off = (uint32_t)(row * (int)g.lda + kel) * ES;
                 const bool vec_ok = chunk_fits(row, kel, g.lda, rows_left, k_left, C::EPC);
                 st.a[q] = load_chunk_any<ES>(ra, off, ok ? min(C::EPC, k_left - kel) : 0, vec_ok);
             }
-        }
 #pragma unroll
-        for (int q = 0; q < C::B_INSTR; ++q) {
-            int krow, nel;
-            b_chunk<C>(wave, lane, q, krow, nel);
-            const bool ok = krow < k_left && nel < n_left;
-            const uint32_t off = (uint32_t)(krow * (int)g.ldb + nel) * ES;
-            if (C::P == PROD_REGISTER || n_left >= C::BN || n_left % C::EPC == 0) {
-                // likewise for the end of B's rows
-                st.b[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? off : OOB, 0, 0);
-            } else {
+            for (int q = 0; q < C::B_INSTR; ++q) {
+                int krow, nel;
+                b_chunk<C>(wave, lane, q, krow, nel);
+                const bool ok = krow < k_left && nel < n_left;
+                const uint32_t off = (uint32_t)(krow * (int)g.ldb + nel) * ES;
                 const bool vec_ok = chunk_fits(krow, nel, g.ldb, k_left, n_left, C::EPC);
                 st.b[q] = load_chunk_any<ES>(rb, off, ok ? min(C::EPC, n_left - nel) : 0, vec_ok);
             }

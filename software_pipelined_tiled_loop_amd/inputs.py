@@ -13,6 +13,11 @@ benchmark configurations of this library:
   fp16/bf16 A, B i.i.d. normal(0, 1) rounded to the dtype (round-to-nearest-even)
   int8    A, B i.i.d. uniform over the integers [-128, 127]
 
+The hazard demonstrator (page "Software pipelines and asynchronous copies",
+section "Practice": randomized input to a copy-and-reduce over a 4096 x 4096
+array) takes int32 i.i.d. uniform over [-32768, 32767], with any padding
+columns set to POISON_I32 so that a read past the columns is caught.
+
 When beta == 0, C is pre-filled with a poison value (NaN for float, 0x7F7F7F7F
 for int32) so a kernel that reads C when it must not is caught.
 
@@ -134,3 +139,11 @@ CONFIGS = {
             K_sweep=(32, 64, 256, 1024, 4096, 16384), alpha=1.0, beta=0.0),
 }
 RAGGED = dict(dtype="bf16", M=4000, N=3968, K=4001, lda=4001, ldb=3968, ldc=3968)
+
+
+def make_hazard_input(rows: int, cols: int, seed: int, ldx: int | None = None) -> torch.Tensor:
+    """A rows x ldx int32 CPU tensor: columns < cols uniform over [-32768, 32767], the rest POISON_I32."""
+    ldx = cols if ldx is None else ldx
+    X = torch.full((rows, ldx), POISON_I32, dtype=torch.int32)
+    X[:, :cols] = torch.randint(-32768, 32768, (rows, cols), generator=_gen(seed), dtype=torch.int32)
+    return X

@@ -19,6 +19,7 @@
 #include <algorithm>
 #include <vector>
 
+#include "../software_pipelined_tiled_loop_amd/csrc/hazard_demo.hpp"
 #include "../software_pipelined_tiled_loop_amd/csrc/pgemm_kernel.hpp"
 
 using namespace pgemm;
@@ -213,6 +214,135 @@ static int check_chunk_fits() {
     return cases;
 }
 
+// The generic producer's choice of whole 16-byte loads for a K tile
+// (whole_loads), over the exact chunk sets of tile class C, for remaining
+// extents k_left, n_left around every boundary and leading dimensions from the
+// smallest up.  Whenever whole loads are chosen, every in-range chunk's read
+// ends at or before the last element of its matrix, and no in-range A chunk
+// reaches past K (elements past N in a B chunk feed only outputs that are
+// never stored).  K tiles before the last one always take whole loads when
+// ldb >= EPC.
+template <class C>
+static int check_whole_loads(const char* name) {
+    constexpr int EPC = C::EPC, BK = C::BK, BN = C::BN;
+    std::vector<std::pair<int, int>> ach, bch;
+    for (int w = 0; w < C::NW; ++w)
+        for (int l = 0; l < 64; ++l) {
+            for (int q = 0; q < C::A_INSTR; ++q) {
+                int row, kel;
+                a_chunk<C>(w, l, q, row, kel);
+                ach.push_back({row, kel});
+            }
+            for (int q = 0; q < C::B_INSTR; ++q) {
+                int krow, nel;
+                b_chunk<C>(w, l, q, krow, nel);
+                bch.push_back({krow, nel});
+            }
+        }
+    int cases = 0;
+    std::vector<int> ks = {-BK, 3 * BK + 5};
+    for (int k = -1; k <= 2 * BK + 1; ++k) ks.push_back(k);
+    std::vector<int> ns;
+    for (int n = 1; n <= 3 * EPC; ++n) ns.push_back(n);
+    for (int n = BN - 3 * EPC; n <= BN + 2 * EPC; ++n) ns.push_back(n);
+    for (int k_left : ks)
+        for (int n_left : ns)
+            for (int ldb = n_left; ldb <= n_left + EPC + 1; ++ldb) {
+                const bool whole = whole_loads<C>(k_left, n_left, ldb);
+                if (!whole && k_left > BK && ldb >= EPC) FAIL("K tile before the last not on whole loads");
+                if (!whole || k_left <= 0) continue;
+                ++cases;
+                const long b_last = (long)(k_left - 1) * ldb + n_left - 1;
+                for (auto [krow, nel] : bch)
+                    if (krow < k_left && nel < n_left && (long)krow * ldb + nel + EPC - 1 > b_last)
+                        FAIL("B chunk (%d,%d) k_left %d n_left %d ldb %d reads past B", krow, nel, k_left, n_left, ldb);
+                for (auto [row, kel] : ach)
+                    if (kel < k_left && kel + EPC > k_left) FAIL("A chunk (%d,%d) straddles K, k_left %d", row, kel, k_left);
+                if (n_left != ns[0] || ldb != n_left) continue;  // A's reads do not depend on N
+                for (int rows_left : {1, 2, C::BM})
+                    for (int lda : {k_left, k_left + 1, k_left + EPC}) {
+                        const long a_last = (long)(rows_left - 1) * lda + k_left - 1;
+                        for (auto [row, kel] : ach)
+                            if (row < rows_left && kel < k_left && (long)row * lda + kel + EPC - 1 > a_last)
+                                FAIL("A chunk (%d,%d) reads past A", row, kel);
+                    }
+            }
+    return cases;
+}
+
+// Hazard demonstrator indexing (hazard_demo.hpp), for the shapes and leading
+// dimensions the entry point admits: every global read (tiles 0, 1 and, per
+// iteration, t+2 or t) lies inside the caller's rows x cols, every LDS index
+// inside a stage, every row sum and timeline stamp inside its buffer; the
+// producers fill each stage chunk exactly once and the consumers read each
+// exactly once, wave w the rows 4w..4w+3; and every wave's rows are written
+// by other waves, so a missing reuse barrier can corrupt them.
+static int check_hazard_indexing() {
+    using namespace hazard;
+    const char* name = "hazard";
+    int cases = 0;
+    for (int rows : {16, 48})
+        for (int cols : {256, 512, 1280})
+            for (int ldx : {cols, cols + 4, cols + 260}) {
+                const int nT = cols / TC, grid = rows / RB;
+                for (int b = 0; b < grid; ++b)
+                    for (int t = -1; t < nT; ++t) {
+                        // t = -1: the prologue's tiles 0 and 1; else the loop's load
+                        std::vector<int> tiles;
+                        if (t < 0) {
+                            tiles.push_back(0);
+                            if (nT > 1) tiles.push_back(1);
+                        } else {
+                            tiles.push_back(t + 2 < nT ? t + 2 : t);
+                        }
+                        for (int tt : tiles)
+                            for (int tid = 0; tid < NTH; ++tid)
+                                for (int j = 0; j < CPT; ++j) {
+                                    const int c = prod_chunk(tid, j);
+                                    if (c < 0 || c >= CHUNKS) FAIL("stage index %d", c);
+                                    const int64_t off = (int64_t)b * RB * ldx + x_offset(ldx, chunk_row(c), tt, chunk_col(c));
+                                    const int64_t r = off / ldx, col = off % ldx;
+                                    if (off < 0 || r >= rows || col + 3 >= cols)
+                                        FAIL("read (%lld,%lld) outside %dx%d ld %d", (long long)r, (long long)col, rows, cols, ldx);
+                                    if (r != b * RB + chunk_row(c) || col != tt * TC + chunk_col(c)) FAIL("chunk placement");
+                                    ++cases;
+                                }
+                    }
+                for (int w = 0; w < NWAVE; ++w)
+                    for (int t = 0; t < nT; ++t)
+                        for (int e = 0; e < EV; ++e)
+                            if (trace_index(w, nT, t, e) < 0 || trace_index(w, nT, t, e) >= (int64_t)NWAVE * EV * nT)
+                                FAIL("trace index");
+                for (int b = 0; b < grid; ++b)
+                    for (int w = 0; w < NWAVE; ++w)
+                        for (int rr = 0; rr < ROWS_PER_WAVE; ++rr)
+                            if (b * RB + ROWS_PER_WAVE * w + rr >= rows) FAIL("row sum index");
+            }
+    std::vector<int> prod(CHUNKS, 0), cons(CHUNKS, 0);
+    for (int tid = 0; tid < NTH; ++tid)
+        for (int j = 0; j < CPT; ++j) prod[prod_chunk(tid, j)]++;
+    for (int w = 0; w < NWAVE; ++w)
+        for (int l = 0; l < 64; ++l)
+            for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
+                const int c = cons_chunk(w, l, rr);
+                if (c < 0 || c >= CHUNKS) FAIL("consumer index %d", c);
+                if (chunk_row(c) != ROWS_PER_WAVE * w + rr || chunk_col(c) != 4 * l) FAIL("consumer placement");
+                cons[c]++;
+            }
+    for (int c = 0; c < CHUNKS; ++c)
+        if (prod[c] != 1 || cons[c] != 1) FAIL("chunk %d produced %d, consumed %d times", c, prod[c], cons[c]);
+    for (int w = 0; w < NWAVE; ++w) {
+        bool foreign = false;
+        for (int tid = 0; tid < NTH; ++tid)
+            for (int j = 0; j < CPT; ++j) {
+                const int row = chunk_row(prod_chunk(tid, j));
+                if (tid / 64 != w && row / ROWS_PER_WAVE == w) foreign = true;
+            }
+        if (!foreign) FAIL("rows of wave %d written only by itself", w);
+    }
+    return cases;
+}
+
 // Work split: for every tile count and grid (a multiple of 8, at most one
 // workgroup per tile rounded up to 8, as the host launches), each logical tile
 // goes to exactly one workgroup, each XCD (b % 8) gets a contiguous range,
@@ -261,12 +391,13 @@ static int check_work_split() {
 #define CHECK(D, BM, BN, BK, WGM, WGN)                                              \
     do {                                                                           \
         emulate<Cfg<D, BM, BN, BK, 2, WGM, WGN, PROD_DIRECT>>(#D " " #BM "x" #BN "x" #BK); \
+        wl += check_whole_loads<Cfg<D, BM, BN, BK, 2, WGM, WGN, PROD_GENERIC>>("whole_loads " #D); \
         ++n;                                                                       \
         printf("class %d %d %d %d %d %d\n", D, BM, BN, BK, WGM, WGN);              \
     } while (0)
 
 int main() {
-    int n = 0;
+    int n = 0, wl = 0;
     CHECK(DT_BF16, 256, 256, 32, 2, 4);
     CHECK(DT_BF16, 256, 256, 64, 2, 4);
     CHECK(DT_BF16, 128, 128, 64, 2, 2);
@@ -279,8 +410,10 @@ int main() {
     CHECK(DT_F32, 128, 64, 16, 2, 2);
     CHECK(DT_F32, 256, 256, 32, 2, 4);
     CHECK(DT_F32, 128, 128, 32, 2, 2);
+    printf("whole_loads %d cases\n", wl);
     printf("chunk_fits %d cases\n", check_chunk_fits());
     printf("work_split %d cases\n", check_work_split());
+    printf("hazard %d cases\n", check_hazard_indexing());
     printf("OK %d\n", n);
     return 0;
 }

@@ -5,7 +5,11 @@ functions on the CPU: producer placement into an LDS stage (each byte written
 exactly once), the fragment reads with the probed lane semantics of
 ds_read_b128 / ds_read_b64_tr_b16 / ds_read_b64_tr_b8 / ds_read_b32 (every read
 inside its region), and the MFMA lane layouts, compared with a naive GEMM of
-the tile.  No GPU is used; hipcc only compiles host code here.
+the tile.  It also checks by brute force the generic producer's choice of
+whole 16-byte loads (every admitted read inside its matrix, none of A past K)
+and the hazard demonstrator's indexing (every read, LDS, row-sum and timeline
+index inside its buffer; each stage chunk produced and consumed exactly once).
+No GPU is used; hipcc only compiles host code here.
 """
 import os
 import re
@@ -32,6 +36,8 @@ def test_emulated_data_path_matches_naive_gemm(tmp_path):
     assert out.strip().splitlines()[-1].startswith("OK"), out[-2000:]
     assert re.search(r"^chunk_fits \d+ cases$", out, re.M), out[-2000:]
     assert re.search(r"^work_split \d+ cases$", out, re.M), out[-2000:]
+    assert re.search(r"^whole_loads \d+ cases$", out, re.M), out[-2000:]
+    assert re.search(r"^hazard \d+ cases$", out, re.M), out[-2000:]
     emulated = set(tuple(int(x) for x in m) for m in re.findall(r"^class (\d+) (\d+) (\d+) (\d+) (\d+) (\d+)$", out, re.M))
     # every tile class the library compiles is emulated
     for i in range(lib.pgemm_num_variants()):

@@ -16,6 +16,11 @@ semantics of page "Double Buffering: Software Pipelining the K-Loop", section
   * int8 results reduced modulo 2^32 match Python's unbounded integers;
   * beta == 0 never reads C0 (NaN poison stays out), K == 0 gives beta*C0,
     and padding beyond K / N (NaN-filled) is never read.
+
+The hazard demonstrator's row sums (oracle.row_sums) are pinned by closed
+forms (X[r, c] = r*cols + c, constant rows), Python's unbounded integers
+reduced modulo 2^32 on random rows with and without padding, and the wrap of
+two int32 maxima.
 """
 import itertools
 import math
@@ -250,3 +255,31 @@ def test_rejects_bad_arguments():
         oracle.gemm("f32", 3, 2, 2, 1.0, a, a)
     with pytest.raises(ValueError):
         oracle.gemm("i8", 2, 2, 2, 0.5, a.astype(np.int8), a.astype(np.int8))
+
+
+def test_row_sums_closed_forms():
+    rows, cols = 7, 300
+    X = (np.arange(rows, dtype=np.int64)[:, None] * cols + np.arange(cols)).astype(np.int32)
+    expect = [r * cols * cols + cols * (cols - 1) // 2 for r in range(rows)]
+    assert oracle.row_sums(X, rows, cols).tolist() == expect
+    assert oracle.row_sums(np.full((3, 5), -7, np.int32), 3, 5).tolist() == [-35] * 3
+
+
+def test_row_sums_match_unbounded_integers_modulo_2_32():
+    rng = random.Random(11)
+    for rows, cols, ldx in [(1, 1, 1), (3, 5, 5), (4, 9, 13), (5, 256, 260), (2, 1000, 1000)]:
+        vals = [[rng.randint(-2 ** 31, 2 ** 31 - 1) for _ in range(ldx)] for _ in range(rows)]
+        X = np.array(vals, np.int64).astype(np.int32)
+        got = oracle.row_sums(X, rows, cols, ldx)
+        for r in range(rows):
+            s = sum(vals[r][:cols])  # columns past cols are padding
+            assert int(got[r]) == (s + 2 ** 31) % 2 ** 32 - 2 ** 31
+
+
+def test_row_sums_wrap_and_ignore_poisoned_padding():
+    X = np.array([[2 ** 31 - 1, 2 ** 31 - 1, inputs.POISON_I32]], np.int32)
+    assert oracle.row_sums(X, 1, 2, 3).tolist() == [-2]
+    X = inputs.make_hazard_input(32, 256, seed=3, ldx=260).numpy()
+    assert (X[:, 256:] == inputs.POISON_I32).all()
+    ref = X[:, :256].astype(np.int64).sum(axis=1)
+    assert oracle.row_sums(X, 32, 256, 260).tolist() == ref.tolist()

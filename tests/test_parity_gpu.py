@@ -235,11 +235,15 @@ def test_edge_sizes(lib, dtype):
 def test_generic_producer_misaligned(lib, dtype):
     """Odd K, N and leading dimensions select the generic producer.  Its
     16-byte reads cross the end of a row (into NaN/0x7F padding when the
-    leading dimension is padded, into the next row when it is tight) and must
-    zero every element past K or N; element-wise reads take the chunk at the
-    very end of the matrix."""
+    leading dimension is padded, into the next row when it is tight).  Past K
+    every element must be zero; past N the elements only feed columns that are
+    never stored.  The last K tile reads chunk by chunk, element-wise at the
+    very end of the matrix.  The narrow shapes put ldb below and just above 16
+    bytes over many K tiles: below, every K tile takes the chunk-by-chunk path;
+    above, whole reads spill into the next row of B."""
     for (M, N, K, pa, pb, pc) in [(130, 77, 203, 1, 2, 3), (129, 131, 97, 0, 0, 0), (64, 5, 3, 0, 1, 0),
-                                  (200, 255, 1001, 3, 0, 1), (300, 272, 400, 1, 1, 0), (260, 400, 272, 1, 0, 0)]:
+                                  (200, 255, 1001, 3, 0, 1), (300, 272, 400, 1, 1, 0), (260, 400, 272, 1, 0, 0),
+                                  (70, 3, 300, 0, 0, 0), (70, 6, 300, 1, 1, 0), (33, 17, 500, 0, 0, 1)]:
         for stages in (1, 2, 3, 4):
             say("misaligned", dtype, (M, N, K), "ld pads", (pa, pb, pc), "stages", stages)
             op = inputs.make_operands(dtype, M, N, K, seed=5 + K, alpha=1.0, beta=0.0, lda=K + pa, ldb=N + pb,
@@ -251,11 +255,11 @@ def test_generic_producer_misaligned(lib, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
 def test_generic_matches_direct_on_zero_padded_copy(lib, dtype):
-    """The generic producer on an odd-sized problem fills each LDS stage with
-    exactly the bytes the direct producer copies from a zero-padded, aligned
-    copy of the same matrices (K and N rounded up to 16 bytes), so within one
-    tile class C is bit-identical, for every tile class and depth the generic
-    producer is compiled for."""
+    """The generic producer on an odd-sized problem fills each LDS stage, in
+    every column below N, with exactly the bytes the direct producer copies
+    from a zero-padded, aligned copy of the same matrices (K and N rounded up
+    to 16 bytes), so within one tile class the stored C is bit-identical, for
+    every tile class and depth the generic producer is compiled for."""
     epc = 16 // inputs.ELEM_BYTES[dtype]
     classes = {}
     for i in range(lib.pgemm_num_variants()):
