@@ -15,7 +15,7 @@ static const VariantDesc k_table[] = {
     V(128, 128, 64, 1, 2, 2, PROD_DIRECT),   V(128, 128, 64, 2, 2, 2, PROD_DIRECT),
     V(128, 128, 64, 3, 2, 2, PROD_DIRECT),   V(128, 128, 64, 4, 2, 2, PROD_DIRECT),
     V(128, 128, 64, 2, 2, 2, PROD_REGISTER),
-    // element-wise producer for misaligned operands
+    // generic producer for misaligned operands
     V(128, 128, 64, 1, 2, 2, PROD_GENERIC),  V(128, 128, 64, 2, 2, 2, PROD_GENERIC),
     V(128, 128, 64, 3, 2, 2, PROD_GENERIC),  V(128, 128, 64, 4, 2, 2, PROD_GENERIC),
     V(256, 256, 32, 1, 2, 4, PROD_GENERIC), V(256, 256, 32, 2, 2, 4, PROD_GENERIC),

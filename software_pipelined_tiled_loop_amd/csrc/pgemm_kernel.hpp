@@ -33,10 +33,13 @@
 //   REGISTER  buffer_load_dwordx4 into VGPRs at the top of the iteration,
 //             ds_write_b128 into the stage after the MFMA work.
 //   GENERIC   as REGISTER for any element-aligned layout: 16-byte loads at
-//             unaligned addresses, elements past K or N zeroed in registers,
-//             element loads only for a chunk at the very end of a matrix.
-// All three write byte-identical LDS images, so the arithmetic, and hence the
-// result, does not depend on the producer or on S.
+//             unaligned addresses; in the last K tile, elements past K zeroed
+//             in registers and element loads for a chunk at the very end of a
+//             matrix.
+// All three write the same LDS bytes for every element inside the matrix and
+// zeros past K and M (the generic producer may leave other values in columns
+// past N, which feed only outputs that are never stored), so the stored result
+// does not depend on the producer or on S.
 //
 // Launches: one workgroup per output tile (the per-tile pipeline, epilogue
 // after it), or persistent workgroups that stream the K tiles of all their
