@@ -11,7 +11,7 @@ the stage-count sweep (1 vs 2 vs 3-4 stages) and producer comparison, and
 the bf16 K-sweep with the ragged 4000 x 3968 x 4001 shape.  The oracle is
 timed on a bounded sample of the headline workload on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--quick] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 40] [--quick] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -76,12 +76,18 @@ def make_device_operands(dtype, M, N, K, seed, alpha, beta, lda=None, ldb=None, 
     return op, op.A.cuda(), op.B.cuda(), op.C.cuda()
 
 
+WARMUP_MS = 150.0
+
+
 def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=20, warmup=None, trials=3):
     """ms per call: the median over `trials` of the average over `reps`
     back-to-back launches (HIP events on the launch stream).  The median
     keeps one disturbed trial (clock ramp, a profiler's buffer flush) out of
-    the reported sweep points.  Warm-up runs the kernel for at least ~20 ms
-    first, so the clock has settled whichever point is timed first."""
+    the reported sweep points.  Warm-up runs the kernel for about
+    WARMUP_MS first: after the GPU has idled (while the host draws the next
+    operands) its clock takes on the order of 100 ms of load to settle, and
+    with a 20 ms warm-up the first of several successive timings of one
+    kernel read 10-13 % low."""
     import torch
     stream = torch.cuda.current_stream()
     opts = lib._opts(producer, tile)
@@ -100,7 +106,7 @@ def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=20, war
         call()
         e1.record(stream)
         e1.synchronize()
-        warmup = max(3, min(200, int(20.0 / max(e0.elapsed_time(e1), 1e-3))))
+        warmup = max(3, min(20000, int(WARMUP_MS / max(e0.elapsed_time(e1), 1e-3))))
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -171,7 +177,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="f32", choices=sorted(WORKLOADS),
