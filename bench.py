@@ -60,13 +60,15 @@ KERNEL_FILES = ("pgemm_kernel.hpp", "kern_f32.hip", "kern_f16.hip", "kern_bf16.h
 
 def kernel_source_hash() -> str:
     """Hash of the code (comments stripped) of the files that define the
-    kernels and their compiled variants -- not the host launcher or planner:
-    HBM traffic measured on one version stays valid while only comments or
-    host code change."""
+    kernels and their compiled variants, and of the hipcc flags they are built
+    with -- not the host launcher or planner: HBM traffic measured on one
+    version stays valid while only comments or host code change."""
+    from software_pipelined_tiled_loop_amd import build
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "software_pipelined_tiled_loop_amd", "csrc")
     for f in KERNEL_FILES:
         h.update(_code_only(open(os.path.join(csrc, f)).read()).encode())
+    h.update(" ".join(build.HIPCC_FLAGS).encode())
     return h.hexdigest()[:16]
 
 

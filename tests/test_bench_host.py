@@ -1,0 +1,67 @@
+"""Host-side checks of bench.py (no GPU needed).
+
+* More than one GPU is refused with a message, before anything touches a GPU.
+* The kernel source hash ignores comments and blank lines but sees code and
+  build flags, so HBM traffic from profiles/traffic.json is reported only for
+  the kernel version that was profiled.
+* The algorithmic byte count of the headline workload.
+* Every benchmark workload has a plan.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+from software_pipelined_tiled_loop_amd import binding as lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    for args, env in (([" --gpus", "2"], {}), ([], {"WORLD_SIZE": "2"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + [a.strip() for a in args],
+                           capture_output=True, text=True, env=dict(os.environ, **env), timeout=120)
+        assert r.returncode == 2, r.stderr
+        assert "one GPU" in r.stderr or "single MI355X" in r.stderr
+
+
+def test_code_only_ignores_comments_and_layout():
+    a = "int x = 1; // one\n/* block\n comment */\n\n  int   y = 2;\n"
+    b = "int x = 1;\nint y = 2;"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(b.replace("2", "3"))
+
+
+def test_source_hash_is_stable_and_covers_build_flags(monkeypatch):
+    h = bench.kernel_source_hash()
+    assert h == bench.kernel_source_hash() and len(h) == 16
+    from software_pipelined_tiled_loop_amd import build
+    monkeypatch.setattr(build, "HIPCC_FLAGS", build.HIPCC_FLAGS + ["-O0"])
+    assert bench.kernel_source_hash() != h
+
+
+def test_traffic_only_for_the_profiled_sources():
+    d = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    entries = {k: v for k, v in d.items() if not k.startswith("_")}
+    assert entries
+    for key, e in entries.items():
+        assert bench.load_traffic(key, e["kernel_source_hash"]) == e["bytes_per_launch"]
+        assert bench.load_traffic(key, "0" * 16) is None
+        assert abs(e["bytes_per_launch"] - e["read_bytes"] - e["write_bytes"]) <= 1  # each rounded down
+    assert bench.load_traffic("no_such_kernel", bench.kernel_source_hash()) is None
+
+
+def test_headline_algorithmic_bytes():
+    # A and B read once, C read (beta != 0) and written once, fp32
+    assert bench.algorithmic_bytes("f32", 4096, 4096, 4096, 0.5) == 4 * 4096 * 4096 * 4
+    assert bench.algorithmic_bytes("bf16", 4096, 4096, 4096, 0.0) == 2 * 4096 * 4096 * 2 + 4096 * 4096 * 4
+
+
+def test_every_workload_has_a_plan():
+    from software_pipelined_tiled_loop_amd import inputs
+    for name, w in bench.WORKLOADS.items():
+        dt, M, N, K = w["dtype"], w["M"], w["N"], w["K"]
+        lda, ldb = w.get("lda", K), w.get("ldb", N)
+        aligned = int(all(x * inputs.ELEM_BYTES[dt] % 16 == 0 for x in (lda, ldb, K, N)))
+        assert bench.plan_of(lib, dt, M, N, K, aligned=aligned) is not None, name
