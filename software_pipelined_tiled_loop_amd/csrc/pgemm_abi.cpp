@@ -3,14 +3,18 @@
 // The planner picks (tile, stages, producer) for a problem:
 //   * producer: DIRECT whenever the 16-byte vector rules hold, GENERIC
 //     otherwise (REGISTER only on request);
-//   * tile: the compiled tile class with the smallest estimated time, counting
-//     how many rounds of workgroups the problem needs on 256 CUs;
+//   * tile: the compiled tile class with the smallest estimated time of the
+//     busiest CU (its tiles in rounds of co-resident workgroups, a partial
+//     last round at its measured cost, a prologue per round), each class
+//     estimated at the ring depth it would run with; near-equal estimates go
+//     to the larger tile;
 //   * stages (DIRECT): the smallest ring depth whose lookahead covers the load latency,
 //     using the uncovered-latency estimate max(0, L - (S-1)*C) of page
 //     "Software pipelines and asynchronous copies" (section "Worked example:
 //     Choosing between two and four stages"), with C the MFMA time of one K
-//     tile on a SIMD.  The depth is clipped to the number of K tiles (section
-//     "Prologue, steady state, and epilogue": fewer K tiles than stages).
+//     tile on a SIMD shared by the workgroups actually resident on the CU.
+//     The depth is clipped to the number of K tiles (section "Prologue,
+//     steady state, and epilogue": fewer K tiles than stages).
 //   * register-staged producers take tile and depth together from measured
 //     per-variant efficiencies (register pressure decides their depth).
 #include <hip/hip_runtime.h>
@@ -34,6 +38,14 @@ constexpr int kLdsPerCU = 163840;
 // (>= 1024 MFMA cycles) covers it, and deeper rings measured slower there
 // (more loads in flight, same L2 bandwidth), so the model asks for S = 2.
 constexpr double kLoadLatencyCycles = 1000.0;
+// Exposed start of a round of workgroups (launch, first K tile in flight), in
+// SIMD clocks; the choice of tile is insensitive to it between 1000 and 4000.
+constexpr double kPrologueCycles = 2000.0;
+// Estimates within this factor of the best count as equal, and the larger
+// tile wins: it pulls fewer bytes from L2 per flop, and when it leaves CUs
+// idle the busy ones run at a higher clock (bf16 6144^3: 256 x 256 measured
+// 11 % faster than 128 x 128, whose estimate was 1 % lower).
+constexpr double kTieMargin = 1.10;
 
 struct Table {
     const VariantDesc* v;
@@ -51,6 +63,8 @@ Table table_for(int dtype) {
     }
     return t;
 }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int elem_bytes(int dtype) { return dtype == PGEMM_F32 ? 4 : dtype == PGEMM_I8 ? 1 : 2; }
 
@@ -94,24 +108,65 @@ double tile_compute_cycles(const VariantDesc& d, int share) {
     return flops / (4.0 * flops_per_simd_clk(d.dtype)) * share;
 }
 
-// Measured efficiency of a tile class (fraction of dense peak at 4096^3 with
-// its best ring depth, seeded inputs, MI355X): the re-run tile search that
-// follows any change to the pipelined kernel.  Classes not listed fall back
-// to an operand-traffic estimate.
-double tile_efficiency(const VariantDesc& d) {
-    struct E { int dt, bm, bn, bk; double e; };
+// Measured behaviour of a tile class on MI355X (seeded inputs), the re-run
+// tile search that follows any change to the pipelined kernel:
+//   eff  fraction of dense peak at 4096^3 with the class's best ring depth;
+//   lam  cost of a partial last round: r < occ co-resident workgroups take
+//        r + lam*(occ - r) workgroup-times.  0 would be perfect sharing; 1
+//        would make a lone workgroup take as long as a full round.
+//        Measured: bf16 128 x 128 0.37 (one workgroup alone on a CU runs
+//        only 1.46x faster than two), fp32 128 x 64 x 16 0.11.
+// Classes not listed fall back to an operand-traffic estimate.
+struct ClassModel {
+    double eff, lam;
+};
+
+ClassModel class_model(const VariantDesc& d) {
+    struct E { int dt, bm, bn, bk; double e, lam; };
     static const E table[] = {
-        {PGEMM_BF16, 256, 256, 64, 0.50}, {PGEMM_BF16, 256, 256, 32, 0.44}, {PGEMM_BF16, 128, 128, 64, 0.42},
-        {PGEMM_F16, 256, 256, 64, 0.48},  {PGEMM_F16, 256, 256, 32, 0.44},  {PGEMM_F16, 128, 128, 64, 0.40},
-        {PGEMM_I8, 256, 256, 128, 0.44},  {PGEMM_I8, 256, 256, 64, 0.41},   {PGEMM_I8, 128, 128, 128, 0.32},
-        {PGEMM_F32, 256, 256, 32, 0.90},  {PGEMM_F32, 128, 64, 16, 0.86},   {PGEMM_F32, 128, 128, 32, 0.82},
+        {PGEMM_BF16, 256, 256, 64, 0.504, 0.0}, {PGEMM_BF16, 256, 256, 32, 0.481, 0.0},
+        {PGEMM_BF16, 128, 128, 64, 0.400, 0.37}, {PGEMM_F16, 256, 256, 64, 0.475, 0.0},
+        {PGEMM_F16, 256, 256, 32, 0.459, 0.0},  {PGEMM_F16, 128, 128, 64, 0.387, 0.37},
+        {PGEMM_I8, 256, 256, 128, 0.445, 0.0},  {PGEMM_I8, 256, 256, 64, 0.426, 0.0},
+        {PGEMM_I8, 128, 128, 128, 0.346, 0.37}, {PGEMM_F32, 256, 256, 32, 0.92, 0.0},
+        {PGEMM_F32, 128, 64, 16, 0.90, 0.11},   {PGEMM_F32, 128, 128, 32, 0.82, 0.3},
     };
     for (const E& x : table)
-        if (x.dt == d.dtype && x.bm == d.bm && x.bn == d.bn && x.bk == d.bk) return x.e;
+        if (x.dt == d.dtype && x.bm == d.bm && x.bn == d.bn && x.bk == d.bk) return {x.e, x.lam};
     const double per = (double)(d.bm + d.bn) / (2.0 * d.bm * d.bn);
     const double ref = 512.0 / (2.0 * 256 * 256);
     const double e = ref / per;
-    return 0.4 * (e > 1.0 ? 1.0 : std::pow(e, 0.5));
+    return {0.4 * (e > 1.0 ? 1.0 : std::pow(e, 0.5)), 0.3};
+}
+
+double tile_efficiency(const VariantDesc& d) { return class_model(d).eff; }
+
+// Output tiles on the busiest CU: the dispatcher spreads workgroups over all
+// CUs before it stacks them.
+int64_t tiles_per_cu(const VariantDesc& d, int64_t M, int64_t N) {
+    return ceil_div(ceil_div(M, d.bm) * ceil_div(N, d.bn), kNumCU);
+}
+
+// Estimated SIMD clocks of the busiest CU for variant d at efficiency eff:
+// its tiles run in rounds of up to wg_per_cu co-resident workgroups, a
+// partial last round costs as the class model says, and every round pays the
+// prologue once.
+double est_cycles(const VariantDesc& d, int64_t M, int64_t N, int64_t K, double eff) {
+    const int64_t occ = wg_per_cu(d);
+    const int64_t n = tiles_per_cu(d, M, N);
+    const int64_t full = n / occ, r = n % occ;
+    const double units = (double)(full * occ) + (r ? (double)r + class_model(d).lam * (double)(occ - r) : 0.0);
+    const double kp = (double)(ceil_div(K, d.bk) * d.bk);
+    const double per_tile = 2.0 * d.bm * d.bn * kp / (eff * 4.0 * flops_per_simd_clk(d.dtype));
+    return units * per_tile + (double)ceil_div(n, occ) * kPrologueCycles;
+}
+
+// MFMA cycles of one K tile on one SIMD with the workgroups that actually
+// share the CU: at most wg_per_cu, and no more than the CU has tiles.
+double shared_tile_cycles(const VariantDesc& d, int64_t M, int64_t N) {
+    const int64_t n = tiles_per_cu(d, M, N);
+    const int occ = wg_per_cu(d);
+    return tile_compute_cycles(d, (int)(n < occ ? (n < 1 ? 1 : n) : occ));
 }
 
 // Register-staged producers (REGISTER, GENERIC): measured efficiency of each
@@ -153,7 +208,6 @@ double staged_efficiency(const VariantDesc& d) {
     return 0.5 * tile_efficiency(d);
 }
 
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Workgroups to launch: one per output tile (default), or, on request
 // (pgemm_opts.workgroups), fewer persistent ones that loop over the tiles
@@ -205,8 +259,9 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligne
         return PGEMM_ERR_INVALID_ARG;
     const int force_waves = opts ? opts->waves : 0;
 
-    // Register-staged producers: the (tile, depth) pair with the best measured
-    // time; an explicit depth restricts the choice to variants of that depth.
+    // Register-staged producers: the (tile, depth) pair with the best
+    // estimated time at its measured efficiency; an explicit depth restricts
+    // the choice to variants of that depth.
     if (want_prod != PROD_DIRECT) {
         double best_time = 0.0;
         int best = -1;
@@ -216,11 +271,7 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligne
             if (force_tile && (d.bm != opts->tile_m || d.bn != opts->tile_n || d.bk != opts->tile_k)) continue;
             if (force_waves && d.wgm * d.wgn != force_waves) continue;
             if (stages != 0 && d.stages != stages) continue;
-            const int occ = wg_per_cu(d);
-            const int64_t tiles = ceil_div(M, d.bm) * ceil_div(N, d.bn);
-            const int64_t rounds = ceil_div(tiles, (int64_t)kNumCU * occ);
-            const double work = (double)d.bm * d.bn * (double)(ceil_div(K, d.bk) * d.bk + d.bk);
-            const double time = (double)rounds * occ * work / staged_efficiency(d);
+            const double time = est_cycles(d, M, N, K, staged_efficiency(d));
             if (best < 0 || time < best_time * 0.999) {
                 best = i;
                 best_time = time;
@@ -230,73 +281,81 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligne
         const VariantDesc& d = t.v[best];
         out.index = best;
         out.stages_req = d.stages;
-        out.uncovered = pgemm_model_uncovered_cycles(kLoadLatencyCycles, tile_compute_cycles(d, wg_per_cu(d)), d.stages);
+        out.uncovered = pgemm_model_uncovered_cycles(kLoadLatencyCycles, shared_tile_cycles(d, M, N), d.stages);
         return PGEMM_OK;
     }
 
-    // 1. tile class: best estimated time among variants with the producer.
-    double best_time = 0.0;
-    int best = -1;
-    for (int i = 0; i < t.n; ++i) {
-        const VariantDesc& d = t.v[i];
-        if (!producer_matches(d, want_prod)) continue;
-        if (force_tile && (d.bm != opts->tile_m || d.bn != opts->tile_n || d.bk != opts->tile_k)) continue;
-        if (force_waves && d.wgm * d.wgn != force_waves) continue;
-        if (stages != 0) {
-            // the tile class must offer the requested depth
-            bool has = false;
-            for (int j = 0; j < t.n; ++j)
-                if (t.v[j].dtype == d.dtype && t.v[j].bm == d.bm && t.v[j].bn == d.bn && t.v[j].bk == d.bk &&
-                    t.v[j].wgm == d.wgm && t.v[j].wgn == d.wgn && producer_matches(t.v[j], want_prod) &&
-                    t.v[j].stages == stages)
-                    has = true;
-            if (!has) continue;
+    // DIRECT: every tile class is estimated at the ring depth it would run
+    // with, and the cheapest wins (the larger tile among near-equal ones).
+    auto same_class = [](const VariantDesc& a, const VariantDesc& b) {
+        return a.bm == b.bm && a.bn == b.bn && a.bk == b.bk && a.wgm == b.wgm && a.wgn == b.wgn;
+    };
+    // The variant of class `c` with ring depth S, or the deepest one below it
+    // (an explicit depth is never downgraded); -1 when there is none.
+    auto variant_at = [&](const VariantDesc& c, int S, bool exact) {
+        for (int s = S; s >= 1; --s) {
+            for (int i = 0; i < t.n; ++i)
+                if (same_class(t.v[i], c) && producer_matches(t.v[i], want_prod) && t.v[i].stages == s) return i;
+            if (exact) break;
         }
-        const int occ = wg_per_cu(d);
-        const int64_t tiles = ceil_div(M, d.bm) * ceil_div(N, d.bn);
-        const int64_t rounds = ceil_div(tiles, (int64_t)kNumCU * occ);
-        const double work = (double)d.bm * d.bn * (double)(ceil_div(K, d.bk) * d.bk + d.bk);
-        const double time = (double)rounds * occ * work / tile_efficiency(d);
-        if (best < 0 || time < best_time * 0.999) {
-            best = i;
-            best_time = time;
-        }
-    }
-    if (best < 0) return PGEMM_ERR_INFEASIBLE_PLAN;
-    const VariantDesc& bt = t.v[best];
-    const int nK = (int)ceil_div(K, bt.bk);
-
-    // 2. ring depth.
-    const int occ = wg_per_cu(bt);
-    const double C = tile_compute_cycles(bt, occ);
-    int S = stages;
-    if (S == 0) {
-        S = 4;
+        return -1;
+    };
+    // Ring depth: the smallest S in 2..4 whose lookahead covers the load
+    // latency, max(0, L - (S-1)*C) = 0, with C the MFMA time of one K tile on a
+    // SIMD shared by the workgroups that really share the CU; clipped to the
+    // number of K tiles.
+    auto depth_for = [&](const VariantDesc& c) {
+        if (stages != 0) return variant_at(c, stages, true);
+        int S = 4;
         for (int s = 2; s <= 4; ++s) {
-            if (pgemm_model_uncovered_cycles(kLoadLatencyCycles, C, s) <= 0.0) {
+            const int i = variant_at(c, s, true);
+            if (i >= 0 && pgemm_model_uncovered_cycles(kLoadLatencyCycles, shared_tile_cycles(t.v[i], M, N), s) <= 0.0) {
                 S = s;
                 break;
             }
         }
-        if (S > nK) S = nK < 1 ? 1 : nK;  // no more stages than K tiles
+        const int nK = (int)ceil_div(K, c.bk);
+        if (S > nK) S = nK < 1 ? 1 : nK;
+        return variant_at(c, S, false);
+    };
+    struct Cand {
+        int index;
+        double time;
+    };
+    Cand cands[64];
+    int nc = 0;
+    for (int i = 0; i < t.n && nc < 64; ++i) {
+        const VariantDesc& d = t.v[i];
+        if (!producer_matches(d, want_prod)) continue;
+        if (force_tile && (d.bm != opts->tile_m || d.bn != opts->tile_n || d.bk != opts->tile_k)) continue;
+        if (force_waves && d.wgm * d.wgn != force_waves) continue;
+        bool seen = false;  // one candidate per tile class
+        for (int j = 0; j < nc; ++j) seen = seen || same_class(t.v[cands[j].index], d);
+        if (seen) continue;
+        const int pick = depth_for(d);
+        if (pick < 0) continue;
+        cands[nc++] = {pick, est_cycles(t.v[pick], M, N, K, tile_efficiency(t.v[pick]))};
     }
-    // 3. pick the variant of this tile class with depth S (or the deepest below it).
+    if (nc == 0) return PGEMM_ERR_INFEASIBLE_PLAN;
+    double best_time = cands[0].time;
+    for (int j = 1; j < nc; ++j) best_time = cands[j].time < best_time ? cands[j].time : best_time;
     int pick = -1;
-    for (int s = S; s >= 1 && pick < 0; --s) {
-        for (int i = 0; i < t.n; ++i) {
-            const VariantDesc& d = t.v[i];
-            if (d.bm == bt.bm && d.bn == bt.bn && d.bk == bt.bk && d.wgm == bt.wgm && d.wgn == bt.wgn &&
-                producer_matches(d, want_prod) && d.stages == s) {
-                pick = i;
-                break;
-            }
+    for (int j = 0; j < nc; ++j) {
+        if (cands[j].time > best_time * kTieMargin) continue;
+        const VariantDesc& d = t.v[cands[j].index];
+        if (pick < 0) {
+            pick = cands[j].index;
+            continue;
         }
-        if (stages != 0) break;  // an explicit depth is not downgraded
+        const VariantDesc& p = t.v[pick];
+        const int64_t area = (int64_t)d.bm * d.bn, parea = (int64_t)p.bm * p.bn;
+        if (area > parea || (area == parea && cands[j].time < est_cycles(p, M, N, K, tile_efficiency(p))))
+            pick = cands[j].index;
     }
-    if (pick < 0) return PGEMM_ERR_INFEASIBLE_PLAN;
     out.index = pick;
     out.stages_req = t.v[pick].stages;
-    out.uncovered = pgemm_model_uncovered_cycles(kLoadLatencyCycles, C, t.v[pick].stages);
+    out.uncovered = pgemm_model_uncovered_cycles(kLoadLatencyCycles, shared_tile_cycles(t.v[pick], M, N),
+                                                 t.v[pick].stages);
     return PGEMM_OK;
 }
 

@@ -151,6 +151,23 @@ def test_hazard_without_rows_is_a_noop():
     assert lib.pgemm_hazard_copy_reduce(**dict(HAZARD_OK, rows=0, X=None, row_sums=None), stream=0) == 0
 
 
+@pytest.mark.parametrize("dtype,shape,tile", [
+    ("f32", (4096, 4096, 4096), (256, 256, 32)), ("bf16", (4096, 4096, 4096), (256, 256, 64)),
+    ("f16", (4096, 4096, 4096), (256, 256, 64)), ("i8", (4096, 4096, 4096), (256, 256, 128)),
+    ("bf16", (3000, 3000, 3000), (256, 256, 64)), ("bf16", (6144, 6144, 6144), (256, 256, 64)),
+    ("bf16", (5120, 5120, 5120), (256, 256, 64)), ("bf16", (2048, 2048, 2048), (128, 128, 64)),
+    ("f32", (1024, 1024, 1024), (128, 64, 16)), ("f32", (2048, 2048, 2048), (128, 64, 16)),
+    ("f16", (4096, 4096, 256), (256, 256, 64)), ("i8", (2560, 2560, 2560), (128, 128, 128)),
+])
+def test_planner_picks_the_tile_measured_fastest(dtype, shape, tile):
+    """A regression check of the planner's cost model, not a correctness
+    property: each expectation is the tile class measured fastest on MI355X
+    for that shape (every compiled DIRECT variant timed, seeded inputs)."""
+    r, p = lib.pgemm_plan(*shape, dtype, 0, 1)
+    assert r == 0
+    assert (p["tile_m"], p["tile_n"], p["tile_k"]) == tile
+
+
 def test_strerror_covers_every_status():
     for code in range(0, -8, -1):
         assert lib.pgemm_strerror(code) != "unknown status"
