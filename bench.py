@@ -68,7 +68,8 @@ def kernel_source_hash() -> str:
     csrc = os.path.join(ROOT, "software_pipelined_tiled_loop_amd", "csrc")
     for f in KERNEL_FILES:
         h.update(_code_only(open(os.path.join(csrc, f)).read()).encode())
-    h.update(" ".join(build.HIPCC_FLAGS).encode())
+    # code-generation flags only: include paths name this checkout's location
+    h.update(" ".join(f for f in build.HIPCC_FLAGS if not f.startswith("-I")).encode())
     return h.hexdigest()[:16]
 
 
@@ -79,13 +80,16 @@ def make_device_operands(dtype, M, N, K, seed, alpha, beta, lda=None, ldb=None, 
 
 
 WARMUP_MS = 150.0
+TRIAL_MS = 5.0
 
 
-def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=20, warmup=None, trials=3):
+def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=None, warmup=None, trials=5):
     """ms per call: the median over `trials` of the average over `reps`
-    back-to-back launches (HIP events on the launch stream).  The median
-    keeps one disturbed trial (clock ramp, a profiler's buffer flush) out of
-    the reported sweep points.  Warm-up runs the kernel for about
+    back-to-back launches (HIP events on the launch stream), `reps` chosen so
+    that a trial lasts about TRIAL_MS (at least 20 launches).  The median
+    keeps a disturbed trial (clock ramp, a profiler's buffer flush) out of the
+    reported sweep points; with 20-launch trials, kernels of ~15 us varied by
+    10 % between identical runs.  Warm-up runs the kernel for about
     WARMUP_MS first: after the GPU has idled (while the host draws the next
     operands) its clock takes on the order of 100 ms of load to settle, and
     with a 20 ms warm-up the first of several successive timings of one
@@ -108,7 +112,12 @@ def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=20, war
         call()
         e1.record(stream)
         e1.synchronize()
-        warmup = max(3, min(20000, int(WARMUP_MS / max(e0.elapsed_time(e1), 1e-3))))
+        per = max(e0.elapsed_time(e1), 1e-3)
+        warmup = max(3, min(20000, int(WARMUP_MS / per)))
+        if reps is None:
+            reps = max(20, min(2000, int(TRIAL_MS / per)))
+    if reps is None:
+        reps = 20
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -282,7 +291,7 @@ def plan_label(p):
     return "%dx%dx%d s%d %s" % (p["tile_m"], p["tile_n"], p["tile_k"], p["stages"], p["producer"])
 
 
-def variant_sweep(lib, op, A, B, C, M, N, K, reps=20):
+def variant_sweep(lib, op, A, B, C, M, N, K, reps=None):
     """Every compiled vector-producer variant of the dtype on this problem."""
     out = {}
     for i in range(lib.pgemm_num_variants()):
@@ -340,7 +349,7 @@ def run_reports(lib, torch):
     op, A, B, C = make_device_operands("f32", M, N, K, inputs.seed_for(1), 1.0, 0.5)
     d = {}
     for s in (1, 2):
-        ms = time_gemm(lib, op, A, B, C, stages=s, tile=(128, 64, 16), reps=10)
+        ms = time_gemm(lib, op, A, B, C, stages=s, tile=(128, 64, 16))
         d["128x64x16 s%d direct" % s] = round(tflops(M, N, K, ms), 2)
     rep["f32_4096_page_tile"] = d
     del A, B, C
@@ -352,9 +361,9 @@ def run_reports(lib, torch):
         row = {}
         for s in (1, 2, 3, 4):
             p = plan_of(lib, "bf16", M, N, Ks, stages=s)
-            ms = time_gemm(lib, op, A, B, C, stages=s, reps=10)
+            ms = time_gemm(lib, op, A, B, C, stages=s)
             row["s%d" % s] = {"tflops": round(tflops(M, N, Ks, ms), 1), "plan": plan_label(p)}
-        ms = time_gemm(lib, op, A, B, C, reps=10)
+        ms = time_gemm(lib, op, A, B, C)
         byts = algorithmic_bytes("bf16", M, N, Ks, 0.0)
         roof = min(PEAK["bf16"], 2.0 * M * N * Ks / byts * HBM_PEAK_GBS / 1e3)
         row["auto"] = {"tflops": round(tflops(M, N, Ks, ms), 1), "plan": plan_label(plan_of(lib, "bf16", M, N, Ks)),
@@ -369,7 +378,7 @@ def run_reports(lib, torch):
     r = inputs.RAGGED
     op, A, B, C = make_device_operands("bf16", r["M"], r["N"], r["K"], inputs.seed_for(4, 9), 1.0, 0.0,
                                        lda=r["lda"], ldb=r["ldb"], ldc=r["ldc"])
-    ms = time_gemm(lib, op, A, B, C, reps=5)
+    ms = time_gemm(lib, op, A, B, C)
     sweep["ragged_4000x3968x4001"] = {"tflops": round(tflops(r["M"], r["N"], r["K"], ms), 1),
                                       "plan": plan_label(plan_of(lib, "bf16", r["M"], r["N"], r["K"], aligned=0))}
     rep["bf16_k_sweep"] = sweep

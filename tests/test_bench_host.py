@@ -41,6 +41,15 @@ def test_source_hash_is_stable_and_covers_build_flags(monkeypatch):
     assert bench.kernel_source_hash() != h
 
 
+def test_source_hash_does_not_depend_on_the_checkout_location(monkeypatch):
+    h = bench.kernel_source_hash()
+    from software_pipelined_tiled_loop_amd import build
+    moved = [("-I/elsewhere/include" if f.startswith("-I") else f) for f in build.HIPCC_FLAGS]
+    assert moved != build.HIPCC_FLAGS
+    monkeypatch.setattr(build, "HIPCC_FLAGS", moved)
+    assert bench.kernel_source_hash() == h
+
+
 def test_traffic_only_for_the_profiled_sources():
     d = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
     entries = {k: v for k, v in d.items() if not k.startswith("_")}
