@@ -225,6 +225,10 @@ def main():
     if plan is None:
         print("no compiled variant for these options", file=sys.stderr)
         sys.exit(1)
+    # the compute/load ratio of the plan's tile, reported as a diagnostic (the
+    # page's thresholds for it are not used to choose)
+    plan["compute_load_ratio"] = round(lib.pgemm_model_compute_load_ratio(
+        plan["tile_m"], plan["tile_n"], plan["tile_k"], inputs.ELEM_BYTES[dt]), 2)
     stream = torch.cuda.current_stream()
     opts = lib._opts(args.producer, tile)
 
@@ -351,6 +355,7 @@ def run_reports(lib, torch):
     for s in (1, 2):
         ms = time_gemm(lib, op, A, B, C, stages=s, tile=(128, 64, 16))
         d["128x64x16 s%d direct" % s] = round(tflops(M, N, K, ms), 2)
+    d["compute_load_ratio"] = round(lib.pgemm_model_compute_load_ratio(128, 64, 16, 4), 2)
     rep["f32_4096_page_tile"] = d
     del A, B, C
 

@@ -161,10 +161,17 @@ int pgemm_variant_info(int index, pgemm_plan_info* out, int* dtype);
  *
  * pgemm_model_global_loads_per_output: global loads per output element of a
  * BM x BN tile over K, K/BN + K/BM (same page, section "What The Overlap
- * Cost": 96 at 128 x 64 and K = 4096, unchanged by pipelining). */
+ * Cost": 96 at 128 x 64 and K = 4096, unchanged by pipelining).
+ *
+ * pgemm_model_compute_load_ratio: flops of one K tile over the bytes loaded
+ * for it, 2*BM*BN*BK / ((BM*BK + BK*BN) * elem_bytes) (page "GPU-Kernel
+ * pipelinen", step 2).  A reported diagnostic only: the page's thresholds for
+ * choosing a producer by it were measured on another GPU, and the planner
+ * chooses by measured sweeps instead.  Returns 0 for non-positive sizes. */
 double pgemm_model_uncovered_cycles(double latency, double compute_per_tile, int stages);
 int64_t pgemm_model_lds_bytes(int bm, int bn, int bk, int stages, int elem_bytes, int a_pad_elems_per_k);
 double pgemm_model_global_loads_per_output(int bm, int bn, int64_t K);
+double pgemm_model_compute_load_ratio(int bm, int bn, int bk, int elem_bytes);
 
 /* Consume-before-reuse hazard demonstrator (page "Software pipelines and
  * asynchronous copies", sections "Producer-consumer synchronization" and

@@ -83,12 +83,14 @@ _lib.pgemm_model_lds_bytes.argtypes = [_int, _int, _int, _int, _int, _int]
 _lib.pgemm_model_lds_bytes.restype = _i64
 _lib.pgemm_model_global_loads_per_output.argtypes = [_int, _int, _i64]
 _lib.pgemm_model_global_loads_per_output.restype = _dbl
+_lib.pgemm_model_compute_load_ratio.argtypes = [_int, _int, _int, _int]
+_lib.pgemm_model_compute_load_ratio.restype = _dbl
 _lib.pgemm_hazard_copy_reduce.argtypes = [_vp, _i64, _i64, _i64, _vp, _int, _int, _int, _vp, _i64, _int, _vp]
 _lib.pgemm_hazard_copy_reduce.restype = _int
 
 EXPORTED = ("pgemm_gemm", "pgemm_gemm_ex", "pgemm_plan", "pgemm_strerror", "pgemm_num_variants",
             "pgemm_variant_info", "pgemm_version", "pgemm_model_uncovered_cycles", "pgemm_model_lds_bytes",
-            "pgemm_model_global_loads_per_output", "pgemm_hazard_copy_reduce")
+            "pgemm_model_global_loads_per_output", "pgemm_model_compute_load_ratio", "pgemm_hazard_copy_reduce")
 
 
 class PgemmError(RuntimeError):
@@ -187,6 +189,10 @@ def pgemm_model_lds_bytes(bm, bn, bk, stages, elem_bytes, a_pad=0):
 
 def pgemm_model_global_loads_per_output(bm, bn, K):
     return _lib.pgemm_model_global_loads_per_output(bm, bn, K)
+
+
+def pgemm_model_compute_load_ratio(bm, bn, bk, elem_bytes):
+    return _lib.pgemm_model_compute_load_ratio(bm, bn, bk, elem_bytes)
 
 
 def gemm(A, B, C, alpha=1.0, beta=0.0, stages=0, producer=None, tile=None, M=None, N=None, K=None,

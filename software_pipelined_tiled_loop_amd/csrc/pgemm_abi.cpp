@@ -405,6 +405,14 @@ double pgemm_model_global_loads_per_output(int bm, int bn, int64_t K) {
     return (double)K / bn + (double)K / bm;
 }
 
+double pgemm_model_compute_load_ratio(int bm, int bn, int bk, int elem_bytes) {
+    if (bm <= 0 || bn <= 0 || bk <= 0 || elem_bytes <= 0) return 0.0;
+    // two flops per multiply-add of the K tile, over the A and B bytes it loads
+    const double flops = 2.0 * bm * bn * bk;
+    const double bytes = ((double)bm * bk + (double)bk * bn) * elem_bytes;
+    return flops / bytes;
+}
+
 const char* pgemm_strerror(int status) {
     switch (status) {
         case PGEMM_OK: return "ok";

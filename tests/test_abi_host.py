@@ -242,3 +242,10 @@ def test_page_models_golden():
         s = g[key]
         assert lib.pgemm_model_lds_bytes(s["bm"], s["bn"], s["bk"], s["stages"], s["elem_bytes"],
                                          s["a_pad_elems_per_k"]) == s["expected"]
+    c = g["compute_load_ratio_page_kernel_tile"]
+    got = lib.pgemm_model_compute_load_ratio(c["bm"], c["bn"], c["bk"], c["elem_bytes"])
+    assert abs(got - c["expected_num"] / c["expected_den"]) < 1e-12
+    # square tiles: 2*B*B*BK / (2*B*BK*s) = B/s, independent of BK
+    for b, bk, es in ((256, 32, 2), (256, 64, 2), (256, 128, 1), (128, 64, 4)):
+        assert lib.pgemm_model_compute_load_ratio(b, b, bk, es) == b / es
+    assert lib.pgemm_model_compute_load_ratio(0, 64, 16, 4) == 0
