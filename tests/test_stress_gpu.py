@@ -6,9 +6,11 @@ consumer, with failure counts.  Here the library's stress hook skews one wave
 of every workgroup per K tile (rotating) by ~8k cycles after the ready
 barrier, so the other waves reach the next barrier, and issue the next
 tile's loads into the freed stage, far ahead of it.  Every launch must give
-exactly the same int8 result, equal to the oracle.  A version with a wait
-removed is not run on the GPU: the host model checker
-(tests/test_schedule_model.py) shows that removing the reuse edge is detected.
+exactly the same int8 result, equal to the oracle: 6 variants x 200 runs.
+The GEMM has no build with a wait removed.  The reuse edge's removal is shown
+by the host model checker (tests/test_schedule_model.py) and, on the GPU, by
+the two-stage copy-and-reduce demonstrator (tests/test_hazard_gpu.py), whose
+variant without the reuse barrier fails every delayed run.
 """
 import numpy as np
 import pytest
