@@ -114,8 +114,9 @@ double tile_compute_cycles(const VariantDesc& d, int share) {
 //   lam  cost of a partial last round: r < occ co-resident workgroups take
 //        r + lam*(occ - r) workgroup-times.  0 would be perfect sharing; 1
 //        would make a lone workgroup take as long as a full round.
-//        Measured: bf16 128 x 128 0.37 (one workgroup alone on a CU runs
-//        only 1.46x faster than two), fp32 128 x 64 x 16 0.11.
+//        Measured: bf16 128 x 128 0.37 (a workgroup alone on a CU finishes
+//        in 0.68 of the time two co-resident ones take), fp32 128 x 64 x 16
+//        0.11.
 // Classes not listed fall back to an operand-traffic estimate.
 struct ClassModel {
     double eff, lam;
