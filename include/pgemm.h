@@ -196,8 +196,9 @@ double pgemm_model_compute_load_ratio(int bm, int bn, int bk, int elem_bytes);
  *       barrier is still executed by all waves and every address is the same
  *       as in the correct protocol, so the variant cannot hang or fault.
  *
- *   delay_wave (-1 = none, else 0..3) sleeps delay_sleeps x 8128 cycles
- *   (0..1000) before reading each tile: the artificial consumer delay.
+ *   delay_wave (-1 = none, else 0..3) sleeps about delay_cycles shader
+ *   clocks (0..10 000 000, in steps of 64) before reading each tile: the
+ *   artificial consumer delay.
  *
  *   trace (optional, NULL = off): for workgroup trace_wg, lane 0 of each wave
  *   w records six shader-clock stamps per tile t at trace[(w*nT + t)*6 + e]:
@@ -213,7 +214,7 @@ double pgemm_model_compute_load_ratio(int bm, int bn, int bk, int elem_bytes);
  * (PGEMM_ERR_INVALID_ARG) are detected before anything is enqueued; a
  * rejected launch returns PGEMM_ERR_HIP.  Asynchronous on `stream`. */
 int pgemm_hazard_copy_reduce(const int32_t* X, int64_t rows, int64_t cols, int64_t ldx,
-                             int32_t* row_sums, int reuse_wait, int delay_wave, int delay_sleeps,
+                             int32_t* row_sums, int reuse_wait, int delay_wave, int delay_cycles,
                              int64_t* trace, int64_t trace_len, int trace_wg, void* stream);
 
 /* ABI version: major*10000 + minor*100 + patch. */

@@ -217,8 +217,8 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, stages=0, producer=None, tile=None, M=Non
     return C
 
 
-def pgemm_hazard_copy_reduce(X, rows, cols, ldx, row_sums, reuse_wait, delay_wave=-1, delay_sleeps=0, trace=None,
+def pgemm_hazard_copy_reduce(X, rows, cols, ldx, row_sums, reuse_wait, delay_wave=-1, delay_cycles=0, trace=None,
                              trace_len=0, trace_wg=0, stream=None):
     return _lib.pgemm_hazard_copy_reduce(_ptr(X), rows, cols, ldx, _ptr(row_sums), int(reuse_wait), int(delay_wave),
-                                         int(delay_sleeps), _ptr(trace), int(trace_len), int(trace_wg),
+                                         int(delay_cycles), _ptr(trace), int(trace_len), int(trace_wg),
                                          _stream(stream))

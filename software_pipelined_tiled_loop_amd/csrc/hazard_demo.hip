@@ -34,7 +34,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 template <bool REUSE_WAIT>
 __global__ void __launch_bounds__(NTH)
     copy_reduce_kernel(const int* __restrict__ X, int64_t ldx, int nT, int* __restrict__ sums, int delay_wave,
-                       int delay_sleeps, long long* trace, int trace_wg) {
+                       int delay_cycles, long long* trace, int trace_wg) {
     __shared__ v4i stage[2][CHUNKS];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -82,8 +82,12 @@ __global__ void __launch_bounds__(NTH)
         // written to LDS): unconditional, it stays in flight under the reads.
         load(refill ? t + 2 : t);
         stamp(t, 0);
-        if (wave == delay_wave)
-            for (int i = 0; i < delay_sleeps; ++i) __builtin_amdgcn_s_sleep(127);
+        if (wave == delay_wave) {
+            // s_sleep takes an immediate: 127 x 64 clocks per long sleep, then
+            // 64-clock steps for the rest
+            for (int i = 0; i < delay_cycles / 8128; ++i) __builtin_amdgcn_s_sleep(127);
+            for (int i = 0; i < delay_cycles % 8128 / 64; ++i) __builtin_amdgcn_s_sleep(1);
+        }
         stamp(t, 1);
         v4i v[ROWS_PER_WAVE];
 #pragma unroll
@@ -117,13 +121,13 @@ __global__ void __launch_bounds__(NTH)
 }  // namespace hazard
 
 extern "C" int pgemm_hazard_copy_reduce(const int32_t* X, int64_t rows, int64_t cols, int64_t ldx, int32_t* row_sums,
-                                        int reuse_wait, int delay_wave, int delay_sleeps, int64_t* trace,
+                                        int reuse_wait, int delay_wave, int delay_cycles, int64_t* trace,
                                         int64_t trace_len, int trace_wg, void* stream) {
     using namespace hazard;
     if (rows < 0 || rows % RB != 0 || cols < 0 || cols % TC != 0 || ldx < cols || ldx % 4 != 0)
         return PGEMM_ERR_INVALID_ARG;
     if (reuse_wait != 0 && reuse_wait != 1) return PGEMM_ERR_INVALID_ARG;
-    if (delay_wave < -1 || delay_wave >= NWAVE || delay_sleeps < 0 || delay_sleeps > 1000)
+    if (delay_wave < -1 || delay_wave >= NWAVE || delay_cycles < 0 || delay_cycles > 10000000)
         return PGEMM_ERR_INVALID_ARG;
     if (rows == 0) return PGEMM_OK;
     if (row_sums == nullptr || (cols > 0 && (X == nullptr || ((uintptr_t)X & 15) != 0))) return PGEMM_ERR_INVALID_ARG;
@@ -137,7 +141,7 @@ extern "C" int pgemm_hazard_copy_reduce(const int32_t* X, int64_t rows, int64_t 
     const int* x = reinterpret_cast<const int*>(X);
     int* sums = reinterpret_cast<int*>(row_sums);
     long long* tr = reinterpret_cast<long long*>(trace);
-    void* args[] = {&x, &ldx, (void*)&nT, &sums, &delay_wave, &delay_sleeps, &tr, &trace_wg};
+    void* args[] = {&x, &ldx, (void*)&nT, &sums, &delay_wave, &delay_cycles, &tr, &trace_wg};
     const void* fn = reuse_wait ? reinterpret_cast<const void*>(&copy_reduce_kernel<true>)
                                 : reinterpret_cast<const void*>(&copy_reduce_kernel<false>);
     const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(NTH), args, 0, (hipStream_t)stream);

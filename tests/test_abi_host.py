@@ -129,15 +129,15 @@ def test_empty_problems_are_noops():
     assert lib._lib.pgemm_gemm(8, 0, 8, 1.0, None, 8, None, 8, 0.0, None, 8, 2, 0, None) == 0
 
 
-HAZARD_OK = dict(X=FAKE, rows=32, cols=512, ldx=512, row_sums=FAKE, reuse_wait=1, delay_wave=-1, delay_sleeps=0,
+HAZARD_OK = dict(X=FAKE, rows=32, cols=512, ldx=512, row_sums=FAKE, reuse_wait=1, delay_wave=-1, delay_cycles=0,
                  trace=None, trace_len=0, trace_wg=0)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(rows=15), -1), (dict(rows=-16), -1), (dict(cols=255), -1), (dict(cols=-256), -1),
     (dict(ldx=508), -1), (dict(ldx=514), -1), (dict(reuse_wait=2), -1), (dict(reuse_wait=-1), -1),
-    (dict(delay_wave=4), -1), (dict(delay_wave=-2), -1), (dict(delay_sleeps=-1), -1),
-    (dict(delay_sleeps=1001), -1), (dict(X=FAKE + 4), -1), (dict(X=None), -1), (dict(row_sums=None), -1),
+    (dict(delay_wave=4), -1), (dict(delay_wave=-2), -1), (dict(delay_cycles=-1), -1),
+    (dict(delay_cycles=10000001), -1), (dict(X=FAKE + 4), -1), (dict(X=None), -1), (dict(row_sums=None), -1),
     (dict(trace=FAKE, trace_len=47), -1), (dict(trace=FAKE, trace_len=48, trace_wg=2), -1),
     (dict(trace=FAKE, trace_len=48, trace_wg=-1), -1), (dict(trace=FAKE + 4, trace_len=48), -1),
     (dict(cols=256 * (2 ** 31 // 24 + 1), ldx=256 * (2 ** 31 // 24 + 1)), -7),

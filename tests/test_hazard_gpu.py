@@ -15,7 +15,9 @@ the oracle bit for bit:
   protocol never fails; without the reuse barrier the runs fail, and the wrong
   rows are the delayed wave's;
 * without the reuse barrier and without a delay the failures are intermittent
-  (counted, not asserted);
+  (counted, not asserted); a sweep of the delay shows where failures begin:
+  once the delayed wave lags by more than the other waves need to load tile
+  t+2 and rewrite the stage;
 * the timeline of one workgroup (shader-clock stamps per wave and tile) shows
   the ordering edge: with the reuse barrier no wave rewrites stage t%2 before
   the delayed wave has finished reading tile t from it; without it the other
@@ -37,6 +39,7 @@ ROWS = COLS = 4096
 RB, TC, NWAVE, EV = 16, 256, 4, 6
 N_INPUTS = 8
 ITERS = 1000
+SLEEP = 8128  # shader clocks of one long s_sleep
 
 
 def say(*a):
@@ -62,9 +65,9 @@ def arrays(lib):
     return xs, refs
 
 
-def run(lib, X, rows, cols, ldx, reuse_wait, delay_wave=-1, delay_sleeps=0, trace=None, trace_wg=0):
+def run(lib, X, rows, cols, ldx, reuse_wait, delay_wave=-1, delay_cycles=0, trace=None, trace_wg=0):
     sums = torch.full((max(rows, 1),), inputs.POISON_I32, dtype=torch.int32, device="cuda")
-    r = lib.pgemm_hazard_copy_reduce(X, rows, cols, ldx, sums, reuse_wait, delay_wave, delay_sleeps, trace,
+    r = lib.pgemm_hazard_copy_reduce(X, rows, cols, ldx, sums, reuse_wait, delay_wave, delay_cycles, trace,
                                      0 if trace is None else trace.numel(), trace_wg)
     assert r == 0, lib.pgemm_strerror(r)
     return sums[:rows]
@@ -78,7 +81,7 @@ def test_correct_protocol_matches_oracle_on_edge_shapes(lib, rows, cols, ldx):
     ref = oracle.row_sums(X.numpy(), rows, cols, ldx)
     Xd = X.cuda()
     for delay_wave in (-1, 0, 3):
-        got = run(lib, Xd, rows, cols, ldx, 1, delay_wave, 2 if delay_wave >= 0 else 0).cpu().numpy()
+        got = run(lib, Xd, rows, cols, ldx, 1, delay_wave, 2 * SLEEP if delay_wave >= 0 else 0).cpu().numpy()
         assert np.array_equal(got, ref), (rows, cols, ldx, delay_wave)
 
 
@@ -95,8 +98,8 @@ def stress(lib, arrays, reuse_wait, with_delay):
     failing_runs = wrong_rows = wrong_rows_of_delayed = 0
     for i in range(ITERS):
         d = i % NWAVE if with_delay else -1
-        sleeps = 1 + i % 4 if with_delay else 0
-        got = run(lib, xs[i % N_INPUTS], ROWS, COLS, COLS, reuse_wait, d, sleeps)
+        cycles = (1 + i % 4) * SLEEP if with_delay else 0
+        got = run(lib, xs[i % N_INPUTS], ROWS, COLS, COLS, reuse_wait, d, cycles)
         bad = (got != refs[i % N_INPUTS]).nonzero().flatten()
         if bad.numel():
             failing_runs += 1
@@ -127,11 +130,11 @@ def test_stress_without_reuse_barrier_and_without_delay_is_counted(lib, arrays):
     say("  failing runs", runs, "of", ITERS, "wrong rows", rows)
 
 
-def timeline(lib, arrays, reuse_wait, delay_wave, sleeps):
+def timeline(lib, arrays, reuse_wait, delay_wave, cycles):
     xs, refs = arrays
     nT = COLS // TC
     trace = torch.zeros(NWAVE * nT * EV, dtype=torch.int64, device="cuda")
-    run(lib, xs[0], ROWS, COLS, COLS, reuse_wait, delay_wave, sleeps, trace=trace, trace_wg=5)
+    run(lib, xs[0], ROWS, COLS, COLS, reuse_wait, delay_wave, cycles, trace=trace, trace_wg=5)
     T = trace.cpu().numpy().reshape(NWAVE, nT, EV)
     return T - T[:, 0, 0].min()
 
@@ -140,12 +143,12 @@ EVENTS = ("top", "read start", "read end", "past reuse", "rewritten", "past read
 
 
 def test_timeline_shows_the_reuse_edge(lib, arrays):
-    d, sleeps = 1, 2
+    d, cycles = 1, 2 * SLEEP
     nT = COLS // TC
     for reuse_wait in (1, 0):
-        T = timeline(lib, arrays, reuse_wait, d, sleeps)
-        say("timeline, workgroup 5, wave %d delayed, reuse barrier %s (cycles from the first stamp)"
-            % (d, "kept" if reuse_wait else "removed"))
+        T = timeline(lib, arrays, reuse_wait, d, cycles)
+        say("timeline, workgroup 5, wave %d delayed by %d cycles, reuse barrier %s (cycles from the first stamp)"
+            % (d, cycles, "kept" if reuse_wait else "removed"))
         for t in range(3):
             for w in range(NWAVE):
                 say("  tile %d wave %d: " % (t, w) + ", ".join("%s %d" % (n, v) for n, v in zip(EVENTS, T[w, t])))
@@ -161,3 +164,20 @@ def test_timeline_shows_the_reuse_edge(lib, arrays):
             say("  rewrites of stage t%%2 before the delayed wave started reading tile t: %d of %d"
                 % (early, len(refills) * len(others)))
             assert early > 0
+
+
+def test_failures_begin_when_the_delay_exceeds_the_rewrite_time(lib, arrays):
+    """Without the reuse barrier, the share of failing runs against the delay of
+    one consumer wave (200 runs per delay, the delayed wave rotating).  The
+    other waves rewrite the stage about as long after the top of the iteration
+    as their loads of tile t+2 take, so short delays leave the race unseen."""
+    xs, refs = arrays
+    rows_out = []
+    for cycles in (0, 256, 512, 768, 1024, 1536, 2048, 3072, 4096, 8192, 16384):
+        fails = 0
+        for i in range(200):
+            got = run(lib, xs[i % N_INPUTS], ROWS, COLS, COLS, 0, i % NWAVE, cycles)
+            fails += int(not torch.equal(got, refs[i % N_INPUTS]))
+        rows_out.append((cycles, fails))
+        say("  delay %5d cycles: %3d of 200 runs failed" % (cycles, fails))
+    assert rows_out[-1][1] == 200 and rows_out[-2][1] == 200
