@@ -34,15 +34,15 @@ PAGE_SGEMM_GFLOPS = 32107.5  # 2-stage SGEMM 4096^3 on the first page's (unnamed
 
 WORKLOADS = {
     "f32": dict(name="fp32 SGEMM M=N=K=4096 row-major alpha=1 beta=0.5", dtype="f32", M=4096, N=4096, K=4096,
-                alpha=1.0, beta=0.5, cfg=1, data="seeded uniform[-1,1) fp32"),
+                alpha=1.0, beta=0.5, seed="fp32_4096", data="seeded uniform[-1,1) fp32"),
     "i8": dict(name="int8 IGEMM M=N=K=4096 int32 out", dtype="i8", M=4096, N=4096, K=4096, alpha=1, beta=0,
-               cfg=2, data="seeded uniform int8 [-128,127]"),
+               seed="int8_4096", data="seeded uniform int8 [-128,127]"),
     "bf16": dict(name="bf16 GEMM M=N=K=4096 fp32 out", dtype="bf16", M=4096, N=4096, K=4096, alpha=1.0,
-                 beta=0.0, cfg=3, data="seeded normal(0,1) rounded to bf16"),
+                 beta=0.0, seed="half_4096", data="seeded normal(0,1) rounded to bf16"),
     "f16": dict(name="fp16 GEMM M=N=K=4096 fp32 out", dtype="f16", M=4096, N=4096, K=4096, alpha=1.0,
-                beta=0.0, cfg=3, data="seeded normal(0,1) rounded to fp16"),
+                beta=0.0, seed="half_4096", seed_variant=1, data="seeded normal(0,1) rounded to fp16"),
     "ragged": dict(name="bf16 GEMM M=4000 N=3968 K=4001 lda=4001 ldb=ldc=3968 fp32 out", dtype="bf16", M=4000,
-                   N=3968, K=4001, lda=4001, ldb=3968, ldc=3968, alpha=1.0, beta=0.0, cfg=4,
+                   N=3968, K=4001, lda=4001, ldb=3968, ldc=3968, alpha=1.0, beta=0.0, seed="bf16_k_sweep", seed_variant=9,
                    data="seeded normal(0,1) rounded to bf16"),
 }
 
@@ -153,7 +153,7 @@ def cpu_baseline(target_s=12.0):
     import oracle
     from software_pipelined_tiled_loop_amd import inputs
     M = N = K = 4096
-    op = inputs.make_operands("f32", M, N, K, seed=inputs.seed_for(1), alpha=1.0, beta=0.5)
+    op = inputs.make_operands("f32", M, N, K, seed=inputs.seed_for("fp32_4096"), alpha=1.0, beta=0.5)
     A, B, C0 = op.numpy_views()
     threads = oracle.num_threads()
     rows = 16
@@ -216,11 +216,12 @@ def main():
 
     # ---- timed workload (default: fp32 SGEMM 4096^3, alpha=1, beta=0.5) ----
     w = WORKLOADS[args.workload]
-    dt, M, N, K, alpha, beta, cfg_idx = w["dtype"], w["M"], w["N"], w["K"], w["alpha"], w["beta"], w["cfg"]
+    dt, M, N, K, alpha, beta = w["dtype"], w["M"], w["N"], w["K"], w["alpha"], w["beta"]
     tile = tuple(int(x) for x in args.tile.split("x")) if args.tile else None
     lda, ldb, ldc = w.get("lda", K), w.get("ldb", N), w.get("ldc", N)
     aligned = int(all(x * inputs.ELEM_BYTES[dt] % 16 == 0 for x in (lda, ldb, K, N)))
-    op, A, B, C = make_device_operands(dt, M, N, K, inputs.seed_for(cfg_idx), alpha, beta, lda, ldb, ldc)
+    op, A, B, C = make_device_operands(dt, M, N, K, inputs.seed_for(w["seed"], w.get("seed_variant", 0)), alpha, beta,
+                                       lda, ldb, ldc)
     plan = plan_of(lib, dt, M, N, K, args.stages, args.producer, tile, aligned=aligned)
     if plan is None:
         print("no compiled variant for these options", file=sys.stderr)
@@ -312,8 +313,9 @@ def run_reports(lib, torch):
     from software_pipelined_tiled_loop_amd import inputs
     rep = {}
     M = N = K = 4096
-    for dt, cfg, alpha, beta in (("i8", 2, 1, 0), ("bf16", 3, 1.0, 0.0), ("f16", 3, 1.0, 0.0)):
-        op, A, B, C = make_device_operands(dt, M, N, K, inputs.seed_for(cfg, 0 if dt != "f16" else 1), alpha, beta)
+    for dt, seed, alpha, beta in (("i8", inputs.seed_for("int8_4096"), 1, 0), ("bf16", inputs.seed_for("half_4096"), 1.0, 0.0),
+                                  ("f16", inputs.seed_for("half_4096", 1), 1.0, 0.0)):
+        op, A, B, C = make_device_operands(dt, M, N, K, seed, alpha, beta)
         ms = time_gemm(lib, op, A, B, C)
         auto = tflops(M, N, K, ms)
         rep["%s_4096" % dt] = {"auto": round(auto, 1), "pct_peak": round(100 * auto / PEAK[dt], 2),
@@ -323,7 +325,7 @@ def run_reports(lib, torch):
 
     # fp32 256^3 (alpha=1, beta=0): single vs double buffer on the pages' tile; launch-bound,
     # so also timed as replays of a HIP graph of 50 calls
-    op, A, B, C = make_device_operands("f32", 256, 256, 256, inputs.seed_for(0), 1.0, 0.0)
+    op, A, B, C = make_device_operands("f32", 256, 256, 256, inputs.seed_for("fp32_256"), 1.0, 0.0)
     small = {}
     for s in (1, 2):
         eager_ms = time_gemm(lib, op, A, B, C, stages=s, tile=(128, 64, 16), reps=50)
@@ -346,11 +348,11 @@ def run_reports(lib, torch):
         small["128x64x16 s%d direct" % s] = {"eager_us": round(eager_ms * 1e3, 2), "graph_us": round(graph_ms * 1e3, 2),
                                              "tflops_graph": round(tflops(256, 256, 256, graph_ms), 2)}
         del g
-    rep["f32_256_cfg0"] = small
+    rep["f32_256_pages_tile"] = small
     del A, B, C
 
     # fp32: the pages' tile class, 1 vs 2 stages, and the planner's choice
-    op, A, B, C = make_device_operands("f32", M, N, K, inputs.seed_for(1), 1.0, 0.5)
+    op, A, B, C = make_device_operands("f32", M, N, K, inputs.seed_for("fp32_4096"), 1.0, 0.5)
     d = {}
     for s in (1, 2):
         ms = time_gemm(lib, op, A, B, C, stages=s, tile=(128, 64, 16))
@@ -362,7 +364,7 @@ def run_reports(lib, torch):
     # bf16 K-sweep by ring depth (the planner picks the tile for each depth) + ragged
     sweep = {}
     for Ks in (32, 64, 256, 1024, 4096, 16384):
-        op, A, B, C = make_device_operands("bf16", M, N, Ks, inputs.seed_for(4, Ks % 97), 1.0, 0.0)
+        op, A, B, C = make_device_operands("bf16", M, N, Ks, inputs.seed_for("bf16_k_sweep", Ks % 97), 1.0, 0.0)
         row = {}
         for s in (1, 2, 3, 4):
             p = plan_of(lib, "bf16", M, N, Ks, stages=s)
@@ -381,7 +383,7 @@ def run_reports(lib, torch):
         sweep["K%d" % Ks] = row
         del A, B, C
     r = inputs.RAGGED
-    op, A, B, C = make_device_operands("bf16", r["M"], r["N"], r["K"], inputs.seed_for(4, 9), 1.0, 0.0,
+    op, A, B, C = make_device_operands("bf16", r["M"], r["N"], r["K"], inputs.seed_for("bf16_k_sweep", 9), 1.0, 0.0,
                                        lda=r["lda"], ldb=r["ldb"], ldc=r["ldc"])
     ms = time_gemm(lib, op, A, B, C)
     sweep["ragged_4000x3968x4001"] = {"tflops": round(tflops(r["M"], r["N"], r["K"], ms), 1),

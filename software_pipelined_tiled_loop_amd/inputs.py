@@ -22,7 +22,8 @@ When beta == 0, C is pre-filled with a poison value (NaN for float, 0x7F7F7F7F
 for int32) so a kernel that reads C when it must not is caught.
 
 Every generator is a CPU ``torch.Generator`` seeded explicitly; seeds are
-``1000 + 10*config_index + variant``.
+``1000 + 10*family + variant`` with the family of each workload in
+``SEED_FAMILY``.
 """
 from __future__ import annotations
 
@@ -38,8 +39,12 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
 POISON_I32 = 0x7F7F7F7F
 
 
-def seed_for(config_index: int, variant: int = 0) -> int:
-    return 1000 + 10 * config_index + variant
+# Seed family of each workload: its seeds are 1000 + 10 * family + variant.
+SEED_FAMILY = {"fp32_256": 0, "fp32_4096": 1, "int8_4096": 2, "half_4096": 3, "bf16_k_sweep": 4, "hazard": 7}
+
+
+def seed_for(workload: str, variant: int = 0) -> int:
+    return 1000 + 10 * SEED_FAMILY[workload] + variant
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -130,14 +135,6 @@ def make_operands(dtype: str, M: int, N: int, K: int, seed: int, alpha=1.0, beta
 
 
 # The five benchmark configurations (sizes and value distributions).
-CONFIGS = {
-    0: dict(name="fp32 256^3 alpha=1 beta=0", dtype="f32", M=256, N=256, K=256, alpha=1.0, beta=0.0),
-    1: dict(name="fp32 4096^3 alpha=1 beta=0.5", dtype="f32", M=4096, N=4096, K=4096, alpha=1.0, beta=0.5),
-    2: dict(name="int8 4096^3 int32 out", dtype="i8", M=4096, N=4096, K=4096, alpha=1, beta=0),
-    3: dict(name="bf16/fp16 4096^3 fp32 out", dtype="bf16", M=4096, N=4096, K=4096, alpha=1.0, beta=0.0),
-    4: dict(name="bf16 K-sweep M=N=4096", dtype="bf16", M=4096, N=4096,
-            K_sweep=(32, 64, 256, 1024, 4096, 16384), alpha=1.0, beta=0.0),
-}
 RAGGED = dict(dtype="bf16", M=4000, N=3968, K=4001, lda=4001, ldb=3968, ldc=3968)
 
 

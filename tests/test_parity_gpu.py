@@ -82,16 +82,14 @@ def padding_untouched(op, got):
             assert torch.equal(torch.isnan(pad), torch.isnan(ref))
 
 
-# ------------------------------------------------------------------ small configs
+# ------------------------------------------------------------------ small workloads
 
 @pytest.mark.parametrize("stages", [1, 2])
-def test_config0_fp32_256_single_vs_double(lib, stages):
-    cfg = inputs.CONFIGS[0]
-    say("cfg0 fp32 256^3 stages", stages, "tile 128x64x16")
-    op = inputs.make_operands("f32", 256, 256, 256, seed=inputs.seed_for(0), alpha=1.0, beta=0.0)
+def test_fp32_256_pages_tile_single_vs_double_buffer(lib, stages):
+    say("fp32 256^3 stages", stages, "tile 128x64x16")
+    op = inputs.make_operands("f32", 256, 256, 256, seed=inputs.seed_for("fp32_256"), alpha=1.0, beta=0.0)
     got = run_gpu(lib, op, stages=stages, tile=(128, 64, 16))
     check(op, got)
-    assert cfg["M"] == 256
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
@@ -100,7 +98,7 @@ def test_all_dtypes_all_stages_small(lib, dtype, stages):
     # several tiles in M and N plus ragged tails; K spans several K tiles + tail
     M, N, K = 300, 280, 16 * 37  # K multiple of 16 keeps every dtype on the vector path
     say("small", dtype, "stages", stages, (M, N, K))
-    op = inputs.make_operands(dtype, M, N, K, seed=inputs.seed_for(3, stages), alpha=1.0, beta=0.0)
+    op = inputs.make_operands(dtype, M, N, K, seed=inputs.seed_for("half_4096", stages), alpha=1.0, beta=0.0)
     got = run_gpu(lib, op, stages=stages)
     check(op, got)
 
@@ -340,7 +338,7 @@ def test_argument_errors_before_launch(lib):
     assert lib.pgemm_gemm(0, 8, 8, 1.0, 0, 8, 0, 8, 0.0, 0, 8, "bf16", 0) == 0
 
 
-# ------------------------------------------------------------------ full-size configs
+# ------------------------------------------------------------------ full-size workloads
 
 def sampled_rows(M, n=48, seed=0, run=12):
     """Rows in runs of `run` consecutive rows (the oracle parallelises a run):
@@ -352,20 +350,20 @@ def sampled_rows(M, n=48, seed=0, run=12):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name,dtype,M,N,K,alpha,beta,cfg", [
-    ("cfg1 fp32 4096^3 beta=0.5", "f32", 4096, 4096, 4096, 1.0, 0.5, 1),
-    ("cfg2 int8 4096^3", "i8", 4096, 4096, 4096, 1, 0, 2),
-    ("cfg3 bf16 4096^3", "bf16", 4096, 4096, 4096, 1.0, 0.0, 3),
-    ("cfg3 fp16 4096^3", "f16", 4096, 4096, 4096, 1.0, 0.0, 3),
-    ("cfg4 bf16 K=16384", "bf16", 4096, 4096, 16384, 1.0, 0.0, 4),
+@pytest.mark.parametrize("name,dtype,M,N,K,alpha,beta,workload", [
+    ("fp32 4096^3 beta=0.5", "f32", 4096, 4096, 4096, 1.0, 0.5, "fp32_4096"),
+    ("int8 4096^3", "i8", 4096, 4096, 4096, 1, 0, "int8_4096"),
+    ("bf16 4096^3", "bf16", 4096, 4096, 4096, 1.0, 0.0, "half_4096"),
+    ("fp16 4096^3", "f16", 4096, 4096, 4096, 1.0, 0.0, "half_4096"),
+    ("bf16 4096^2 K=16384", "bf16", 4096, 4096, 16384, 1.0, 0.0, "bf16_k_sweep"),
 ])
-def test_full_size_sampled(lib, name, dtype, M, N, K, alpha, beta, cfg):
+def test_full_size_sampled(lib, name, dtype, M, N, K, alpha, beta, workload):
     """The benchmark shapes with the planner's own launch (what bench.py times),
     checked on sampled rows against the oracle."""
     say(name)
-    op = inputs.make_operands(dtype, M, N, K, seed=inputs.seed_for(cfg), alpha=alpha, beta=beta)
+    op = inputs.make_operands(dtype, M, N, K, seed=inputs.seed_for(workload), alpha=alpha, beta=beta)
     got = run_gpu(lib, op, stages=0)
-    rows = sampled_rows(M, seed=cfg)
+    rows = sampled_rows(M, seed=inputs.SEED_FAMILY[workload])
     check(op, got, rows=rows)
 
 
@@ -385,7 +383,7 @@ def test_persistent_workgroups_full_size(lib):
 @pytest.mark.parametrize("K", [32, 64, 256, 1024])
 def test_k_sweep_sampled(lib, K):
     say("k-sweep K", K)
-    op = inputs.make_operands("bf16", 4096, 4096, K, seed=inputs.seed_for(4, K % 97), alpha=1.0, beta=0.0)
+    op = inputs.make_operands("bf16", 4096, 4096, K, seed=inputs.seed_for("bf16_k_sweep", K % 97), alpha=1.0, beta=0.0)
     for stages in (0, 1, 4):
         got = run_gpu(lib, op, stages=stages)
         check(op, got, rows=sampled_rows(4096, n=24, seed=K))
@@ -394,7 +392,7 @@ def test_k_sweep_sampled(lib, K):
 def test_ragged_4000_3968_4001(lib):
     r = inputs.RAGGED
     say("ragged", r)
-    op = inputs.make_operands("bf16", r["M"], r["N"], r["K"], seed=inputs.seed_for(4, 9), alpha=1.0, beta=0.0,
+    op = inputs.make_operands("bf16", r["M"], r["N"], r["K"], seed=inputs.seed_for("bf16_k_sweep", 9), alpha=1.0, beta=0.0,
                               lda=r["lda"], ldb=r["ldb"], ldc=r["ldc"])
     got = run_gpu(lib, op, stages=0)
     check(op, got, rows=sampled_rows(r["M"], n=24, seed=9))
