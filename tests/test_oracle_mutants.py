@@ -6,7 +6,8 @@ step -- the "forgotten epilogue tile" of page "GPU-Kernel pipelinen", common
 pitfalls -- a wrong fp16 exponent bias, a wrong bf16 shift, an unsigned int8
 read), builds it with gcc and runs a battery of the same kinds of pins used in
 test_oracle_pins.py.  The unmodified source must pass the battery and every
-mutant must fail it.  Nothing here touches a GPU.
+mutant must fail it.  The oracle's row sums (Python) get the same treatment.
+Nothing here touches a GPU.
 """
 import itertools
 import os
@@ -106,3 +107,52 @@ def test_planted_mistake_is_caught(tmp_path, name):
     if shutil.which("gcc") is None:
         pytest.skip("gcc not available")
     assert not battery(_build(tmp_path, name, MUTANTS[name])), "pins missed mutant %s" % name
+
+
+# ---------------------------------------------------------------- row sums
+# Planted mistakes in oracle.row_sums (the hazard demonstrator's reduction):
+# a dropped last column, padding summed in, saturation in place of the int32
+# wrap, the row stride taken from cols instead of ldx.
+ROW_SUM_MUTANTS = {
+    "drop_last_column": ("flat[r * ldx:r * ldx + cols]", "flat[r * ldx:r * ldx + cols - 1]"),
+    "padding_summed": ("flat[r * ldx:r * ldx + cols]", "flat[r * ldx:r * ldx + ldx]"),
+    "saturating": ("out[r] = (s + 2 ** 31) % 2 ** 32 - 2 ** 31", "out[r] = max(min(s, 2 ** 31 - 1), -2 ** 31)"),
+    "stride_from_cols": ("flat[r * ldx:r * ldx + cols]", "flat[r * cols:r * cols + cols]"),
+}
+
+
+def _row_sums_from(patch):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "__init__.py")).read()
+    if patch is not None:
+        old, new = patch
+        assert src.count(old) == 1, "mutation anchor not found exactly once: %s" % (old,)
+        src = src.replace(old, new)
+    ns = {"__name__": "oracle_mutant", "__file__": oracle.__file__}
+    exec(compile(src, "oracle_mutant", "exec"), ns)
+    return ns["row_sums"]
+
+
+def row_sum_battery(row_sums):
+    """The same kinds of pins as test_oracle_pins.py: closed forms, unbounded
+    integers modulo 2^32 with padding, and the wrap of two int32 maxima."""
+    rows, cols = 5, 40
+    X = (np.arange(rows, dtype=np.int64)[:, None] * cols + np.arange(cols)).astype(np.int32)
+    if row_sums(X, rows, cols).tolist() != [r * cols * cols + cols * (cols - 1) // 2 for r in range(rows)]:
+        return False
+    rng = random.Random(3)
+    for rows, cols, ldx in [(3, 5, 5), (4, 9, 13), (2, 64, 70)]:
+        vals = [[rng.randint(-2 ** 31, 2 ** 31 - 1) for _ in range(ldx)] for _ in range(rows)]
+        got = row_sums(np.array(vals, np.int64).astype(np.int32), rows, cols, ldx)
+        for r in range(rows):
+            if int(got[r]) != (sum(vals[r][:cols]) + 2 ** 31) % 2 ** 32 - 2 ** 31:
+                return False
+    return row_sums(np.array([[2 ** 31 - 1, 2 ** 31 - 1, 7]], np.int32), 1, 2, 3).tolist() == [-2]
+
+
+def test_unmodified_row_sums_pass_battery():
+    assert row_sum_battery(_row_sums_from(None))
+
+
+@pytest.mark.parametrize("name", sorted(ROW_SUM_MUTANTS))
+def test_planted_row_sum_mistake_is_caught(name):
+    assert not row_sum_battery(_row_sums_from(ROW_SUM_MUTANTS[name])), "pins missed mutant %s" % name
