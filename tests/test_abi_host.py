@@ -168,6 +168,19 @@ def test_planner_picks_the_tile_measured_fastest(dtype, shape, tile):
     assert (p["tile_m"], p["tile_n"], p["tile_k"]) == tile
 
 
+def test_torch_wrapper_rejects_tensors_that_are_not_row_major():
+    """binding.gemm refuses, before anything reaches the library, tensors
+    whose columns are not contiguous or that are not 2-D."""
+    import torch
+    A, B, C = torch.zeros(8, 8), torch.zeros(8, 8), torch.zeros(8, 8)
+    with pytest.raises(ValueError):
+        lib.gemm(A.t(), B, C)
+    with pytest.raises(ValueError):
+        lib.gemm(A, B[:, ::2], C)
+    with pytest.raises(ValueError):
+        lib.gemm(A, B, C[None])
+
+
 def test_strerror_covers_every_status():
     for code in range(0, -8, -1):
         assert lib.pgemm_strerror(code) != "unknown status"

@@ -82,6 +82,27 @@ def padding_untouched(op, got):
             assert torch.equal(torch.isnan(pad), torch.isnan(ref))
 
 
+# ------------------------------------------------------------------ torch wrapper
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_torch_wrapper_on_column_slices(lib, dtype):
+    """binding.gemm takes the sizes from the tensor shapes, the leading
+    dimensions from the row strides and the dtype from A.  Here A, B and C are
+    column slices of wider tensors, so lda, ldb and ldc exceed K and N; the
+    columns of C beyond the slice must stay untouched."""
+    M, N, K = 200, 136, 300
+    alpha = 2 if dtype == "i8" else 1.5
+    say("torch wrapper", dtype, (M, N, K))
+    op = inputs.make_operands(dtype, M, N, K, seed=inputs.seed_for("half_4096", 40), alpha=alpha, beta=0.0,
+                              lda=K + 8, ldb=N + 24, ldc=N + 8)
+    A, B, C = op.A.cuda(), op.B.cuda(), op.C.cuda()
+    lib.gemm(A[:, :K], B[:, :N], C[:, :N], alpha=alpha)
+    torch.cuda.synchronize()
+    got = C.cpu()
+    check(op, got)
+    padding_untouched(op, got)
+
+
 # ------------------------------------------------------------------ small workloads
 
 @pytest.mark.parametrize("stages", [1, 2])
