@@ -373,7 +373,7 @@ static int check_work_split() {
     }
     for (int tm = 1; tm <= 20; ++tm)
         for (int tn = 1; tn <= 20; ++tn)
-            for (int gm = 1; gm <= 6; ++gm) {
+            for (int gm = 1; gm <= 20; ++gm) {
                 std::vector<int> hit(tm * tn, 0);
                 for (int L = 0; L < tm * tn; ++L) {
                     int a, b;
