@@ -6,7 +6,7 @@ consumer, with failure counts.  Here the library's stress hook skews one wave
 of every workgroup per K tile (rotating) by ~8k cycles after the ready
 barrier, so the other waves reach the next barrier, and issue the next
 tile's loads into the freed stage, far ahead of it.  Every launch must give
-exactly the same int8 result, equal to the oracle: 6 variants x 200 runs.
+exactly the same int8 result, equal to the oracle: 6 variants x 1000 runs.
 The GEMM has no build with a wait removed.  The reuse edge's removal is shown
 by the host model checker (tests/test_schedule_model.py) and, on the GPU, by
 the two-stage copy-and-reduce demonstrator (tests/test_hazard_gpu.py), whose
@@ -29,7 +29,7 @@ pytestmark = pytest.mark.gpu
 def test_skewed_waves_many_runs_bit_exact(producer, stages, tile):
     from software_pipelined_tiled_loop_amd import binding as lib
     M, N, K = 1024, 1024, 768
-    runs = 200
+    runs = 1000
     print("[case] stress", producer, stages, tile, "runs", runs, flush=True)
     op = inputs.make_operands("i8", M, N, K, seed=4321 + stages, alpha=1, beta=0)
     A, B = op.A.cuda(), op.B.cuda()
