@@ -83,27 +83,19 @@ WARMUP_MS = 150.0
 TRIAL_MS = 5.0
 
 
-def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=None, warmup=None, trials=5):
-    """ms per call: the median over `trials` of the average over `reps`
-    back-to-back launches (HIP events on the launch stream), `reps` chosen so
-    that a trial lasts about TRIAL_MS (at least 20 launches).  The median
-    keeps a disturbed trial (clock ramp, a profiler's buffer flush) out of the
-    reported sweep points; with 20-launch trials, kernels of ~15 us varied by
-    10 % between identical runs.  Warm-up runs the kernel for about
-    WARMUP_MS first: after the GPU has idled (while the host draws the next
-    operands) its clock takes on the order of 100 ms of load to settle, and
-    with a 20 ms warm-up the first of several successive timings of one
-    kernel read 10-13 % low."""
+def time_calls(call, reps=None, warmup=None, trials=5):
+    """ms per call of `call` (which launches on the current stream): the
+    median over `trials` of the average over `reps` back-to-back calls (HIP
+    events on that stream), `reps` chosen so that a trial lasts about
+    TRIAL_MS (at least 20 calls).  The median keeps a disturbed trial (clock
+    ramp, a profiler's buffer flush) out of the reported sweep points; with
+    20-launch trials, kernels of ~15 us varied by 10 % between identical
+    runs.  Warm-up runs the call for about WARMUP_MS first: after the GPU has
+    idled (while the host draws the next operands) its clock takes on the
+    order of 100 ms of load to settle, and with a 20 ms warm-up the first of
+    several successive timings of one kernel read 10-13 % low."""
     import torch
     stream = torch.cuda.current_stream()
-    opts = lib._opts(producer, tile)
-
-    def call():
-        r = lib.pgemm_gemm_ex(op.M, op.N, op.K, op.alpha, A, op.lda, B, op.ldb, op.beta, C, op.ldc, op.dtype,
-                              stages, opts, stream)
-        if r != 0:
-            raise lib.PgemmError(r)
-
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     if warmup is None:
@@ -130,6 +122,21 @@ def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=None, w
         e1.synchronize()
         times.append(e0.elapsed_time(e1) / reps)
     return sorted(times)[len(times) // 2]
+
+
+def time_gemm(lib, op, A, B, C, stages=0, producer=None, tile=None, reps=None, warmup=None, trials=5):
+    """ms per pgemm call (see time_calls)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    opts = lib._opts(producer, tile)
+
+    def call():
+        r = lib.pgemm_gemm_ex(op.M, op.N, op.K, op.alpha, A, op.lda, B, op.ldb, op.beta, C, op.ldc, op.dtype,
+                              stages, opts, stream)
+        if r != 0:
+            raise lib.PgemmError(r)
+
+    return time_calls(call, reps=reps, warmup=warmup, trials=trials)
 
 
 def tflops(M, N, K, ms):
@@ -309,6 +316,42 @@ def variant_sweep(lib, op, A, B, C, M, N, K, reps=None):
     return out
 
 
+def vendor_call(torch, dt, A, B, C, op):
+    """The same product through the vendor library behind torch (hipBLASLt /
+    rocBLAS), for context only: fp32 as C = alpha*A*B + beta*C in place;
+    int8 through torch._int_mm (int32 out, beta = 0); fp16/bf16 through
+    torch.mm, whose output is in the input type (half the C bytes of the
+    fp32 output here)."""
+    if dt == "f32":
+        return lambda: C.addmm_(A, B, beta=op.beta, alpha=op.alpha)
+    if dt == "i8":
+        return lambda: torch._int_mm(A, B)
+    return lambda: torch.mm(A, B)
+
+
+def pages_context(rep):
+    """The pages' own figures, measured on other hardware (context only),
+    beside the same ratios measured here.  The first page's two SGEMM
+    kernels (its 128 x 64 x 16 tile, 1 and 2 stages) as a share of the vendor
+    library on its unnamed NVIDIA GPU; the German page's gain from
+    asynchronous-copy pipelining on a 4096^3 int8 GEMM on GA104, against the
+    int8 256 x 256 x 128 tile here at 2 stages over 1."""
+    f = rep["f32_4096_page_tile"]
+    v8 = rep["i8_4096"]["variants"]
+    s1, s2 = v8.get("256x256x128 s1 direct"), v8.get("256x256x128 s2 direct")
+    return {
+        "sgemm_pct_of_vendor_blas": {
+            "pages": {"1 stage": 81.9, "2 stages": 89.2, "hardware": "first page's NVIDIA GPU (model not named)"},
+            "here": {"128x64x16 s1": round(100 * f["128x64x16 s1 direct"] / f["vendor_blas"], 1),
+                     "128x64x16 s2": round(100 * f["128x64x16 s2 direct"] / f["vendor_blas"], 1),
+                     "planner": round(100 * f["auto"] / f["vendor_blas"], 1), "hardware": "MI355X"}},
+        "int8_4096_pipelining_gain_pct": {
+            "pages": {"async-copy pipeline over none": 35, "hardware": "GA104"},
+            "here": {"256x256x128 s2 over s1": round(100 * (s2 / s1 - 1), 1) if s1 and s2 else None,
+                     "hardware": "MI355X"}},
+    }
+
+
 def run_reports(lib, torch):
     from software_pipelined_tiled_loop_amd import inputs
     rep = {}
@@ -320,7 +363,8 @@ def run_reports(lib, torch):
         auto = tflops(M, N, K, ms)
         rep["%s_4096" % dt] = {"auto": round(auto, 1), "pct_peak": round(100 * auto / PEAK[dt], 2),
                                "plan": plan_label(plan_of(lib, dt, M, N, K)),
-                               "variants": variant_sweep(lib, op, A, B, C, M, N, K)}
+                               "variants": variant_sweep(lib, op, A, B, C, M, N, K),
+                               "vendor_blas": round(tflops(M, N, K, time_calls(vendor_call(torch, dt, A, B, C, op))), 1)}
         del A, B, C
 
     # fp32 256^3 (alpha=1, beta=0): single vs double buffer on the pages' tile; launch-bound,
@@ -358,8 +402,11 @@ def run_reports(lib, torch):
         ms = time_gemm(lib, op, A, B, C, stages=s, tile=(128, 64, 16))
         d["128x64x16 s%d direct" % s] = round(tflops(M, N, K, ms), 2)
     d["compute_load_ratio"] = round(lib.pgemm_model_compute_load_ratio(128, 64, 16, 4), 2)
+    d["auto"] = round(tflops(M, N, K, time_gemm(lib, op, A, B, C)), 2)
+    d["vendor_blas"] = round(tflops(M, N, K, time_calls(vendor_call(torch, "f32", A, B, C, op))), 2)
     rep["f32_4096_page_tile"] = d
     del A, B, C
+    rep["pages_context"] = pages_context(rep)
 
     # bf16 K-sweep by ring depth (the planner picks the tile for each depth) + ragged
     sweep = {}

@@ -406,20 +406,25 @@ __device__ __forceinline__ DmaTile dma_setup(const KernelArgs& g, int m0, int n0
 }
 
 // Load piece q (0..LPS-1) of the tile: one 1-KiB LDS-DMA block of A (q <
-// A_INSTR) or of B.
-template <class C>
+// A_INSTR) or of B.  FULL: the caller guarantees a whole K tile of a whole
+// output tile (k_left >= BK, rows_left >= BM, n_left >= BN), so every lane is
+// in range and its offset goes to the load as it is, with no per-lane select
+// (the select's destination would be a temporary register written right
+// under the MFMAs, which stalls the matrix pipe when the register was one of
+// their operands).
+template <class C, bool FULL = false>
 __device__ __forceinline__ void dma_piece(const KernelArgs& g, const DmaTile& d, int q, int wave, int lane) {
     constexpr int ES = C::ES;
     if (q < C::A_INSTR) {
         int row, kel;
         a_chunk<C>(wave, lane, q, row, kel);
-        const bool ok = row < d.rows_left && kel < d.k_left;
+        const bool ok = FULL || (row < d.rows_left && kel < d.k_left);
         dma16(d.ra, ok ? (uint32_t)(row * (int)g.lda + kel) * ES : OOB, d.sa + (uint32_t)q * 1024u);
     } else {
         const int qb = q - C::A_INSTR;
         int krow, nel;
         b_chunk<C>(wave, lane, qb, krow, nel);
-        const bool ok = krow < d.k_left && nel < d.n_left;
+        const bool ok = FULL || (krow < d.k_left && nel < d.n_left);
         dma16(d.rb, ok ? (uint32_t)(krow * (int)g.ldb + nel) * ES : OOB, d.sb + (uint32_t)qb * 1024u);
     }
 }
@@ -644,7 +649,7 @@ __device__ __forceinline__ void mfma_all(typename C::T::Acc (&acc)[C::FM][C::FN]
 // blocks of the tile being issued); after every group: a share of the next
 // step's fragment reads, so none of that issue time leaves the matrix pipe
 // idle.  sched_barrier keeps the groups in this order.
-template <class C, bool READS, bool DMA>
+template <class C, bool READS, bool DMA, bool FULL = false>
 __device__ __forceinline__ void mfma_step(typename C::T::Acc (&acc)[C::FM][C::FN], const Frags<C>& use,
                                           Frags<C>& nxt, const char PGEMM_LDS* rstage, int rks,
                                           const KernelArgs& g, const DmaTile& d, int wave, int lane, int wm0,
@@ -664,7 +669,7 @@ __device__ __forceinline__ void mfma_step(typename C::T::Acc (&acc)[C::FM][C::FN
         if constexpr (DMA) {
 #pragma unroll
             for (int p = gi * PPG; p < (gi + 1) * PPG; ++p)
-                if (p < NP) dma_piece<C>(g, d, p, wave, lane);
+                if (p < NP) dma_piece<C, FULL>(g, d, p, wave, lane);
         }
         if constexpr (READS) {
 #pragma unroll
@@ -770,7 +775,7 @@ __device__ __forceinline__ Cursor cursor_at(const KernelArgs& g, const WgTiles& 
 // constant.  `lc` is the slot to load (DIRECT: s+S; register producers:
 // s+S+1, one more being in flight in registers).  PAR is the fragment buffer
 // holding step 0 of this slot.
-template <class C, int PAR>
+template <class C, int PAR, bool FULL = false>
 __device__ __forceinline__ void tile_body(const KernelArgs& g, const Cursor& lc, int s, char PGEMM_LDS* smem, int& cur,
                                           Staging<C>& st, Frags<C> (&f)[2],
                                           typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane, int wm0,
@@ -792,7 +797,7 @@ __device__ __forceinline__ void tile_body(const KernelArgs& g, const Cursor& lc,
             char PGEMM_LDS* freed = smem + cur * C::STAGE_BYTES;
             if constexpr (C::P == PROD_DIRECT) {
                 const DmaTile d = dma_setup<C>(g, lc.m0, lc.n0, lc.kt, freed, wave);  // slot s+S (maybe none)
-                mfma_step<C, true, true>(acc, use, nxt, rstage, 0, g, d, wave, lane, wm0, wn0);
+                mfma_step<C, true, true, FULL>(acc, use, nxt, rstage, 0, g, d, wave, lane, wm0, wn0);
             } else {
                 store_tile<C>(freed, st, wave, lane);                          // slot s+S, loaded since B_s
                 issue_tile<C>(g, lc.m0, lc.n0, lc.kt, freed, st, wave, lane);  // slot s+S+1 into registers
@@ -844,11 +849,23 @@ __device__ __forceinline__ void pertile_loop(const KernelArgs& g, int m0, int n0
     }
     read_frags<C>(smem, 0, wm0, wn0, lane, f[0]);
     int cur = 0;
+    // Slots t < nfull load a whole K tile of a whole output tile (the
+    // DIRECT producer then issues its loads without per-lane range selects);
+    // the rest, up to LA + 1 of them, take the general path.
+    const bool whole_mn = C::P == PROD_DIRECT && m0 + C::BM <= g.M && n0 + C::BN <= g.N;
+    const int nfull = whole_mn && g.K / C::BK > LA ? g.K / C::BK - LA : 0;
     if constexpr (NKS % 2 == 0) {
-        for (int t = 0; t < nK; ++t)
+        int t = 0;
+        for (; t < nfull; ++t)
+            tile_body<C, 0, true>(g, Cursor{t + LA, m0, n0}, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+        for (; t < nK; ++t)
             tile_body<C, 0>(g, Cursor{t + LA, m0, n0}, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
     } else {
         int t = 0;
+        for (; t + 1 < nfull; t += 2) {
+            tile_body<C, 0, true>(g, Cursor{t + LA, m0, n0}, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+            tile_body<C, 1, true>(g, Cursor{t + 1 + LA, m0, n0}, t + 1, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+        }
         for (; t + 1 < nK; t += 2) {
             tile_body<C, 0>(g, Cursor{t + LA, m0, n0}, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
             tile_body<C, 1>(g, Cursor{t + 1 + LA, m0, n0}, t + 1, smem, cur, st, f, acc, wave, lane, wm0, wn0);

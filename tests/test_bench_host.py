@@ -74,3 +74,22 @@ def test_every_workload_has_a_plan():
         lda, ldb = w.get("lda", K), w.get("ldb", N)
         aligned = int(all(x * inputs.ELEM_BYTES[dt] % 16 == 0 for x in (lda, ldb, K, N)))
         assert bench.plan_of(lib, dt, M, N, K, aligned=aligned) is not None, name
+
+
+def test_pages_context_ratios():
+    """The report's context block: the pages' figures verbatim, and the same
+    ratios from the measured points (vendor share; int8 2-stage gain)."""
+    rep = {"f32_4096_page_tile": {"128x64x16 s1 direct": 120.0, "128x64x16 s2 direct": 135.0, "auto": 145.0,
+                                  "vendor_blas": 150.0},
+           "i8_4096": {"variants": {"256x256x128 s1 direct": 1500.0, "256x256x128 s2 direct": 2100.0}}}
+    c = bench.pages_context(rep)
+    assert c["sgemm_pct_of_vendor_blas"]["pages"]["1 stage"] == 81.9
+    assert c["sgemm_pct_of_vendor_blas"]["pages"]["2 stages"] == 89.2
+    assert c["sgemm_pct_of_vendor_blas"]["here"]["128x64x16 s1"] == 80.0
+    assert c["sgemm_pct_of_vendor_blas"]["here"]["128x64x16 s2"] == 90.0
+    assert c["int8_4096_pipelining_gain_pct"]["pages"]["async-copy pipeline over none"] == 35
+    assert c["int8_4096_pipelining_gain_pct"]["here"]["256x256x128 s2 over s1"] == 40.0
+    # the int8 labels are the ones the variant sweep produces
+    labels = {bench.plan_label(lib.pgemm_variant_info(i)) for i in range(lib.pgemm_num_variants())
+              if lib.pgemm_variant_info(i)["dtype"] == "i8"}
+    assert {"256x256x128 s1 direct", "256x256x128 s2 direct"} <= labels
