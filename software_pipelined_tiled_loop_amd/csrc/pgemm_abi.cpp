@@ -125,12 +125,12 @@ struct ClassModel {
 ClassModel class_model(const VariantDesc& d) {
     struct E { int dt, bm, bn, bk; double e, lam; };
     static const E table[] = {
-        {PGEMM_BF16, 256, 256, 64, 0.504, 0.0}, {PGEMM_BF16, 256, 256, 32, 0.481, 0.0},
-        {PGEMM_BF16, 128, 128, 64, 0.400, 0.37}, {PGEMM_F16, 256, 256, 64, 0.475, 0.0},
-        {PGEMM_F16, 256, 256, 32, 0.459, 0.0},  {PGEMM_F16, 128, 128, 64, 0.387, 0.37},
-        {PGEMM_I8, 256, 256, 128, 0.445, 0.0},  {PGEMM_I8, 256, 256, 64, 0.426, 0.0},
-        {PGEMM_I8, 128, 128, 128, 0.346, 0.37}, {PGEMM_F32, 256, 256, 32, 0.92, 0.0},
-        {PGEMM_F32, 128, 64, 16, 0.90, 0.11},   {PGEMM_F32, 128, 128, 32, 0.82, 0.3},
+        {PGEMM_BF16, 256, 256, 64, 0.541, 0.0}, {PGEMM_BF16, 256, 256, 32, 0.510, 0.0},
+        {PGEMM_BF16, 128, 128, 64, 0.392, 0.37}, {PGEMM_F16, 256, 256, 64, 0.516, 0.0},
+        {PGEMM_F16, 256, 256, 32, 0.477, 0.0},  {PGEMM_F16, 128, 128, 64, 0.375, 0.37},
+        {PGEMM_I8, 256, 256, 128, 0.473, 0.0},  {PGEMM_I8, 256, 256, 64, 0.447, 0.0},
+        {PGEMM_I8, 128, 128, 128, 0.351, 0.37}, {PGEMM_F32, 256, 256, 32, 0.943, 0.0},
+        {PGEMM_F32, 128, 64, 16, 0.949, 0.11},  {PGEMM_F32, 128, 128, 32, 0.82, 0.3},
     };
     for (const E& x : table)
         if (x.dt == d.dtype && x.bm == d.bm && x.bn == d.bn && x.bk == d.bk) return {x.e, x.lam};
