@@ -152,7 +152,12 @@ def tile_classes(lib, dtype):
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
 def test_bit_identical_across_stages_and_producers(lib, dtype):
     """One tile class = one MFMA schedule: every ring depth and producer must
-    give the same bits (a stale, duplicated or skipped K tile would not)."""
+    give the same bits (a stale, duplicated or skipped K tile would not).
+    384 x 320 holds both whole output tiles and edge tiles for every class:
+    with the DIRECT producer the whole ones load all but their last K tiles
+    without per-lane range selects, the edge ones take the general path, and
+    the register producers never take the select-free path, so this also
+    pins that path against the general one bit for bit."""
     M, N, K = 384, 320, 16 * 40
     op = inputs.make_operands(dtype, M, N, K, seed=4242, alpha=1.0, beta=0.0)
     for tile, variants in tile_classes(lib, dtype).items():
