@@ -255,10 +255,12 @@ struct Cfg {
     static constexpr int A_ROWS_PER_KB = 1024 / (BK * ES);
     static constexpr int NKS = BK / KSTEP;               // MFMA K steps per tile
     // MFMA groups of a K step that the DMA blocks of the next tile are spread
-    // over (see mfma_step).  Measured on MI355X at 4096^3: fp32 (one long
-    // MFMA per block) is 0.7 % faster with the blocks in the first two groups,
-    // bf16 and int8 1-4 % faster with them spread over all eight.
-    static constexpr int DMA_GROUPS = D == DT_F32 ? 2 : 8;
+    // over (see mfma_step).  Measured on MI355X at 4096^3 (whole-tile loads,
+    // alternating rounds): fp32 (one long MFMA per block) is fastest with the
+    // blocks in the first four groups (0.3 % ahead of two, 0.4 % of eight),
+    // bf16 and int8 2-3 % faster with them spread over all eight than over
+    // four.
+    static constexpr int DMA_GROUPS = D == DT_F32 ? 4 : 8;
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be whole 16x16 blocks");
     static_assert(BK % KSTEP == 0, "BK must be a multiple of the MFMA K step");
     static_assert(KC == 4 || KC == 8, "A rows must be 64 or 128 bytes");
