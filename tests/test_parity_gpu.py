@@ -171,6 +171,40 @@ def test_bit_identical_across_stages_and_producers(lib, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_whole_tile_load_path_boundaries(lib, dtype):
+    """With the DIRECT producer an output tile that lies wholly inside C loads
+    its slots t + S < K / BK without per-lane range selects and the rest on
+    the general path.  For every DIRECT tile class, K is swept over 2..6 K
+    tiles, whole and with a tail, so that the number of select-free slots runs
+    through -1..4 for each ring depth; M = 520 adds edge tiles beside whole
+    ones.  Each depth must match the oracle and give the same bits as every
+    other depth of its class, the single-buffer loop included."""
+    es = inputs.ELEM_BYTES[dtype]
+    epc = 16 // es
+    classes = {}
+    for i in range(lib.pgemm_num_variants()):
+        v = lib.pgemm_variant_info(i)
+        if v["dtype"] == dtype and v["producer"] == "direct":
+            classes.setdefault((v["tile_m"], v["tile_n"], v["tile_k"]), []).append(v["stages"])
+    for bk in sorted({t[2] for t in classes}):
+        for n in range(2, 7):
+            for K in (bk * n, bk * n + epc):
+                M = 520 if n % 2 else 512
+                op = inputs.make_operands(dtype, M, 512, K, seed=inputs.seed_for("half_4096", 50 + n), alpha=1.0,
+                                          beta=0.0)
+                for tile, depths in sorted(classes.items()):
+                    if tile[2] != bk:
+                        continue
+                    outs = []
+                    for stages in sorted(depths):
+                        say("whole-tile path", dtype, tile, "K", K, "M", M, "stages", stages)
+                        outs.append((stages, run_gpu(lib, op, stages=stages, producer="direct", tile=tile)))
+                    check(op, outs[0][1])
+                    for stages, o in outs[1:]:
+                        assert torch.equal(o.view(torch.int32), outs[0][1].view(torch.int32)), (tile, K, stages)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
 def test_persistent_workgroups_bit_identical(lib, dtype):
     """Persistent workgroups stream the K tiles of several output tiles through
     one ring (the next tile's loads overlap this tile's last K tiles and its
