@@ -29,7 +29,9 @@
 // Producers (page "Double Buffering...", section "Two Stages, One Barrier";
 // page "GPU-Kernel pipelinen", step 2):
 //   DIRECT    buffer_load_dwordx4 ... lds: global memory straight into the LDS
-//             stage without registers; completion observed with vmcnt.
+//             stage without registers; completion observed with vmcnt.  Slots
+//             that load a whole K tile of a whole output tile pass each lane's
+//             offset unselected (no range check can fail there).
 //   REGISTER  buffer_load_dwordx4 into VGPRs at the top of the iteration,
 //             ds_write_b128 into the stage after the MFMA work.
 //   GENERIC   as REGISTER for any element-aligned layout: 16-byte loads at
