@@ -152,12 +152,14 @@ def test_hazard_without_rows_is_a_noop():
 
 
 @pytest.mark.parametrize("dtype,shape,tile", [
-    ("f32", (4096, 4096, 4096), (256, 256, 32)), ("bf16", (4096, 4096, 4096), (256, 256, 64)),
+    ("f32", (4096, 4096, 4096), (128, 64, 16)), ("bf16", (4096, 4096, 4096), (256, 256, 64)),
     ("f16", (4096, 4096, 4096), (256, 256, 64)), ("i8", (4096, 4096, 4096), (256, 256, 128)),
     ("bf16", (3000, 3000, 3000), (256, 256, 64)), ("bf16", (6144, 6144, 6144), (256, 256, 64)),
     ("bf16", (5120, 5120, 5120), (256, 256, 64)), ("bf16", (2048, 2048, 2048), (128, 128, 64)),
     ("f32", (1024, 1024, 1024), (128, 64, 16)), ("f32", (2048, 2048, 2048), (128, 64, 16)),
     ("f16", (4096, 4096, 256), (256, 256, 64)), ("i8", (2560, 2560, 2560), (128, 128, 128)),
+    ("f32", (8192, 8192, 1024), (128, 64, 16)), ("f32", (4096, 4096, 512), (128, 64, 16)),
+    ("f32", (8192, 4096, 4096), (128, 64, 16)),
 ])
 def test_planner_picks_the_tile_measured_fastest(dtype, shape, tile):
     """A regression check of the planner's cost model, not a correctness
