@@ -32,8 +32,9 @@
  *     the generic producer (16-byte loads through registers wherever the bytes
  *     lie inside the matrix, element loads at its very end; slower, same
  *     results).
- *   - 32-bit tile addressing: M, N, K < 2^31, lda * elem * 256, ldb * elem *
- *     128 and ldc * 4 * 256 below 2^31 bytes; otherwise PGEMM_ERR_TOO_LARGE.
+ *   - 32-bit tile addressing: M, N, K <= 2^31 - 256, lda * elem * 256, ldb *
+ *     elem * 128 and ldc * 4 * 256 below 2^31 bytes; otherwise
+ *     PGEMM_ERR_TOO_LARGE.
  *   - Return value: PGEMM_OK (0) or a negative pgemm_status.  Argument errors
  *     are detected on the host before anything is enqueued.
  */

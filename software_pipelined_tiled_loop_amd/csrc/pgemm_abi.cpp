@@ -486,8 +486,9 @@ int pgemm_gemm_ex(int64_t M, int64_t N, int64_t K, double alpha, const void* A, 
     if (K > 0 && (!A || !B)) return PGEMM_ERR_INVALID_ARG;
     const int es = elem_bytes(dtype);
     const int epc = 16 / es;
-    // 32-bit tile addressing: byte offsets inside one tile must stay below 2^31.
-    if (M > 0x7fffffff || N > 0x7fffffff || K > 0x7fffffff) return PGEMM_ERR_TOO_LARGE;
+    // 32-bit tile addressing: byte offsets inside one tile must stay below 2^31,
+    // and a tile origin plus one tile extent (at most 256) must fit a 32-bit int.
+    if (M > 0x7fffff00 || N > 0x7fffff00 || K > 0x7fffff00) return PGEMM_ERR_TOO_LARGE;
     if ((double)lda * es * 256.0 >= 2147483648.0 || (double)ldb * es * 128.0 >= 2147483648.0 ||
         (double)ldc * 4.0 * 256.0 >= 2147483648.0)
         return PGEMM_ERR_TOO_LARGE;

@@ -64,6 +64,9 @@ FAKE = 1 << 20  # never dereferenced: every case below fails validation first
     (dict(A=None), -1),
     (dict(C=None), -1),
     (dict(lda=1 << 26, dtype="f32"), -7),
+    (dict(M=2 ** 31 - 255), -7),           # a tile origin plus one tile would overflow 32 bits
+    (dict(N=2 ** 31 - 255, ldb=2 ** 31 - 255, ldc=2 ** 31 - 255), -7),
+    (dict(K=2 ** 31 - 255, lda=2 ** 31 - 255), -7),
     (dict(A=FAKE + 1, dtype="f32"), -1),   # not element aligned
 ])
 def test_argument_errors_before_any_launch(args, code):
