@@ -6,8 +6,8 @@
 //   * tile: the compiled tile class with the smallest estimated time of the
 //     busiest CU (its tiles in rounds of co-resident workgroups, a partial
 //     last round at its measured cost, a prologue per round), each class
-//     estimated at the ring depth it would run with; near-equal estimates go
-//     to the larger tile;
+//     estimated at the ring depth it would run with; for fp16, bf16 and
+//     int8 near-equal estimates go to the larger tile (tie_margin);
 //   * stages (DIRECT): the smallest ring depth whose lookahead covers the load latency,
 //     using the uncovered-latency estimate max(0, L - (S-1)*C) of page
 //     "Software pipelines and asynchronous copies" (section "Worked example:
@@ -292,7 +292,8 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligne
     }
 
     // DIRECT: every tile class is estimated at the ring depth it would run
-    // with, and the cheapest wins (the larger tile among near-equal ones).
+    // with, and the cheapest wins (for fp16/bf16/int8 the larger tile among
+    // near-equal ones).
     auto same_class = [](const VariantDesc& a, const VariantDesc& b) {
         return a.bm == b.bm && a.bn == b.bn && a.bk == b.bk && a.wgm == b.wgm && a.wgn == b.wgn;
     };
