@@ -50,7 +50,12 @@ def test_skewed_waves_many_runs_bit_exact(producer, stages, tile):
             failures += 1
     torch.cuda.synchronize()
     assert failures == 0, "%d of %d skewed runs differed" % (failures, runs)
-    # the hook really skews: a skewed launch is slower by about nK sleeps
+    # the hook really skews: each K tile waits at its barrier for the sleeping
+    # wave, less the work the other waves do meanwhile.  The visible delay
+    # depends on that overlap and on the clock (one run measured 18.3 us for
+    # 6 K tiles with a sleep of 2 x 8128 cycles each), so the bar is a quarter
+    # of the nominal sleep time at 2.5 GHz: far above run-to-run noise, far
+    # below the delay.
     def timed(skew):
         C = torch.empty((M, N), dtype=torch.int32, device="cuda")
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -63,4 +68,4 @@ def test_skewed_waves_many_runs_bit_exact(producer, stages, tile):
     base = min(timed(0) for _ in range(3))
     skewed = min(timed(2) for _ in range(3))
     nk = (K + tile[2] - 1) // tile[2]
-    assert skewed - base > 0.5 * nk * 2 * 8128 / 2.5e3, (base, skewed)
+    assert skewed - base > 0.25 * nk * 2 * 8128 / 2.5e3, (base, skewed)
