@@ -3,15 +3,16 @@
 One JSON line on stdout.  A "step" is one call of the whole hot path
 (pgemm_gemm: plan, prologue, pipelined K loop, fused alpha/beta epilogue) on
 the headline workload, fp32 SGEMM M = N = K = 4096, alpha = 1, beta = 0.5,
-with inputs resident in HBM.  W untimed warm-up steps, then K timed steps
-between HIP events on the stream the kernels are launched on.
+with inputs resident in HBM.  Untimed calls for --settle-ms (clock settling)
+and W untimed warm-up steps, then K timed steps between HIP events on the
+stream the kernels are launched on.
 
 Also reported (same JSON line, key "reports"): int8 / bf16 / fp16 at 4096^3,
 the stage-count sweep (1 vs 2 vs 3-4 stages) and producer comparison, and
 the bf16 K-sweep with the ragged 4000 x 3968 x 4001 shape.  The oracle is
 timed on a bounded sample of the headline workload on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 40] [--quick] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 40] [--settle-ms 300] [--quick] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -44,7 +45,14 @@ WORKLOADS = {
     "ragged": dict(name="bf16 GEMM M=4000 N=3968 K=4001 lda=4001 ldb=ldc=3968 fp32 out", dtype="bf16", M=4000,
                    N=3968, K=4001, lda=4001, ldb=3968, ldc=3968, alpha=1.0, beta=0.0, seed="bf16_k_sweep", seed_variant=9,
                    data="seeded normal(0,1) rounded to bf16"),
+    "f32_256": dict(name="fp32 SGEMM M=N=K=256 alpha=1 beta=0", dtype="f32", M=256, N=256, K=256, alpha=1.0,
+                    beta=0.0, seed="fp32_256", data="seeded uniform[-1,1) fp32"),
 }
+K_SWEEP = (32, 64, 256, 1024, 4096, 16384)
+for _k in K_SWEEP:
+    WORKLOADS["bf16_k%d" % _k] = dict(name="bf16 GEMM M=N=4096 K=%d fp32 out" % _k, dtype="bf16", M=4096, N=4096, K=_k,
+                                      alpha=1.0, beta=0.0, seed="bf16_k_sweep", seed_variant=_k % 97,
+                                      data="seeded normal(0,1) rounded to bf16")
 
 
 def _code_only(text: str) -> str:
@@ -77,6 +85,27 @@ def make_device_operands(dtype, M, N, K, seed, alpha, beta, lda=None, ldb=None, 
     from software_pipelined_tiled_loop_amd import inputs
     op = inputs.make_operands(dtype, M, N, K, seed=seed, alpha=alpha, beta=beta, lda=lda, ldb=ldb, ldc=ldc)
     return op, op.A.cuda(), op.B.cuda(), op.C.cuda()
+
+
+def workload_operands(name):
+    """Seeded host operands of a named workload (the tests build the same ones)."""
+    from software_pipelined_tiled_loop_amd import inputs
+    w = WORKLOADS[name]
+    return inputs.make_operands(w["dtype"], w["M"], w["N"], w["K"],
+                                seed=inputs.seed_for(w["seed"], w.get("seed_variant", 0)), alpha=w["alpha"],
+                                beta=w["beta"], lda=w.get("lda"), ldb=w.get("ldb"), ldc=w.get("ldc"))
+
+
+def is_aligned(name):
+    """The pgemm_aligned class of a workload: which operands meet the 16-byte
+    vector rules (device tensors start 256-byte aligned, so only the leading
+    dimension and the row length matter): 1 both, 2 A only, 3 B only, 0 none."""
+    from software_pipelined_tiled_loop_amd import inputs
+    w = WORKLOADS[name]
+    K, N, es = w["K"], w["N"], inputs.ELEM_BYTES[w["dtype"]]
+    a = K == 0 or (w.get("lda", K) * es % 16 == 0 and K * es % 16 == 0)
+    b = K == 0 or (w.get("ldb", N) * es % 16 == 0 and N * es % 16 == 0)
+    return 1 if a and b else 2 if a else 3 if b else 0
 
 
 WARMUP_MS = 150.0
@@ -203,6 +232,8 @@ def main():
     ap.add_argument("--stages", type=int, default=0, help="ring depth (0 = planner)")
     ap.add_argument("--producer", default=None, choices=[None, "direct", "register", "generic"])
     ap.add_argument("--tile", default=None, help="BMxBNxBK, e.g. 256x256x32")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed calls before the warm-up, for this long, so the clock has settled (0 = off)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (scales HBM counters)")
     args = ap.parse_args()
@@ -226,7 +257,7 @@ def main():
     dt, M, N, K, alpha, beta = w["dtype"], w["M"], w["N"], w["K"], w["alpha"], w["beta"]
     tile = tuple(int(x) for x in args.tile.split("x")) if args.tile else None
     lda, ldb, ldc = w.get("lda", K), w.get("ldb", N), w.get("ldc", N)
-    aligned = int(all(x * inputs.ELEM_BYTES[dt] % 16 == 0 for x in (lda, ldb, K, N)))
+    aligned = is_aligned(args.workload)
     op, A, B, C = make_device_operands(dt, M, N, K, inputs.seed_for(w["seed"], w.get("seed_variant", 0)), alpha, beta,
                                        lda, ldb, ldc)
     plan = plan_of(lib, dt, M, N, K, args.stages, args.producer, tile, aligned=aligned)
@@ -254,6 +285,19 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # Clock settling before the W warm-up steps: from an idle GPU the shader
+    # clock needs on the order of 100 ms of load to reach its steady value
+    # (the first dispatches of the headline kernel ran 15-20 % long), so a
+    # short warm-up would leave the ramp inside the timed window.  These calls
+    # are untimed, like the warm-up; the timed region holds exactly K steps.
+    settle_calls = 0
+    if args.settle_ms > 0:
+        t_end = time.perf_counter() + args.settle_ms / 1e3
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                step()
+            settle_calls += 8
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -289,7 +333,8 @@ def main():
         "dtype": dt, "data": "synthetic (%s)" % w["data"],
         "config": {"workload": w["name"], "M": M, "N": N, "K": K,
                    "pct_of_peak": round(100.0 * value / PEAK[dt], 2), "plan": plan,
-                   "wall_s_timed_region": round(t_wall, 4), "kernel_source_hash": src_hash},
+                   "wall_s_timed_region": round(t_wall, 4), "clock_settle_calls": settle_calls,
+                   "kernel_source_hash": src_hash},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline and args.workload == "f32":
@@ -303,48 +348,66 @@ def plan_label(p):
     return "%dx%dx%d s%d %s" % (p["tile_m"], p["tile_n"], p["tile_k"], p["stages"], p["producer"])
 
 
-def variant_sweep(lib, op, A, B, C, M, N, K, reps=None):
-    """Every compiled vector-producer variant of the dtype on this problem."""
-    out = {}
-    for i in range(lib.pgemm_num_variants()):
-        v = lib.pgemm_variant_info(i)
-        if v["dtype"] != op.dtype or v["producer"] == "generic":
-            continue
-        tile = (v["tile_m"], v["tile_n"], v["tile_k"])
-        ms = time_gemm(lib, op, A, B, C, stages=v["stages"], producer=v["producer"], tile=tile, reps=reps)
-        out[plan_label(v)] = round(tflops(M, N, K, ms), 1)
-    return out
+def report_points(lib):
+    """Every GEMM launch the report times, as dicts with the report section,
+    the point's label, the workload it runs on and the launch options.  The
+    full-size parity tests walk this same list, so every timed variant is also
+    compared with the oracle on its full output.
 
-
-def vendor_call(torch, dt, A, B, C, op):
-    """The same product through the vendor library behind torch (hipBLASLt /
-    rocBLAS), for context only: fp32 as C = alpha*A*B + beta*C in place;
-    int8 through torch._int_mm (int32 out, beta = 0); fp16/bf16 through
-    torch.mm, whose output is in the input type (half the C bytes of the
-    fp32 output here)."""
-    if dt == "f32":
-        return lambda: C.addmm_(A, B, beta=op.beta, alpha=op.alpha)
-    if dt == "i8":
-        return lambda: torch._int_mm(A, B)
-    return lambda: torch.mm(A, B)
+      * i8_4096, bf16_4096, f16_4096: the planner's plan and every compiled
+        vector-producer variant (tile x depth x producer);
+      * f32_4096_page_tile: the pages' 128 x 64 x 16 tile at 1 and 2 stages
+        and the planner's plan on the headline workload;
+      * f32_256_pages_tile: the same tile at 1 and 2 stages on fp32 256^3;
+      * bf16_k_sweep: per K, the planner's plan at each ring depth 1..4 and
+        with the depth left to it; then the ragged shape."""
+    pts = []
+    for sec, name in (("i8_4096", "i8"), ("bf16_4096", "bf16"), ("f16_4096", "f16")):
+        dt = WORKLOADS[name]["dtype"]
+        pts.append(dict(section=sec, key="auto", workload=name, stages=0, producer=None, tile=None))
+        for i in range(lib.pgemm_num_variants()):
+            v = lib.pgemm_variant_info(i)
+            if v["dtype"] != dt or v["producer"] == "generic":
+                continue
+            pts.append(dict(section=sec, key=plan_label(v), workload=name, stages=v["stages"],
+                            producer=v["producer"], tile=(v["tile_m"], v["tile_n"], v["tile_k"])))
+    for s in (1, 2):
+        pts.append(dict(section="f32_4096_page_tile", key="128x64x16 s%d direct" % s, workload="f32", stages=s,
+                        producer="direct", tile=(128, 64, 16)))
+    pts.append(dict(section="f32_4096_page_tile", key="auto", workload="f32", stages=0, producer=None, tile=None))
+    for s in (1, 2):
+        pts.append(dict(section="f32_256_pages_tile", key="128x64x16 s%d direct" % s, workload="f32_256", stages=s,
+                        producer="direct", tile=(128, 64, 16)))
+    for K in K_SWEEP:
+        for s in (1, 2, 3, 4):
+            pts.append(dict(section="bf16_k_sweep", key="K%d s%d" % (K, s), workload="bf16_k%d" % K, stages=s,
+                            producer=None, tile=None))
+        pts.append(dict(section="bf16_k_sweep", key="K%d auto" % K, workload="bf16_k%d" % K, stages=0,
+                        producer=None, tile=None))
+    pts.append(dict(section="bf16_k_sweep", key="ragged auto", workload="ragged", stages=0, producer=None, tile=None))
+    return pts
 
 
 def pages_context(rep):
     """The pages' own figures, measured on other hardware (context only),
-    beside the same ratios measured here.  The first page's two SGEMM
-    kernels (its 128 x 64 x 16 tile, 1 and 2 stages) as a share of the vendor
-    library on its unnamed NVIDIA GPU; the German page's gain from
+    beside the same ratios measured here: the first page's gain from its
+    2-stage SGEMM over its 1-stage one (kernel 11 over kernel 10 on its
+    128 x 64 x 16 tile, 4.660 -> 4.281 ms on its unnamed NVIDIA GPU, where the
+    two ran at 81.9 % and 89.2 % of the vendor library), against the same
+    tile class at 2 stages over 1 here; and the German page's gain from
     asynchronous-copy pipelining on a 4096^3 int8 GEMM on GA104, against the
     int8 256 x 256 x 128 tile here at 2 stages over 1."""
     f = rep["f32_4096_page_tile"]
     v8 = rep["i8_4096"]["variants"]
     s1, s2 = v8.get("256x256x128 s1 direct"), v8.get("256x256x128 s2 direct")
+    f1, f2 = f.get("128x64x16 s1 direct"), f.get("128x64x16 s2 direct")
     return {
-        "sgemm_pct_of_vendor_blas": {
-            "pages": {"1 stage": 81.9, "2 stages": 89.2, "hardware": "first page's NVIDIA GPU (model not named)"},
-            "here": {"128x64x16 s1": round(100 * f["128x64x16 s1 direct"] / f["vendor_blas"], 1),
-                     "128x64x16 s2": round(100 * f["128x64x16 s2 direct"] / f["vendor_blas"], 1),
-                     "planner": round(100 * f["auto"] / f["vendor_blas"], 1), "hardware": "MI355X"}},
+        "sgemm_2stage_gain_pct": {
+            "pages": {"kernel 11 over kernel 10": round(100 * (4.660 / 4.281 - 1), 1),
+                      "share of vendor library": {"1 stage": 81.9, "2 stages": 89.2},
+                      "hardware": "first page's NVIDIA GPU (model not named)"},
+            "here": {"128x64x16 s2 over s1": round(100 * (f2 / f1 - 1), 1) if f1 and f2 else None,
+                     "hardware": "MI355X"}},
         "int8_4096_pipelining_gain_pct": {
             "pages": {"async-copy pipeline over none": 35, "hardware": "GA104"},
             "here": {"256x256x128 s2 over s1": round(100 * (s2 / s1 - 1), 1) if s1 and s2 else None,
@@ -352,90 +415,81 @@ def pages_context(rep):
     }
 
 
+def _graph_us(lib, torch, op, A, B, C, p):
+    """Per-call time of 50 calls replayed from a HIP graph (launch overhead
+    out of the way on the small, launch-bound problem)."""
+    opts = lib._opts(p["producer"], p["tile"])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(50):
+            lib.pgemm_gemm_ex(op.M, op.N, op.K, op.alpha, A, op.lda, B, op.ldb, op.beta, C, op.ldc, op.dtype,
+                              p["stages"], opts, None)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        g.replay()
+    e1.record()
+    e1.synchronize()
+    del g
+    return e0.elapsed_time(e1) / 250 * 1e3
+
+
 def run_reports(lib, torch):
-    from software_pipelined_tiled_loop_amd import inputs
+    pts = report_points(lib)
     rep = {}
-    M = N = K = 4096
-    for dt, seed, alpha, beta in (("i8", inputs.seed_for("int8_4096"), 1, 0), ("bf16", inputs.seed_for("half_4096"), 1.0, 0.0),
-                                  ("f16", inputs.seed_for("half_4096", 1), 1.0, 0.0)):
-        op, A, B, C = make_device_operands(dt, M, N, K, seed, alpha, beta)
-        ms = time_gemm(lib, op, A, B, C)
-        auto = tflops(M, N, K, ms)
-        rep["%s_4096" % dt] = {"auto": round(auto, 1), "pct_peak": round(100 * auto / PEAK[dt], 2),
-                               "plan": plan_label(plan_of(lib, dt, M, N, K)),
-                               "variants": variant_sweep(lib, op, A, B, C, M, N, K),
-                               "vendor_blas": round(tflops(M, N, K, time_calls(vendor_call(torch, dt, A, B, C, op))), 1)}
-        del A, B, C
+    ops = {}
 
-    # fp32 256^3 (alpha=1, beta=0): single vs double buffer on the pages' tile; launch-bound,
-    # so also timed as replays of a HIP graph of 50 calls
-    op, A, B, C = make_device_operands("f32", 256, 256, 256, inputs.seed_for("fp32_256"), 1.0, 0.0)
-    small = {}
-    for s in (1, 2):
-        eager_ms = time_gemm(lib, op, A, B, C, stages=s, tile=(128, 64, 16), reps=50)
-        opts = lib._opts(None, (128, 64, 16))
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(50):
-                lib.pgemm_gemm_ex(256, 256, 256, 1.0, A, 256, B, 256, 0.0, C, 256, "f32", s, opts, None)
-        for _ in range(3):
-            g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(5):
-            g.replay()
-        e1.record()
-        e1.synchronize()
-        graph_ms = e0.elapsed_time(e1) / 250
-        small["128x64x16 s%d direct" % s] = {"eager_us": round(eager_ms * 1e3, 2), "graph_us": round(graph_ms * 1e3, 2),
-                                             "tflops_graph": round(tflops(256, 256, 256, graph_ms), 2)}
-        del g
-    rep["f32_256_pages_tile"] = small
-    del A, B, C
+    def operands(name):
+        if name not in ops:
+            ops.clear()  # one workload resident at a time
+            op = workload_operands(name)
+            ops[name] = (op, op.A.cuda(), op.B.cuda(), op.C.cuda())
+        return ops[name]
 
-    # fp32: the pages' tile class, 1 vs 2 stages, and the planner's choice
-    op, A, B, C = make_device_operands("f32", M, N, K, inputs.seed_for("fp32_4096"), 1.0, 0.5)
-    d = {}
-    for s in (1, 2):
-        ms = time_gemm(lib, op, A, B, C, stages=s, tile=(128, 64, 16))
-        d["128x64x16 s%d direct" % s] = round(tflops(M, N, K, ms), 2)
-    d["compute_load_ratio"] = round(lib.pgemm_model_compute_load_ratio(128, 64, 16, 4), 2)
-    d["auto"] = round(tflops(M, N, K, time_gemm(lib, op, A, B, C)), 2)
-    d["vendor_blas"] = round(tflops(M, N, K, time_calls(vendor_call(torch, "f32", A, B, C, op))), 2)
-    rep["f32_4096_page_tile"] = d
-    del A, B, C
+    for p in pts:
+        op, A, B, C = operands(p["workload"])
+        M, N, K = op.M, op.N, op.K
+        if p["section"] == "f32_256_pages_tile":
+            ms = time_gemm(lib, op, A, B, C, stages=p["stages"], producer=p["producer"], tile=p["tile"], reps=50)
+            rep.setdefault(p["section"], {})[p["key"]] = {
+                "eager_us": round(ms * 1e3, 2), "graph_us": round(_graph_us(lib, torch, op, A, B, C, p), 2)}
+            continue
+        ms = time_gemm(lib, op, A, B, C, stages=p["stages"], producer=p["producer"], tile=p["tile"])
+        t = round(tflops(M, N, K, ms), 2)
+        aligned = is_aligned(p["workload"])
+        plan = plan_of(lib, op.dtype, M, N, K, p["stages"], p["producer"], p["tile"], aligned=aligned)
+        if p["section"] in ("i8_4096", "bf16_4096", "f16_4096"):
+            d = rep.setdefault(p["section"], {"variants": {}})
+            if p["key"] == "auto":
+                d.update(auto=t, pct_peak=round(100 * t / PEAK[op.dtype], 2), plan=plan_label(plan))
+            else:
+                d["variants"][p["key"]] = t
+        elif p["section"] == "f32_4096_page_tile":
+            rep.setdefault(p["section"], {"compute_load_ratio": round(
+                lib.pgemm_model_compute_load_ratio(128, 64, 16, 4), 2)})[p["key"]] = t
+        else:  # bf16_k_sweep
+            sweep = rep.setdefault("bf16_k_sweep", {})
+            if p["workload"] == "ragged":
+                sweep["ragged_4000x3968x4001"] = {"tflops": t, "pct_peak": round(100 * t / PEAK["bf16"], 2),
+                                                  "plan": plan_label(plan)}
+                continue
+            row = sweep.setdefault("K%d" % K, {})
+            tag = p["key"].split()[1]
+            row[tag] = {"tflops": t, "plan": plan_label(plan)}
+            if tag == "auto":
+                byts = algorithmic_bytes("bf16", M, N, K, 0.0)
+                roof = min(PEAK["bf16"], 2.0 * M * N * K / byts * HBM_PEAK_GBS / 1e3)
+                row["auto"].update(pct_of_roof=round(100 * t / roof, 1), roof="hbm" if roof < PEAK["bf16"] else "mfma",
+                                   GBs=round(byts / (ms * 1e-3) / 1e9, 0))
+                best = max(("s1", "s2", "s3", "s4"), key=lambda k: row[k]["tflops"])
+                row["best_measured"] = {"stages": best, "plan": row[best]["plan"], "tflops": row[best]["tflops"],
+                                        "auto_vs_best": round(t / row[best]["tflops"], 3)}
+    ops.clear()
     rep["pages_context"] = pages_context(rep)
-
-    # bf16 K-sweep by ring depth (the planner picks the tile for each depth) + ragged
-    sweep = {}
-    for Ks in (32, 64, 256, 1024, 4096, 16384):
-        op, A, B, C = make_device_operands("bf16", M, N, Ks, inputs.seed_for("bf16_k_sweep", Ks % 97), 1.0, 0.0)
-        row = {}
-        for s in (1, 2, 3, 4):
-            p = plan_of(lib, "bf16", M, N, Ks, stages=s)
-            ms = time_gemm(lib, op, A, B, C, stages=s)
-            row["s%d" % s] = {"tflops": round(tflops(M, N, Ks, ms), 1), "plan": plan_label(p)}
-        ms = time_gemm(lib, op, A, B, C)
-        byts = algorithmic_bytes("bf16", M, N, Ks, 0.0)
-        roof = min(PEAK["bf16"], 2.0 * M * N * Ks / byts * HBM_PEAK_GBS / 1e3)
-        row["auto"] = {"tflops": round(tflops(M, N, Ks, ms), 1), "plan": plan_label(plan_of(lib, "bf16", M, N, Ks)),
-                       "pct_of_roof": round(100 * tflops(M, N, Ks, ms) / roof, 1),
-                       "roof": "hbm" if roof < PEAK["bf16"] else "mfma",
-                       "GBs": round(byts / (ms * 1e-3) / 1e9, 0)}
-        best = max(("s1", "s2", "s3", "s4"), key=lambda k: row[k]["tflops"])
-        row["best_measured"] = {"stages": best, "plan": row[best]["plan"], "tflops": row[best]["tflops"],
-                                "auto_vs_best": round(row["auto"]["tflops"] / row[best]["tflops"], 3)}
-        sweep["K%d" % Ks] = row
-        del A, B, C
-    r = inputs.RAGGED
-    op, A, B, C = make_device_operands("bf16", r["M"], r["N"], r["K"], inputs.seed_for("bf16_k_sweep", 9), 1.0, 0.0,
-                                       lda=r["lda"], ldb=r["ldb"], ldc=r["ldc"])
-    ms = time_gemm(lib, op, A, B, C)
-    sweep["ragged_4000x3968x4001"] = {"tflops": round(tflops(r["M"], r["N"], r["K"], ms), 1),
-                                      "plan": plan_label(plan_of(lib, "bf16", r["M"], r["N"], r["K"], aligned=0))}
-    rep["bf16_k_sweep"] = sweep
     return rep
 
 

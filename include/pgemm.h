@@ -28,10 +28,10 @@
  *   - C must not overlap A or B.
  *   - stream: a hipStream_t (NULL = the default stream).  The call only
  *     enqueues work and returns; completion is observed through the stream.
- *   - Misaligned pointers or leading dimensions are not an error: they select
- *     the generic producer (16-byte loads through registers wherever the bytes
- *     lie inside the matrix, element loads at its very end; slower, same
- *     results).
+ *   - Misaligned pointers or leading dimensions are not an error: the
+ *     misaligned operand goes through registers (16-byte loads wherever the
+ *     bytes lie inside the matrix, element loads at its very end; slower, same
+ *     results) and an aligned one keeps the direct copy (pgemm_producer).
  *   - 32-bit tile addressing: M, N, K <= 2^31 - 256, lda * elem * 256, ldb *
  *     elem * 128 and ldc * 4 * 256 below 2^31 bytes; otherwise
  *     PGEMM_ERR_TOO_LARGE.
@@ -54,6 +54,25 @@ enum pgemm_dtype {
     PGEMM_I8 = 3
 };
 
+/* Status codes.  Each error is detected on the host before anything is
+ * enqueued, except PGEMM_ERR_HIP.  Their sources:
+ *   INVALID_ARG, TOO_LARGE -- the indexing of page "Double Buffering:
+ *     Software Pipelining the K-Loop", section "The Kernel" (row-major A, B,
+ *     C addressed by row * leading dimension + column), generalised to
+ *     leading dimensions of at least the row length and bounded by the
+ *     kernels' 32-bit tile offsets;
+ *   UNSUPPORTED_DTYPE -- the data types of page "GPU-Kernel pipelinen",
+ *     section "Eingaben" (FP16, FP32, INT8), with bf16 beside fp16;
+ *   BAD_STAGES, INFEASIBLE_PLAN -- the stage counts and tile shapes of page
+ *     "Software pipelines and asynchronous copies", section "Selecting the
+ *     number of stages" (a ring depth, and a tile, that the LDS and the
+ *     compiled variants can hold);
+ *   NONINTEGRAL_SCALAR -- the int32 epilogue of an int8 GEMM: alpha and beta
+ *     must be integers so that int8 results stay exact (page "GPU-Kernel
+ *     pipelinen", step 5: pipelining changes no arithmetic);
+ *   HIP -- a launch the runtime rejected (page "Software pipelines and
+ *     asynchronous copies", section "Common errors": issuing work is not
+ *     completing it, so only the launch itself can fail here). */
 enum pgemm_status {
     PGEMM_OK = 0,
     PGEMM_ERR_INVALID_ARG = -1,        /* negative size, ld too small, null pointer with work to do */
@@ -76,12 +95,36 @@ enum pgemm_status {
  *               in the last K tile the elements past K are zeroed in
  *               registers and the chunk at the very end of a matrix is loaded
  *               element by element.  Elements read past N reach only output
- *               columns that are never stored. */
+ *               columns that are never stored.
+ *   STAGED_A -- one producer per operand, as the first page's kernel 11 does
+ *   STAGED_B    (one operand copied asynchronously, the other staged through
+ *               registers): STAGED_A moves A as GENERIC and B by LDS-DMA,
+ *               STAGED_B moves A by LDS-DMA and B as GENERIC.  The operand
+ *               that meets the 16-byte rules keeps the direct copy while the
+ *               other, misaligned one goes through registers.  Two LDS stages.
+ *
+ * The 16-byte rules, per operand (K == 0 meets both):
+ *   A: A 16-byte aligned, lda * elem and K * elem multiples of 16 bytes;
+ *   B: B 16-byte aligned, ldb * elem and N * elem multiples of 16 bytes.
+ * DIRECT and REGISTER need both, STAGED_A needs B's, STAGED_B needs A's,
+ * GENERIC needs neither.  The planner (stages = 0, producer AUTO) picks
+ * DIRECT when both hold and otherwise the fastest admissible variant by its
+ * measured efficiencies. */
 enum pgemm_producer {
     PGEMM_PRODUCER_AUTO = 0,
     PGEMM_PRODUCER_DIRECT = 1,
     PGEMM_PRODUCER_REGISTER = 2,
-    PGEMM_PRODUCER_GENERIC = 3
+    PGEMM_PRODUCER_GENERIC = 3,
+    PGEMM_PRODUCER_STAGED_A = 4,
+    PGEMM_PRODUCER_STAGED_B = 5
+};
+
+/* Which operands meet the 16-byte rules above (pgemm_plan's `aligned`). */
+enum pgemm_aligned {
+    PGEMM_ALIGNED_NONE = 0,
+    PGEMM_ALIGNED_BOTH = 1,
+    PGEMM_ALIGNED_A = 2,  /* A only */
+    PGEMM_ALIGNED_B = 3   /* B only */
 };
 
 /* Optional overrides for pgemm_gemm_ex / pgemm_plan.  Zero-initialise and set
@@ -120,29 +163,57 @@ typedef struct pgemm_plan_info {
 } pgemm_plan_info;
 
 /* C = alpha*A*B + beta*C with the planner's choices (stages = 0: auto, 1..4:
- * ring depth).  Asynchronous on `stream`. */
+ * ring depth).  The operation is the one defined at the top of this file
+ * (page "Double Buffering: Software Pipelining the K-Loop", section "The
+ * Kernel").  Asynchronous on `stream`: the call returns once the kernel is
+ * enqueued, and C is complete only when the stream has reached that point
+ * (page "Software pipelines and asynchronous copies", section "Common
+ * errors": an issued operation is not a completed one; synchronise on the
+ * stream or record an event before reading C).  A, B and C are device
+ * memory owned by the caller; the library keeps no pointer after the call
+ * returns.  Returns PGEMM_OK or a pgemm_status error; on error nothing has
+ * been enqueued unless the status is PGEMM_ERR_HIP. */
 int pgemm_gemm(int64_t M, int64_t N, int64_t K, double alpha,
                const void* A, int64_t lda, const void* B, int64_t ldb,
                double beta, void* C, int64_t ldc,
                int dtype, int stages, void* stream);
 
-/* As pgemm_gemm, with producer/tile overrides (opts may be NULL). */
+/* As pgemm_gemm, with producer, tile, wave-layout and persistent-launch
+ * overrides (opts may be NULL; see pgemm_opts).  The producer choice is the
+ * one of page "Double Buffering: Software Pipelining the K-Loop", section
+ * "Two Stages, One Barrier" (an operand copied straight into shared memory
+ * asynchronously, or staged through registers) and page "GPU-Kernel
+ * pipelinen", step 2 (the LDG-register and asynchronous-copy variants).
+ * Asynchronous exactly as pgemm_gemm.  An override no compiled variant
+ * satisfies returns PGEMM_ERR_INFEASIBLE_PLAN before anything is enqueued. */
 int pgemm_gemm_ex(int64_t M, int64_t N, int64_t K, double alpha,
                   const void* A, int64_t lda, const void* B, int64_t ldb,
                   double beta, void* C, int64_t ldc,
                   int dtype, int stages, const pgemm_opts* opts, void* stream);
 
-/* Host-only: the plan pgemm_gemm_ex would use for these sizes.  `aligned`
- * states whether A, B, lda, ldb, K, N meet the 16-byte vector-load rules
- * (1) or not (0).  Touches no GPU state. */
+/* Host-only: the plan pgemm_gemm_ex would use for these sizes (page
+ * "Software pipelines and asynchronous copies", sections "Selecting the
+ * number of stages" and "Worked example: Choosing between two and four
+ * stages": the ring depth balances the latency one K tile's arithmetic
+ * covers against shared-memory use and resident workgroups, and is clipped
+ * to the number of K tiles).  `aligned` (a pgemm_aligned value) says which
+ * operands meet the 16-byte rules of pgemm_producer; any other value returns
+ * PGEMM_ERR_INVALID_ARG.  Writes *out and touches no GPU state.
+ * Returns PGEMM_OK or the error pgemm_gemm_ex would return for the same
+ * sizes and options. */
 int pgemm_plan(int64_t M, int64_t N, int64_t K, int dtype, int stages,
                int aligned, const pgemm_opts* opts, pgemm_plan_info* out);
 
-/* Static description of a pgemm_status value. */
+/* Static description of a pgemm_status value (the sources of each code are
+ * listed at enum pgemm_status); "unknown status" for any other value.  The
+ * string is owned by the library and never freed. */
 const char* pgemm_strerror(int status);
 
 /* Number of compiled kernel variants and their static description
- * (host-only; for sweeps and tests). */
+ * (host-only; for sweeps and tests): the instantiation table the re-run tile
+ * and depth search of page "Double Buffering: Software Pipelining the
+ * K-Loop", section "What Could Be Improved", walks.  pgemm_variant_info
+ * returns PGEMM_ERR_INVALID_ARG for an index outside 0..num-1. */
 int pgemm_num_variants(void);
 int pgemm_variant_info(int index, pgemm_plan_info* out, int* dtype);
 
@@ -218,7 +289,8 @@ int pgemm_hazard_copy_reduce(const int32_t* X, int64_t rows, int64_t cols, int64
                              int32_t* row_sums, int reuse_wait, int delay_wave, int delay_cycles,
                              int64_t* trace, int64_t trace_len, int trace_wg, void* stream);
 
-/* ABI version: major*10000 + minor*100 + patch. */
+/* ABI version: major*10000 + minor*100 + patch (a library convention, not
+ * from the pages). */
 int pgemm_version(void);
 
 #ifdef __cplusplus

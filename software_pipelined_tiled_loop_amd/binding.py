@@ -36,7 +36,9 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 PGEMM_F32, PGEMM_F16, PGEMM_BF16, PGEMM_I8 = 0, 1, 2, 3
 DTYPE_CODE = {"f32": PGEMM_F32, "f16": PGEMM_F16, "bf16": PGEMM_BF16, "i8": PGEMM_I8}
-PRODUCER = {"auto": 0, "direct": 1, "register": 2, "generic": 3}
+PRODUCER = {"auto": 0, "direct": 1, "register": 2, "generic": 3, "staged_a": 4, "staged_b": 5}
+# pgemm_aligned: which operands meet the 16-byte rules
+ALIGNED_NONE, ALIGNED_BOTH, ALIGNED_A, ALIGNED_B = 0, 1, 2, 3
 PRODUCER_NAME = {v: k for k, v in PRODUCER.items()}
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED_DTYPE", -3: "BAD_STAGES", -4: "INFEASIBLE_PLAN",
           -5: "NONINTEGRAL_SCALAR", -6: "HIP", -7: "TOO_LARGE"}
@@ -200,16 +202,34 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, stages=0, producer=None, tile=None, M=Non
     """C = alpha*A@B + beta*C on torch tensors (2-D, row-major, unit column stride).
 
     dtype is taken from A: float32 -> f32, float16 -> f16, bfloat16 -> bf16, int8 -> i8.
-    Sizes default to the logical shapes; leading dimensions are the row strides.
+    B must have A's dtype; C is float32 (int32 for int8).  Sizes default to the
+    logical shapes and must fit inside the tensors; leading dimensions are the
+    row strides.  All three tensors must live on one GPU.  Every check runs
+    before anything reaches the library, so a bad call raises ValueError and
+    launches nothing.
     """
     import torch
-    dt = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8"}[A.dtype]
+    in_dt = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8"}
+    if A.dtype not in in_dt:
+        raise ValueError("A has unsupported dtype %s" % A.dtype)
+    dt = in_dt[A.dtype]
+    out_dt = torch.int32 if dt == "i8" else torch.float32
+    if B.dtype != A.dtype:
+        raise ValueError("B must have A's dtype %s, got %s" % (A.dtype, B.dtype))
+    if C.dtype != out_dt:
+        raise ValueError("C must be %s for %s inputs, got %s" % (out_dt, A.dtype, C.dtype))
     for name, t in (("A", A), ("B", B), ("C", C)):
         if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
             raise ValueError("%s must be a 2-D row-major tensor with unit column stride" % name)
     M = A.shape[0] if M is None else M
     K = A.shape[1] if K is None else K
     N = B.shape[1] if N is None else N
+    for name, t, rows, cols in (("A", A, M, K), ("B", B, K, N), ("C", C, M, N)):
+        if rows < 0 or cols < 0 or (rows and cols and (t.shape[0] < rows or t.shape[1] < cols)):
+            raise ValueError("%s is %s, the call needs %d x %d" % (name, tuple(t.shape), rows, cols))
+    devs = {t.device for t in (A, B, C)}
+    if len(devs) != 1 or next(iter(devs)).type != "cuda":
+        raise ValueError("A, B and C must be GPU tensors on one device, got %s" % sorted(str(d) for d in devs))
     r = pgemm_gemm_ex(M, N, K, alpha, A, max(A.stride(0), 1), B, max(B.stride(0), 1), beta, C,
                       max(C.stride(0), 1), dt, stages, _opts(producer, tile), stream)
     if r != 0:

@@ -1,4 +1,4 @@
-"""Build the HIP library libpgemm.so (gfx950) and the oracle's C library.
+"""Build the HIP library libpgemm.so (gfx950).
 
 ``build_library()`` compiles every translation unit under ``csrc/`` with hipcc
 for gfx950 in parallel and links them into ``libpgemm.so`` next to this file.
@@ -73,15 +73,5 @@ def build_library(jobs: int | None = None, verbose: bool = True) -> str:
     return LIB_PATH
 
 
-def build_oracle() -> str:
-    import importlib
-    import sys
-    if ROOT not in sys.path:
-        sys.path.insert(0, ROOT)
-    oracle = importlib.import_module("oracle")
-    return oracle.build()
-
-
 if __name__ == "__main__":
     build_library()
-    print("built", build_oracle())

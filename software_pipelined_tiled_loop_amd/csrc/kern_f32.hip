@@ -18,6 +18,9 @@ static const VariantDesc k_table[] = {
     V(128, 128, 32, 3, 2, 2, PROD_GENERIC),   V(128, 128, 32, 4, 2, 2, PROD_GENERIC),
     V(128, 64, 16, 1, 2, 2, PROD_GENERIC),    V(128, 64, 16, 2, 2, 2, PROD_GENERIC),
     V(256, 256, 32, 1, 2, 4, PROD_GENERIC),   V(256, 256, 32, 2, 2, 4, PROD_GENERIC),
+    // one producer per operand: the misaligned operand through registers, the other by LDS-DMA
+    V(128, 64, 16, 2, 2, 2, PROD_STAGED_A),   V(128, 64, 16, 2, 2, 2, PROD_STAGED_B),
+    V(256, 256, 32, 2, 2, 4, PROD_STAGED_A),  V(256, 256, 32, 2, 2, 4, PROD_STAGED_B),
 };
 #undef V
 

@@ -1,8 +1,11 @@
 // pgemm_abi.cpp -- the C ABI: argument validation, the planner and the launch.
 //
 // The planner picks (tile, stages, producer) for a problem:
-//   * producer: DIRECT whenever the 16-byte vector rules hold, GENERIC
-//     otherwise (REGISTER only on request);
+//   * producer: DIRECT whenever both operands meet the 16-byte vector rules;
+//     otherwise the register-staged variants the alignment admits (GENERIC,
+//     and STAGED_A / STAGED_B when B / A alone keeps the rules), chosen with
+//     tile and depth by their measured efficiencies (REGISTER only on
+//     request);
 //   * tile: the compiled tile class with the smallest estimated time of the
 //     busiest CU (its tiles in rounds of co-resident workgroups, a partial
 //     last round at its measured cost, a prologue per round), each class
@@ -207,6 +210,11 @@ double staged_efficiency(const VariantDesc& d) {
         {PGEMM_I8, 256, 256, 64, 1, PROD_REGISTER, 0.326},   {PGEMM_I8, 256, 256, 64, 2, PROD_REGISTER, 0.341},
         {PGEMM_I8, 256, 256, 64, 3, PROD_REGISTER, 0.338},   {PGEMM_I8, 256, 256, 64, 4, PROD_REGISTER, 0.346},
         {PGEMM_F32, 128, 64, 16, 1, PROD_REGISTER, 0.858},   {PGEMM_F32, 128, 64, 16, 2, PROD_REGISTER, 0.787},
+        {PGEMM_BF16, 256, 256, 32, 2, PROD_STAGED_A, 0.470}, {PGEMM_BF16, 256, 256, 32, 2, PROD_STAGED_B, 0.470},
+        {PGEMM_F16, 256, 256, 32, 2, PROD_STAGED_A, 0.450},  {PGEMM_F16, 256, 256, 32, 2, PROD_STAGED_B, 0.450},
+        {PGEMM_I8, 256, 256, 64, 2, PROD_STAGED_A, 0.420},   {PGEMM_I8, 256, 256, 64, 2, PROD_STAGED_B, 0.420},
+        {PGEMM_F32, 128, 64, 16, 2, PROD_STAGED_A, 0.900},   {PGEMM_F32, 128, 64, 16, 2, PROD_STAGED_B, 0.900},
+        {PGEMM_F32, 256, 256, 32, 2, PROD_STAGED_A, 0.900},  {PGEMM_F32, 256, 256, 32, 2, PROD_STAGED_B, 0.900},
     };
     for (const E& x : table)
         if (x.dt == d.dtype && x.bm == d.bm && x.bn == d.bn && x.bk == d.bk && x.s == d.stages && x.p == d.producer)
@@ -241,6 +249,22 @@ int launch_grid(int64_t M, int64_t N, const VariantDesc& d, const pgemm_opts* op
 
 bool producer_matches(const VariantDesc& d, int want) { return d.producer == want; }
 
+// Whether a producer can run on operands of the given pgemm_aligned class:
+// LDS-DMA and the REGISTER producer's unchecked 16-byte loads need the
+// 16-byte rules for every operand they move.
+bool admissible(int producer, int aligned) {
+    const bool a = aligned == PGEMM_ALIGNED_BOTH || aligned == PGEMM_ALIGNED_A;
+    const bool b = aligned == PGEMM_ALIGNED_BOTH || aligned == PGEMM_ALIGNED_B;
+    switch (producer) {
+        case PROD_DIRECT:
+        case PROD_REGISTER: return a && b;
+        case PROD_STAGED_A: return b;
+        case PROD_STAGED_B: return a;
+        case PROD_GENERIC: return true;
+        default: return false;
+    }
+}
+
 struct Choice {
     int index = -1;
     int stages_req = 0;
@@ -252,11 +276,13 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligne
     Table t = table_for(dtype);
     if (!t.v) return PGEMM_ERR_UNSUPPORTED_DTYPE;
     if (stages < 0 || stages > 4) return PGEMM_ERR_BAD_STAGES;
-    int want_prod = aligned ? PROD_DIRECT : PROD_GENERIC;
+    if (aligned < PGEMM_ALIGNED_NONE || aligned > PGEMM_ALIGNED_B) return PGEMM_ERR_INVALID_ARG;
+    // 0: the planner chooses among the producers the alignment admits
+    int want_prod = aligned == PGEMM_ALIGNED_BOTH ? PROD_DIRECT : 0;
     if (opts && opts->producer != PGEMM_PRODUCER_AUTO) {
-        if (opts->producer < PGEMM_PRODUCER_DIRECT || opts->producer > PGEMM_PRODUCER_GENERIC)
+        if (opts->producer < PGEMM_PRODUCER_DIRECT || opts->producer > PGEMM_PRODUCER_STAGED_B)
             return PGEMM_ERR_INVALID_ARG;
-        if (!aligned && opts->producer != PGEMM_PRODUCER_GENERIC) return PGEMM_ERR_INFEASIBLE_PLAN;
+        if (!admissible(opts->producer, aligned)) return PGEMM_ERR_INFEASIBLE_PLAN;
         want_prod = opts->producer;
     }
     const bool force_tile = opts && (opts->tile_m || opts->tile_n || opts->tile_k);
@@ -265,15 +291,18 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int dtype, int stages, int aligne
         return PGEMM_ERR_INVALID_ARG;
     const int force_waves = opts ? opts->waves : 0;
 
-    // Register-staged producers: the (tile, depth) pair with the best
-    // estimated time at its measured efficiency; an explicit depth restricts
-    // the choice to variants of that depth.
+    // Register-staged producers: the (producer, tile, depth) with the best
+    // estimated time at its measured efficiency, among the forced producer or
+    // every one the alignment admits; an explicit depth restricts the choice
+    // to variants of that depth.
     if (want_prod != PROD_DIRECT) {
         double best_time = 0.0;
         int best = -1;
         for (int i = 0; i < t.n; ++i) {
             const VariantDesc& d = t.v[i];
-            if (!producer_matches(d, want_prod)) continue;
+            if (want_prod ? !producer_matches(d, want_prod)
+                          : (d.producer == PROD_DIRECT || d.producer == PROD_REGISTER || !admissible(d.producer, aligned)))
+                continue;
             if (force_tile && (d.bm != opts->tile_m || d.bn != opts->tile_n || d.bk != opts->tile_k)) continue;
             if (force_waves && d.wgm * d.wgn != force_waves) continue;
             if (stages != 0 && d.stages != stages) continue;
@@ -496,8 +525,15 @@ int pgemm_gemm_ex(int64_t M, int64_t N, int64_t K, double alpha, const void* A, 
     if (ceil_div(M, 128) * ceil_div(N, 64) > 0x7ffffff0) return PGEMM_ERR_TOO_LARGE;
     // Element alignment is required; 16-byte alignment selects the vector producers.
     if (((uintptr_t)A % es) || ((uintptr_t)B % es) || ((uintptr_t)C % 4)) return PGEMM_ERR_INVALID_ARG;
-    const int aligned = K == 0 || (is_aligned16(A) && is_aligned16(B) && (lda * es) % 16 == 0 &&
-                                   (ldb * es) % 16 == 0 && K % epc == 0 && N % epc == 0);
+    // The 16-byte rules per operand: a chunk of 16 bytes never straddles the
+    // end of A's K columns (A) or of B's N columns (B), and every row starts
+    // 16-byte aligned.
+    const bool a_ok = K == 0 || (is_aligned16(A) && (lda * es) % 16 == 0 && K % epc == 0);
+    const bool b_ok = K == 0 || (is_aligned16(B) && (ldb * es) % 16 == 0 && N % epc == 0);
+    const int aligned = a_ok && b_ok ? PGEMM_ALIGNED_BOTH
+                        : a_ok       ? PGEMM_ALIGNED_A
+                        : b_ok       ? PGEMM_ALIGNED_B
+                                     : PGEMM_ALIGNED_NONE;
 
     Choice c;
     int r = plan_impl(M, N, K, dtype, stages, aligned, opts, c);

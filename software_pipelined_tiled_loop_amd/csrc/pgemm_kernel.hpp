@@ -38,7 +38,12 @@
 //             unaligned addresses; in the last K tile, elements past K zeroed
 //             in registers and element loads for a chunk at the very end of a
 //             matrix.
-// All three write the same LDS bytes for every element inside the matrix and
+//   STAGED_A  one producer per operand: A as GENERIC (any alignment), B by
+//   STAGED_B  LDS-DMA; or A by LDS-DMA, B as GENERIC.  The operand that is a
+//             straight aligned copy goes direct while the other goes through
+//             registers (the split of the first page's kernel 11, which copies
+//             B asynchronously and stages A in registers).  Two-stage ring.
+// All of them write the same LDS bytes for every element inside the matrix and
 // zeros past K and M (the generic producer may leave other values in columns
 // past N, which feed only outputs that are never stored), so the stored result
 // does not depend on the producer or on S.
@@ -66,7 +71,7 @@
 namespace pgemm {
 
 enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3 };
-enum Producer : int { PROD_DIRECT = 1, PROD_REGISTER = 2, PROD_GENERIC = 3 };
+enum Producer : int { PROD_DIRECT = 1, PROD_REGISTER = 2, PROD_GENERIC = 3, PROD_STAGED_A = 4, PROD_STAGED_B = 5 };
 
 struct KernelArgs {
     const void* A;
@@ -263,6 +268,29 @@ struct Cfg {
     // bf16 and int8 2-3 % faster with them spread over all eight than over
     // four.
     static constexpr int DMA_GROUPS = D == DT_F32 ? 4 : 8;
+    // Which operands the LDS-DMA producer moves; the others are staged
+    // through registers.  LDS-DMA pieces q of a K tile are [DMA_P0, DMA_P1):
+    // A's blocks are 0 .. A_INSTR-1, B's A_INSTR .. LPS-1.
+    static constexpr bool A_DMA = P == PROD_DIRECT || P == PROD_STAGED_B;
+    static constexpr bool B_DMA = P == PROD_DIRECT || P == PROD_STAGED_A;
+    static constexpr bool ANY_DMA = A_DMA || B_DMA;
+    static constexpr bool ANY_STAGED = !(A_DMA && B_DMA);
+    static constexpr bool MIXED = ANY_DMA && ANY_STAGED;
+    static constexpr int DMA_P0 = A_DMA ? 0 : A_INSTR;
+    static constexpr int DMA_P1 = B_DMA ? LPS : A_INSTR;
+    static constexpr int STAGED_LOADS = LPS - (DMA_P1 - DMA_P0);  // register loads per thread per K tile
+    // K tiles ahead of the one being multiplied that are loaded: S for the
+    // LDS-DMA pieces, one more for register-staged operands, which hold a
+    // K tile in registers before it is written to its stage.
+    static constexpr int LA_DMA = S;
+    static constexpr int LA_REG = S + 1;
+    // MFMA groups of a K step (mfma_step), and the first group after the
+    // last one that issues LDS-DMA blocks: the register-staged loads of a
+    // one-producer-per-operand ring go there, behind every piece.
+    static constexpr int NGROUPS = FM * FN < 8 ? FM * FN : 8;
+    static constexpr int DMA_NG = DMA_GROUPS < NGROUPS ? DMA_GROUPS : NGROUPS;
+    static constexpr int DMA_PPG = (DMA_P1 - DMA_P0 + DMA_NG - 1) / (DMA_NG > 0 ? DMA_NG : 1);
+    static constexpr int REG_GROUP = MIXED ? (DMA_P1 - DMA_P0 + DMA_PPG - 1) / DMA_PPG : 1;
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be whole 16x16 blocks");
     static_assert(BK % KSTEP == 0, "BK must be a multiple of the MFMA K step");
     static_assert(KC == 4 || KC == 8, "A rows must be 64 or 128 bytes");
@@ -272,6 +300,8 @@ struct Cfg {
     static_assert(LDS_BYTES <= 163840, "LDS ring exceeds 160 KiB");
     static_assert(S >= 1 && S <= 4, "1..4 stages");
     static_assert(LPS * (S > 2 ? S - 2 : 0) <= 63, "vmcnt is a 6-bit counter");
+    static_assert(P >= PROD_DIRECT && P <= PROD_STAGED_B, "unknown producer");
+    static_assert(!MIXED || S == 2, "one producer per operand runs a two-stage ring");
 };
 
 // ---- producers -------------------------------------------------------------
@@ -366,10 +396,10 @@ __device__ __forceinline__ i32x4 load_chunk_any(__amdgpu_buffer_rsrc_t r, uint32
     return load_chunk_elementwise<ES>(r, off, valid);
 }
 
-// GENERIC producer: true when every chunk of the K tile whose remaining
-// extents from the tile origin are k_left and n_left may be read as one whole
-// 16-byte load, so the tile's loads form one straight run with no waits
-// between them.  Chunks start at multiples of EPC, so no A chunk straddles the
+// GENERIC producer (and the staged operand of STAGED_A / STAGED_B): true
+// when every register-staged chunk of the K tile whose remaining extents from
+// the tile origin are k_left and n_left may be read as one whole 16-byte load,
+// so the tile's loads form one straight run with no waits between them.  Chunks start at multiples of EPC, so no A chunk straddles the
 // end of K when the K tile is whole or k_left is a multiple of EPC; likewise
 // for B and N.  A B chunk that does straddle N carries the first elements of
 // B's next row into columns >= N, which feed only outputs that are never
@@ -379,9 +409,9 @@ __device__ __forceinline__ i32x4 load_chunk_any(__amdgpu_buffer_rsrc_t r, uint32
 // tile (k_left <= 0) every chunk is out of range and loads nothing.
 template <class C>
 PGEMM_HD bool whole_loads(int k_left, int n_left, int64_t ldb) {
-    const bool a_whole = k_left >= C::BK || k_left % C::EPC == 0;
-    const bool b_whole = n_left >= C::BN || n_left % C::EPC == 0;
-    return k_left <= 0 || (a_whole && (b_whole || (k_left > C::BK && ldb >= C::EPC)));
+    const bool a_whole = C::A_DMA || k_left >= C::BK || k_left % C::EPC == 0;
+    const bool b_whole = C::B_DMA || n_left >= C::BN || n_left % C::EPC == 0 || (k_left > C::BK && ldb >= C::EPC);
+    return k_left <= 0 || (a_whole && b_whole);
 }
 
 // DIRECT producer state for one K tile: buffer descriptors of the tile's A
@@ -433,34 +463,40 @@ __device__ __forceinline__ void dma_piece(const KernelArgs& g, const DmaTile& d,
     }
 }
 
-// Issue the global loads of K tile `kt`: DIRECT straight into LDS stage
-// `stage`, the other producers into the staging registers.  Lanes whose
-// chunk lies outside the matrix get offset 2^31 and receive zeros.
+// LDS-DMA pieces of K tile `kt` for the operands the DMA producer moves,
+// straight into LDS stage `stage`.  Lanes whose chunk lies outside the matrix
+// get offset 2^31 and receive zeros.  FULL as for dma_piece.
+template <class C, bool FULL = false>
+__device__ __forceinline__ void issue_dma(const KernelArgs& g, int m0, int n0, int kt, char PGEMM_LDS* stage,
+                                          int wave, int lane) {
+    const DmaTile d = dma_setup<C>(g, m0, n0, kt, stage, wave);
+#pragma unroll
+    for (int q = C::DMA_P0; q < C::DMA_P1; ++q) dma_piece<C, FULL>(g, d, q, wave, lane);
+}
+
+// Global loads of K tile `kt` for the register-staged operands, into the
+// staging registers.  Lanes whose chunk lies outside the matrix load zeros.
 template <class C>
-__device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, int kt, char PGEMM_LDS* stage,
-                                           Staging<C>& st, int wave, int lane) {
+__device__ __forceinline__ void issue_regs(const KernelArgs& g, int m0, int n0, int kt, Staging<C>& st, int wave,
+                                           int lane) {
     constexpr int ES = C::ES;
     const int k0 = kt * C::BK;
     // Tile-local bases keep every byte offset below 2^31.
     const char* a_base = (const char*)g.A + ((int64_t)m0 * g.lda + k0) * ES;
     const char* b_base = (const char*)g.B + ((int64_t)k0 * g.ldb + n0) * ES;
     const int rows_left = g.M - m0, k_left = g.K - k0, n_left = g.N - n0;
-    if constexpr (C::P == PROD_DIRECT) {
-        const DmaTile d = dma_setup<C>(g, m0, n0, kt, stage, wave);
-#pragma unroll
-        for (int q = 0; q < C::LPS; ++q) dma_piece<C>(g, d, q, wave, lane);
-    } else {
-        // With a ring (S >= 2) the chunk offsets are recomputed from an opaque
-        // copy of the lane id at every issue: hoisted out of the K loop they
-        // would hold a dozen registers for the whole loop next to the doubled
-        // fragment set and, at the register limit, spill.
-        if constexpr (C::S > 1) {
-            __builtin_amdgcn_sched_barrier(0);
-            asm volatile("" : "+v"(lane));
-        }
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base);
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base);
-        if (C::P == PROD_REGISTER || whole_loads<C>(k_left, n_left, g.ldb)) {
+    // With a ring (S >= 2) the chunk offsets are recomputed from an opaque
+    // copy of the lane id at every issue: hoisted out of the K loop they
+    // would hold a dozen registers for the whole loop next to the doubled
+    // fragment set and, at the register limit, spill.
+    if constexpr (C::S > 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" : "+v"(lane));
+    }
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base);
+    if (C::P == PROD_REGISTER || whole_loads<C>(k_left, n_left, g.ldb)) {
+        if constexpr (!C::A_DMA) {
 #pragma unroll
             for (int q = 0; q < C::A_INSTR; ++q) {
                 int row, kel;
@@ -469,6 +505,8 @@ __device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, 
                 st.a[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? (uint32_t)(row * (int)g.lda + kel) * ES : OOB,
                                                                 0, 0);
             }
+        }
+        if constexpr (!C::B_DMA) {
 #pragma unroll
             for (int q = 0; q < C::B_INSTR; ++q) {
                 int krow, nel;
@@ -477,7 +515,9 @@ __device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, 
                 st.b[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? (uint32_t)(krow * (int)g.ldb + nel) * ES : OOB,
                                                                 0, 0);
             }
-        } else {
+        }
+    } else {
+        if constexpr (!C::A_DMA) {
 #pragma unroll
             for (int q = 0; q < C::A_INSTR; ++q) {
                 int row, kel;
@@ -487,6 +527,8 @@ __device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, 
                 const bool vec_ok = chunk_fits(row, kel, g.lda, rows_left, k_left, C::EPC);
                 st.a[q] = load_chunk_any<ES>(ra, off, ok ? min(C::EPC, k_left - kel) : 0, vec_ok);
             }
+        }
+        if constexpr (!C::B_DMA) {
 #pragma unroll
             for (int q = 0; q < C::B_INSTR; ++q) {
                 int krow, nel;
@@ -500,16 +542,33 @@ __device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, 
     }
 }
 
-// Register producers: write the staged chunks to the same LDS bytes the
-// direct producer fills.
+// Register-staged operands: write the staged chunks to the same LDS bytes
+// the direct producer fills.
 template <class C>
 __device__ __forceinline__ void store_tile(char PGEMM_LDS* stage, const Staging<C>& st, int wave, int lane) {
+    if constexpr (!C::A_DMA) {
 #pragma unroll
-    for (int q = 0; q < C::A_INSTR; ++q)
-        *(i32x4 PGEMM_LDS*)(stage + (wave * C::A_INSTR + q) * 1024 + lane * 16) = st.a[q];
+        for (int q = 0; q < C::A_INSTR; ++q)
+            *(i32x4 PGEMM_LDS*)(stage + (wave * C::A_INSTR + q) * 1024 + lane * 16) = st.a[q];
+    }
+    if constexpr (!C::B_DMA) {
 #pragma unroll
-    for (int q = 0; q < C::B_INSTR; ++q)
-        *(i32x4 PGEMM_LDS*)(stage + C::A_BYTES + (wave * C::B_INSTR + q) * 1024 + lane * 16) = st.b[q];
+        for (int q = 0; q < C::B_INSTR; ++q)
+            *(i32x4 PGEMM_LDS*)(stage + C::A_BYTES + (wave * C::B_INSTR + q) * 1024 + lane * 16) = st.b[q];
+    }
+}
+
+// All loads of K tile `kt` that go to stage `stage` now: every operand for
+// DIRECT, the register loads for REGISTER / GENERIC (written to the stage
+// later by store_tile).  Used by the single-buffer loop.
+template <class C>
+__device__ __forceinline__ void issue_tile(const KernelArgs& g, int m0, int n0, int kt, char PGEMM_LDS* stage,
+                                           Staging<C>& st, int wave, int lane) {
+    static_assert(!C::MIXED, "the one-producer-per-operand ring issues its two parts separately");
+    if constexpr (C::ANY_DMA)
+        issue_dma<C>(g, m0, n0, kt, stage, wave, lane);
+    else
+        issue_regs<C>(g, m0, n0, kt, st, wave, lane);
 }
 
 // ---- consumer: MFMA fragments from one LDS stage ------------------------------
@@ -653,27 +712,34 @@ __device__ __forceinline__ void mfma_all(typename C::T::Acc (&acc)[C::FM][C::FN]
 // blocks of the tile being issued); after every group: a share of the next
 // step's fragment reads, so none of that issue time leaves the matrix pipe
 // idle.  sched_barrier keeps the groups in this order.
-template <class C, bool READS, bool DMA, bool FULL = false>
+struct NoHook {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+
+// `hook(gi)` runs after the MFMAs of group gi, before its DMA blocks: the
+// register-staged producers put their stage writes and next loads there.
+template <class C, bool READS, bool DMA, bool FULL = false, class Hook = NoHook>
 __device__ __forceinline__ void mfma_step(typename C::T::Acc (&acc)[C::FM][C::FN], const Frags<C>& use,
                                           Frags<C>& nxt, const char PGEMM_LDS* rstage, int rks,
                                           const KernelArgs& g, const DmaTile& d, int wave, int lane, int wm0,
-                                          int wn0) {
+                                          int wn0, Hook hook = Hook{}) {
     constexpr int NMF = C::FM * C::FN;
     constexpr int NG = NMF < 8 ? NMF : 8;
     constexpr int GS = NMF / NG;
     constexpr int NR = C::FM + C::FN;
     constexpr int RPG = (NR + NG - 1) / NG;
-    constexpr int NP = C::LPS;
+    constexpr int NP = C::DMA_P1 - C::DMA_P0;
     constexpr int DG = C::DMA_GROUPS < NG ? C::DMA_GROUPS : NG;
     constexpr int PPG = (NP + DG - 1) / DG;  // DMA blocks per group, in the first DG groups
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
 #pragma unroll
         for (int m = gi * GS; m < (gi + 1) * GS; ++m) mfma_block<C>(acc[m / C::FN][m % C::FN], use.a[m / C::FN], use.b[m % C::FN]);
+        hook(gi);
         if constexpr (DMA) {
 #pragma unroll
             for (int p = gi * PPG; p < (gi + 1) * PPG; ++p)
-                if (p < NP) dma_piece<C, FULL>(g, d, p, wave, lane);
+                if (p < NP) dma_piece<C, FULL>(g, d, C::DMA_P0 + p, wave, lane);
         }
         if constexpr (READS) {
 #pragma unroll
@@ -687,10 +753,19 @@ __device__ __forceinline__ void mfma_step(typename C::T::Acc (&acc)[C::FM][C::FN
 // Barrier of the uniform pipelined loop: every K-tile slot issues exactly
 // LPS loads (real, or all-out-of-range for slots past nK), so when tile t+1
 // must have landed the loads of the S-2 later slots may still be in flight.
+// Register producers wait for their loads where the registers are written to
+// LDS (the compiler's own vmcnt, after the barrier: each wave waits for its
+// own loads only, not for the slowest wave's), so their barrier needs only
+// lgkmcnt.  With one producer per operand (two stages) each slot issues its
+// LDS-DMA pieces and then the register loads of the slot after it, so when
+// slot t+1's pieces must have landed only those register loads may still be
+// in flight: vmcnt(STAGED_LOADS), and they are waited for after the barrier.
 template <class C>
 __device__ __forceinline__ void sync_ring() {
     if constexpr (C::P == PROD_DIRECT) {
         wait_barrier<C::LPS * (C::S - 2)>();
+    } else if constexpr (C::MIXED) {
+        wait_barrier<C::STAGED_LOADS>();
     } else {
         lgkm_barrier();
     }
@@ -776,12 +851,13 @@ __device__ __forceinline__ Cursor cursor_at(const KernelArgs& g, const WgTiles& 
 // MFMAs.  The body is the same for every slot: slots past the workgroup's
 // last K tile load nothing (every lane out of range, zeros land in a stage
 // nobody reads), so the loop has no drain branches and the wait count is a
-// constant.  `lc` is the slot to load (DIRECT: s+S; register producers:
-// s+S+1, one more being in flight in registers).  PAR is the fragment buffer
-// holding step 0 of this slot.
+// constant.  `dc` is the slot whose LDS-DMA pieces are issued now (s+S), `rc`
+// the slot loaded into registers now (s+S+1: the registers hold one more K
+// tile, slot s+S, which is written to the freed stage right after the
+// barrier).  PAR is the fragment buffer holding step 0 of this slot.
 template <class C, int PAR, bool FULL = false>
-__device__ __forceinline__ void tile_body(const KernelArgs& g, const Cursor& lc, int s, char PGEMM_LDS* smem, int& cur,
-                                          Staging<C>& st, Frags<C> (&f)[2],
+__device__ __forceinline__ void tile_body(const KernelArgs& g, const Cursor& dc, const Cursor& rc, int s,
+                                          char PGEMM_LDS* smem, int& cur, Staging<C>& st, Frags<C> (&f)[2],
                                           typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane, int wm0,
                                           int wn0) {
     constexpr int NKS = C::BK / C::KSTEP;
@@ -799,13 +875,22 @@ __device__ __forceinline__ void tile_body(const KernelArgs& g, const Cursor& lc,
             debug_skew(g, s, wave, C::NW);
             const char PGEMM_LDS* rstage = smem + nstage * C::STAGE_BYTES;
             char PGEMM_LDS* freed = smem + cur * C::STAGE_BYTES;
-            if constexpr (C::P == PROD_DIRECT) {
-                const DmaTile d = dma_setup<C>(g, lc.m0, lc.n0, lc.kt, freed, wave);  // slot s+S (maybe none)
-                mfma_step<C, true, true, FULL>(acc, use, nxt, rstage, 0, g, d, wave, lane, wm0, wn0);
+            if constexpr (C::ANY_STAGED) {
+                // Spread over the MFMA groups: after group 0 the staged
+                // operand of slot s+S (in registers since B_s) is written to
+                // the freed stage, then the LDS-DMA pieces of slot s+S (if
+                // any) follow in the first groups, and after group REG_GROUP
+                // the register loads of slot s+S+1 -- behind every piece, so
+                // the next barrier waits for the pieces only.
+                const DmaTile d = C::ANY_DMA ? dma_setup<C>(g, dc.m0, dc.n0, dc.kt, freed, wave) : none;
+                auto staged = [&](int gi) {
+                    if (gi == 0) store_tile<C>(freed, st, wave, lane);
+                    if (gi == C::REG_GROUP) issue_regs<C>(g, rc.m0, rc.n0, rc.kt, st, wave, lane);
+                };
+                mfma_step<C, true, C::ANY_DMA, FULL>(acc, use, nxt, rstage, 0, g, d, wave, lane, wm0, wn0, staged);
             } else {
-                store_tile<C>(freed, st, wave, lane);                          // slot s+S, loaded since B_s
-                issue_tile<C>(g, lc.m0, lc.n0, lc.kt, freed, st, wave, lane);  // slot s+S+1 into registers
-                mfma_step<C, true, false>(acc, use, nxt, rstage, 0, g, none, wave, lane, wm0, wn0);
+                const DmaTile d = dma_setup<C>(g, dc.m0, dc.n0, dc.kt, freed, wave);  // slot s+S (maybe none)
+                mfma_step<C, true, true, FULL>(acc, use, nxt, rstage, 0, g, d, wave, lane, wm0, wn0);
             }
         }
     }
@@ -825,56 +910,64 @@ __device__ __forceinline__ void store_c(const KernelArgs& g, int m0, int n0, int
                                         typename C::T::Acc (&acc)[C::FM][C::FN]);
 
 // The S >= 2 pipeline of one output tile: prologue, steady state, drain.
-// The slot to load is LA K tiles ahead (S for DIRECT, S+1 for the register
-// producers); past the last K tile that lies beyond K, so every lane is out
-// of range and the slot loads nothing.
+// The slots to load are LA_DMA = S K tiles ahead for LDS-DMA pieces and
+// LA_REG = S+1 for register-staged operands; past the last K tile those lie
+// beyond K, so every lane is out of range and the slot loads nothing.
 template <class C>
 __device__ __forceinline__ void pertile_loop(const KernelArgs& g, int m0, int n0, int nK, char PGEMM_LDS* smem,
                                              typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane, int wm0,
                                              int wn0) {
     constexpr int NKS = C::BK / C::KSTEP;
-    constexpr int LA = C::P == PROD_DIRECT ? C::S : C::S + 1;
+    constexpr int LD = C::LA_DMA, LR = C::LA_REG;
     Staging<C> st;
     Frags<C> f[2];
     // Prologue: K tiles 0 .. S-2 into stages 0 .. S-2.
 #pragma unroll
     for (int p = 0; p < C::S - 1; ++p) {
-        issue_tile<C>(g, m0, n0, p, smem + p * C::STAGE_BYTES, st, wave, lane);
-        if constexpr (C::P != PROD_DIRECT) store_tile<C>(smem + p * C::STAGE_BYTES, st, wave, lane);
+        if constexpr (C::ANY_STAGED) issue_regs<C>(g, m0, n0, p, st, wave, lane);
+        if constexpr (C::ANY_DMA) issue_dma<C>(g, m0, n0, p, smem + p * C::STAGE_BYTES, wave, lane);
+        if constexpr (C::ANY_STAGED) store_tile<C>(smem + p * C::STAGE_BYTES, st, wave, lane);
     }
-    if constexpr (C::P != PROD_DIRECT) issue_tile<C>(g, m0, n0, C::S - 1, smem, st, wave, lane);
+    if constexpr (C::ANY_STAGED) issue_regs<C>(g, m0, n0, C::S - 1, st, wave, lane);
     sync_ring<C>();  // B_0
-    // Stage S-1 has never been used: K tile S-1 goes there now.
-    if constexpr (C::P == PROD_DIRECT) {
-        issue_tile<C>(g, m0, n0, C::S - 1, smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
-    } else {
-        store_tile<C>(smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
-        issue_tile<C>(g, m0, n0, C::S, smem, st, wave, lane);
-    }
+    // Stage S-1 has never been used: K tile S-1 goes there now (the staged
+    // operand from registers, then the LDS-DMA pieces), then K tile S into
+    // registers -- the order of every slot of the loop.
+    if constexpr (C::ANY_STAGED) store_tile<C>(smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
+    if constexpr (C::ANY_DMA) issue_dma<C>(g, m0, n0, C::S - 1, smem + (C::S - 1) * C::STAGE_BYTES, wave, lane);
+    if constexpr (C::ANY_STAGED) issue_regs<C>(g, m0, n0, C::S, st, wave, lane);
     read_frags<C>(smem, 0, wm0, wn0, lane, f[0]);
     int cur = 0;
-    // Slots t < nfull load a whole K tile of a whole output tile (the
-    // DIRECT producer then issues its loads without per-lane range selects);
-    // the rest, up to LA + 1 of them, take the general path.
-    const bool whole_mn = C::P == PROD_DIRECT && m0 + C::BM <= g.M && n0 + C::BN <= g.N;
-    const int nfull = whole_mn && g.K / C::BK > LA ? g.K / C::BK - LA : 0;
+    // Slots t < nfull load a whole K tile of a whole output tile by LDS-DMA
+    // (issued without per-lane range selects); the rest, up to LD + 1 of
+    // them, take the general path.
+    const bool whole = C::ANY_DMA && (!C::A_DMA || m0 + C::BM <= g.M) && (!C::B_DMA || n0 + C::BN <= g.N);
+    const int nfull = whole && g.K / C::BK > LD ? g.K / C::BK - LD : 0;
     if constexpr (NKS % 2 == 0) {
         int t = 0;
         for (; t < nfull; ++t)
-            tile_body<C, 0, true>(g, Cursor{t + LA, m0, n0}, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+            tile_body<C, 0, true>(g, Cursor{t + LD, m0, n0}, Cursor{t + LR, m0, n0}, t, smem, cur, st, f, acc, wave,
+                                  lane, wm0, wn0);
         for (; t < nK; ++t)
-            tile_body<C, 0>(g, Cursor{t + LA, m0, n0}, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+            tile_body<C, 0>(g, Cursor{t + LD, m0, n0}, Cursor{t + LR, m0, n0}, t, smem, cur, st, f, acc, wave, lane,
+                            wm0, wn0);
     } else {
         int t = 0;
         for (; t + 1 < nfull; t += 2) {
-            tile_body<C, 0, true>(g, Cursor{t + LA, m0, n0}, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
-            tile_body<C, 1, true>(g, Cursor{t + 1 + LA, m0, n0}, t + 1, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+            tile_body<C, 0, true>(g, Cursor{t + LD, m0, n0}, Cursor{t + LR, m0, n0}, t, smem, cur, st, f, acc, wave,
+                                  lane, wm0, wn0);
+            tile_body<C, 1, true>(g, Cursor{t + 1 + LD, m0, n0}, Cursor{t + 1 + LR, m0, n0}, t + 1, smem, cur, st, f,
+                                  acc, wave, lane, wm0, wn0);
         }
         for (; t + 1 < nK; t += 2) {
-            tile_body<C, 0>(g, Cursor{t + LA, m0, n0}, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
-            tile_body<C, 1>(g, Cursor{t + 1 + LA, m0, n0}, t + 1, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+            tile_body<C, 0>(g, Cursor{t + LD, m0, n0}, Cursor{t + LR, m0, n0}, t, smem, cur, st, f, acc, wave, lane,
+                            wm0, wn0);
+            tile_body<C, 1>(g, Cursor{t + 1 + LD, m0, n0}, Cursor{t + 1 + LR, m0, n0}, t + 1, smem, cur, st, f, acc,
+                            wave, lane, wm0, wn0);
         }
-        if (t < nK) tile_body<C, 0>(g, Cursor{t + LA, m0, n0}, t, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+        if (t < nK)
+            tile_body<C, 0>(g, Cursor{t + LD, m0, n0}, Cursor{t + LR, m0, n0}, t, smem, cur, st, f, acc, wave, lane,
+                            wm0, wn0);
     }
     // No load may still be writing LDS when the workgroup retires.
     __builtin_amdgcn_s_waitcnt(0);
@@ -885,39 +978,43 @@ __device__ __forceinline__ void pertile_loop(const KernelArgs& g, int m0, int n0
 // per-tile pipeline; with several, tile j+1's first K tiles load while tile
 // j's last ones are multiplied and stored.
 //
-// Each output tile's K loop has two phases.  In phase A the slot to load
-// (LA slots ahead: S for DIRECT, S+1 for the register producers, which hold
-// one more in registers) lies in the same output tile, so its cursor is
-// plain arithmetic: this is the hot loop.  Phase B covers the last LA slots,
-// whose loads belong to later tiles.
+// Each output tile's K loop has two phases.  In phase A every slot to load
+// (LA_DMA and LA_REG slots ahead) lies in the same output tile, so its
+// cursor is plain arithmetic: this is the hot loop.  Phase B covers the last
+// LA slots, whose loads belong to later tiles.
 template <class C>
 __device__ __forceinline__ void stream_loop(const KernelArgs& g, const WgTiles& w, int nK, char PGEMM_LDS* smem,
                                             typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane, int wm0,
                                             int wn0) {
     constexpr int NKS = C::BK / C::KSTEP;
-    constexpr int LA = C::P == PROD_DIRECT ? C::S : C::S + 1;
+    constexpr int LD = C::LA_DMA, LR = C::LA_REG;
+    constexpr int LA = C::ANY_STAGED ? LR : LD;
     Staging<C> st;
     Frags<C> f[2];
     // Prologue: slots 0 .. S-2 into stages 0 .. S-2.
 #pragma unroll
     for (int p = 0; p < C::S - 1; ++p) {
         const Cursor c = cursor_at<C>(g, w, nK, p);
-        issue_tile<C>(g, c.m0, c.n0, c.kt, smem + p * C::STAGE_BYTES, st, wave, lane);
-        if constexpr (C::P != PROD_DIRECT) store_tile<C>(smem + p * C::STAGE_BYTES, st, wave, lane);
+        if constexpr (C::ANY_STAGED) issue_regs<C>(g, c.m0, c.n0, c.kt, st, wave, lane);
+        if constexpr (C::ANY_DMA) issue_dma<C>(g, c.m0, c.n0, c.kt, smem + p * C::STAGE_BYTES, wave, lane);
+        if constexpr (C::ANY_STAGED) store_tile<C>(smem + p * C::STAGE_BYTES, st, wave, lane);
     }
-    if constexpr (C::P != PROD_DIRECT) {
+    if constexpr (C::ANY_STAGED) {
         const Cursor c = cursor_at<C>(g, w, nK, C::S - 1);
-        issue_tile<C>(g, c.m0, c.n0, c.kt, smem, st, wave, lane);  // slot S-1 into registers
+        issue_regs<C>(g, c.m0, c.n0, c.kt, st, wave, lane);  // slot S-1 into registers
     }
     sync_ring<C>();  // B_0
-    // Stage S-1 has never been used: slot S-1 goes there now.
-    if constexpr (C::P == PROD_DIRECT) {
+    // Stage S-1 has never been used: slot S-1 goes there now (the staged
+    // operand from registers, then the LDS-DMA pieces), then slot S into
+    // registers -- the order of every slot of the loop.
+    if constexpr (C::ANY_STAGED) store_tile<C>(smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
+    if constexpr (C::ANY_DMA) {
         const Cursor c = cursor_at<C>(g, w, nK, C::S - 1);
-        issue_tile<C>(g, c.m0, c.n0, c.kt, smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
-    } else {
+        issue_dma<C>(g, c.m0, c.n0, c.kt, smem + (C::S - 1) * C::STAGE_BYTES, wave, lane);
+    }
+    if constexpr (C::ANY_STAGED) {
         const Cursor c = cursor_at<C>(g, w, nK, C::S);
-        store_tile<C>(smem + (C::S - 1) * C::STAGE_BYTES, st, wave, lane);
-        issue_tile<C>(g, c.m0, c.n0, c.kt, smem, st, wave, lane);  // slot S into registers
+        issue_regs<C>(g, c.m0, c.n0, c.kt, st, wave, lane);  // slot S into registers
     }
     read_frags<C>(smem, 0, wm0, wn0, lane, f[0]);
     int cur = 0;
@@ -928,27 +1025,33 @@ __device__ __forceinline__ void stream_loop(const KernelArgs& g, const WgTiles& 
         int m0, n0;
         wg_tile_origin<C>(g, w, i, m0, n0);
         const int nA = nK > LA ? nK - LA : 0;
+        // phase B cursors: the slot LD (LR) ahead of slot s0 + kt, in whatever
+        // output tile it falls
+        auto dc_at = [&](int kt) { return C::ANY_DMA ? cursor_at<C>(g, w, nK, s0 + kt + LD) : Cursor{0, 0, 0}; };
+        auto rc_at = [&](int kt) { return C::ANY_STAGED ? cursor_at<C>(g, w, nK, s0 + kt + LR) : Cursor{0, 0, 0}; };
         int kt = 0;
         if constexpr (NKS % 2 == 0) {
             for (; kt < nA; ++kt)
-                tile_body<C, 0>(g, Cursor{kt + LA, m0, n0}, s0 + kt, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+                tile_body<C, 0>(g, Cursor{kt + LD, m0, n0}, Cursor{kt + LR, m0, n0}, s0 + kt, smem, cur, st, f, acc,
+                                wave, lane, wm0, wn0);
             for (; kt < nK; ++kt)
-                tile_body<C, 0>(g, cursor_at<C>(g, w, nK, s0 + kt + LA), s0 + kt, smem, cur, st, f, acc, wave, lane,
-                                wm0, wn0);
+                tile_body<C, 0>(g, dc_at(kt), rc_at(kt), s0 + kt, smem, cur, st, f, acc, wave, lane, wm0, wn0);
         } else {
             // Pairs of slots keep the fragment buffers' roles fixed at the
             // back edge of the hot loop (one buffer live between slots).
             for (; kt + 1 < nA; kt += 2) {
-                tile_body<C, 0>(g, Cursor{kt + LA, m0, n0}, s0 + kt, smem, cur, st, f, acc, wave, lane, wm0, wn0);
-                tile_body<C, 1>(g, Cursor{kt + 1 + LA, m0, n0}, s0 + kt + 1, smem, cur, st, f, acc, wave, lane, wm0,
-                                wn0);
+                tile_body<C, 0>(g, Cursor{kt + LD, m0, n0}, Cursor{kt + LR, m0, n0}, s0 + kt, smem, cur, st, f, acc,
+                                wave, lane, wm0, wn0);
+                tile_body<C, 1>(g, Cursor{kt + 1 + LD, m0, n0}, Cursor{kt + 1 + LR, m0, n0}, s0 + kt + 1, smem, cur,
+                                st, f, acc, wave, lane, wm0, wn0);
             }
             // The rest (at most LA + 1 slots): one slot at a time, the look-ahead
             // fragments moved back to buffer 0 after each, so a single buffer
             // is live at every join.
             for (; kt < nK; ++kt) {
-                const Cursor c = kt < nA ? Cursor{kt + LA, m0, n0} : cursor_at<C>(g, w, nK, s0 + kt + LA);
-                tile_body<C, 0>(g, c, s0 + kt, smem, cur, st, f, acc, wave, lane, wm0, wn0);
+                const Cursor dc = kt < nA ? Cursor{kt + LD, m0, n0} : dc_at(kt);
+                const Cursor rc = kt < nA ? Cursor{kt + LR, m0, n0} : rc_at(kt);
+                tile_body<C, 0>(g, dc, rc, s0 + kt, smem, cur, st, f, acc, wave, lane, wm0, wn0);
                 f[0] = f[1];
             }
         }

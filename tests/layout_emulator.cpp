@@ -253,9 +253,12 @@ static int check_whole_loads(const char* name) {
                 if (!whole || k_left <= 0) continue;
                 ++cases;
                 const long b_last = (long)(k_left - 1) * ldb + n_left - 1;
-                for (auto [krow, nel] : bch)
-                    if (krow < k_left && nel < n_left && (long)krow * ldb + nel + EPC - 1 > b_last)
-                        FAIL("B chunk (%d,%d) k_left %d n_left %d ldb %d reads past B", krow, nel, k_left, n_left, ldb);
+                if (!C::B_DMA)  // a B moved by LDS-DMA meets the 16-byte rules: N is whole chunks
+                    for (auto [krow, nel] : bch)
+                        if (krow < k_left && nel < n_left && (long)krow * ldb + nel + EPC - 1 > b_last)
+                            FAIL("B chunk (%d,%d) k_left %d n_left %d ldb %d reads past B", krow, nel, k_left, n_left,
+                                 ldb);
+                if (C::A_DMA) continue;  // likewise an A moved by LDS-DMA: K is whole chunks
                 for (auto [row, kel] : ach)
                     if (kel < k_left && kel + EPC > k_left) FAIL("A chunk (%d,%d) straddles K, k_left %d", row, kel, k_left);
                 if (n_left != ns[0] || ldb != n_left) continue;  // A's reads do not depend on N
@@ -392,6 +395,8 @@ static int check_work_split() {
     do {                                                                           \
         emulate<Cfg<D, BM, BN, BK, 2, WGM, WGN, PROD_DIRECT>>(#D " " #BM "x" #BN "x" #BK); \
         wl += check_whole_loads<Cfg<D, BM, BN, BK, 2, WGM, WGN, PROD_GENERIC>>("whole_loads " #D); \
+        wl += check_whole_loads<Cfg<D, BM, BN, BK, 2, WGM, WGN, PROD_STAGED_A>>("whole_loads staged A " #D); \
+        wl += check_whole_loads<Cfg<D, BM, BN, BK, 2, WGM, WGN, PROD_STAGED_B>>("whole_loads staged B " #D); \
         ++n;                                                                       \
         printf("class %d %d %d %d %d %d\n", D, BM, BN, BK, WGM, WGN);              \
     } while (0)

@@ -186,6 +186,34 @@ def test_torch_wrapper_rejects_tensors_that_are_not_row_major():
         lib.gemm(A, B, C[None])
 
 
+def test_torch_wrapper_validates_before_any_launch():
+    """Each bad call raises ValueError before the library is reached: these
+    tensors are on the CPU, so a call that got through would hand host
+    addresses to a kernel.  The dtype and size checks come first, so each
+    fault is named even with CPU tensors; well-formed CPU tensors then fail
+    the device check."""
+    import torch
+    f32, bf = torch.float32, torch.bfloat16
+    A, B, C = torch.zeros(8, 16, dtype=bf), torch.zeros(16, 12, dtype=bf), torch.zeros(8, 12)
+    bad = [
+        (A, B.to(torch.float16), C),                                # B dtype differs from A
+        (A, B, C.to(bf)),                                           # C not fp32
+        (A.to(torch.int8), B.to(torch.int8), C),                    # int8 needs int32 C
+        (A.to(torch.float64), B.to(torch.float64), C),              # unsupported input dtype
+        (A, B[:12], C),                                             # B has fewer than K rows
+        (A, B, C[:7]),                                              # C has fewer than M rows
+        (A, B, C[:, :11]),                                          # C has fewer than N columns
+        (A, B, C),                                                  # well-formed, but on the CPU
+    ]
+    for args in bad:
+        with pytest.raises(ValueError):
+            lib.gemm(*args)
+    with pytest.raises(ValueError):
+        lib.gemm(A, B, C, M=9)                                      # M beyond A's rows
+    with pytest.raises(ValueError):
+        lib.gemm(A.to(f32), B.to(f32), C, K=17)                     # K beyond A's columns
+
+
 def test_strerror_covers_every_status():
     for code in range(0, -8, -1):
         assert lib.pgemm_strerror(code) != "unknown status"
@@ -237,6 +265,33 @@ def test_planner_honours_explicit_depth(dtype):
     assert r == 0 and p["producer"] == "generic"
     r, _ = lib.pgemm_plan(1024, 1024, 2048, dtype, 0, 1, {"tile": (8, 8, 8)})
     assert r == -4
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_planner_keeps_the_direct_copy_for_the_aligned_operand(dtype):
+    """Per-operand producers: each forced producer is admitted exactly for the
+    alignment classes whose operands it moves by LDS-DMA or unchecked 16-byte
+    loads; with one operand aligned the planner picks among GENERIC and the
+    staged producer that keeps that operand on LDS-DMA; unknown classes are
+    argument errors."""
+    need = {"direct": {lib.ALIGNED_BOTH}, "register": {lib.ALIGNED_BOTH},
+            "staged_a": {lib.ALIGNED_BOTH, lib.ALIGNED_B}, "staged_b": {lib.ALIGNED_BOTH, lib.ALIGNED_A},
+            "generic": {lib.ALIGNED_NONE, lib.ALIGNED_BOTH, lib.ALIGNED_A, lib.ALIGNED_B}}
+    for prod, ok in need.items():
+        for cls in (lib.ALIGNED_NONE, lib.ALIGNED_BOTH, lib.ALIGNED_A, lib.ALIGNED_B):
+            r, p = lib.pgemm_plan(4096, 4096, 4096, dtype, 0, cls, {"producer": prod})
+            assert (r == 0) == (cls in ok), (prod, cls, r)
+            if r == 0:
+                assert p["producer"] == prod
+    for cls, allowed in ((lib.ALIGNED_A, {"generic", "staged_b"}), (lib.ALIGNED_B, {"generic", "staged_a"}),
+                         (lib.ALIGNED_NONE, {"generic"})):
+        r, p = lib.pgemm_plan(4000, 3968, 4001, dtype, 0, cls)
+        assert r == 0 and p["producer"] in allowed, (cls, p)
+    # at the ragged benchmark size the staged producer wins over GENERIC
+    r, p = lib.pgemm_plan(4000, 3968, 4001, dtype, 0, lib.ALIGNED_B)
+    assert p["producer"] == "staged_a"
+    for bad in (-1, 4, 7):
+        assert lib.pgemm_plan(64, 64, 64, dtype, 0, bad)[0] == -1
 
 
 def test_planner_prefers_big_tiles_for_big_problems_and_small_for_small():

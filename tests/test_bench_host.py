@@ -68,28 +68,47 @@ def test_headline_algorithmic_bytes():
 
 
 def test_every_workload_has_a_plan():
-    from software_pipelined_tiled_loop_amd import inputs
     for name, w in bench.WORKLOADS.items():
         dt, M, N, K = w["dtype"], w["M"], w["N"], w["K"]
-        lda, ldb = w.get("lda", K), w.get("ldb", N)
-        aligned = int(all(x * inputs.ELEM_BYTES[dt] % 16 == 0 for x in (lda, ldb, K, N)))
-        assert bench.plan_of(lib, dt, M, N, K, aligned=aligned) is not None, name
+        assert bench.plan_of(lib, dt, M, N, K, aligned=bench.is_aligned(name)) is not None, name
+    # the ragged workload: lda = 4001 breaks A's rules only, so B keeps LDS-DMA
+    assert bench.is_aligned("ragged") == lib.ALIGNED_B
+    p = bench.plan_of(lib, "bf16", 4000, 3968, 4001, aligned=lib.ALIGNED_B)
+    assert p["producer"] == "staged_a"
 
 
 def test_pages_context_ratios():
     """The report's context block: the pages' figures verbatim, and the same
-    ratios from the measured points (vendor share; int8 2-stage gain)."""
-    rep = {"f32_4096_page_tile": {"128x64x16 s1 direct": 120.0, "128x64x16 s2 direct": 135.0, "auto": 145.0,
-                                  "vendor_blas": 150.0},
+    ratios from the measured points (2-stage over 1-stage gains)."""
+    rep = {"f32_4096_page_tile": {"128x64x16 s1 direct": 120.0, "128x64x16 s2 direct": 135.0, "auto": 145.0},
            "i8_4096": {"variants": {"256x256x128 s1 direct": 1500.0, "256x256x128 s2 direct": 2100.0}}}
     c = bench.pages_context(rep)
-    assert c["sgemm_pct_of_vendor_blas"]["pages"]["1 stage"] == 81.9
-    assert c["sgemm_pct_of_vendor_blas"]["pages"]["2 stages"] == 89.2
-    assert c["sgemm_pct_of_vendor_blas"]["here"]["128x64x16 s1"] == 80.0
-    assert c["sgemm_pct_of_vendor_blas"]["here"]["128x64x16 s2"] == 90.0
+    assert c["sgemm_2stage_gain_pct"]["pages"]["kernel 11 over kernel 10"] == 8.9
+    assert c["sgemm_2stage_gain_pct"]["pages"]["share of vendor library"] == {"1 stage": 81.9, "2 stages": 89.2}
+    assert c["sgemm_2stage_gain_pct"]["here"]["128x64x16 s2 over s1"] == 12.5
     assert c["int8_4096_pipelining_gain_pct"]["pages"]["async-copy pipeline over none"] == 35
     assert c["int8_4096_pipelining_gain_pct"]["here"]["256x256x128 s2 over s1"] == 40.0
     # the int8 labels are the ones the variant sweep produces
-    labels = {bench.plan_label(lib.pgemm_variant_info(i)) for i in range(lib.pgemm_num_variants())
-              if lib.pgemm_variant_info(i)["dtype"] == "i8"}
+    labels = {p["key"] for p in bench.report_points(lib) if p["section"] == "i8_4096"}
     assert {"256x256x128 s1 direct", "256x256x128 s2 direct"} <= labels
+
+
+def test_report_points_cover_every_timed_variant():
+    """The report times the planner's plan and every compiled vector-producer
+    variant at 4096^3 for int8, bf16 and fp16, the pages' fp32 tile at 1 and 2
+    stages, and the K-sweep at every depth: the list the full-size parity
+    tests walk holds all of them, each on a workload with a plan."""
+    pts = bench.report_points(lib)
+    for dt, sec in (("i8", "i8_4096"), ("bf16", "bf16_4096"), ("f16", "f16_4096")):
+        want = {bench.plan_label(v) for v in (lib.pgemm_variant_info(i) for i in range(lib.pgemm_num_variants()))
+                if v["dtype"] == dt and v["producer"] != "generic"}
+        assert {p["key"] for p in pts if p["section"] == sec} == want | {"auto"}
+    for K in bench.K_SWEEP:
+        assert {p["key"] for p in pts if p["workload"] == "bf16_k%d" % K} == {"K%d s%d" % (K, s) for s in
+                                                                             (1, 2, 3, 4)} | {"K%d auto" % K}
+    assert any(p["workload"] == "ragged" for p in pts)
+    for p in pts:
+        w = bench.WORKLOADS[p["workload"]]
+        plan = bench.plan_of(lib, w["dtype"], w["M"], w["N"], w["K"], p["stages"], p["producer"], p["tile"],
+                             aligned=bench.is_aligned(p["workload"]))
+        assert plan is not None, p

@@ -249,6 +249,42 @@ def test_row_sampling_equals_full_rows():
     assert np.array_equal(oracle.gemm("i8", 20, 17, 50, 1, A8, B8, rows=[3, 19]), full8[[3, 19]])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+def test_row_sampling_with_beta_reads_the_right_rows_of_C0(dtype):
+    """With beta != 0 each sampled row combines with its own row of C0 (a
+    wrong C0 offset would pair row i with row 0 or with a neighbour): rows
+    picked out of order and in runs are compared with exact rational
+    arithmetic over dyadic (float) or integer inputs, and with the matching
+    rows of the full call."""
+    M, N, K, pad = 23, 9, 13, 2
+    rng = random.Random(4711)
+    if dtype == "i8":
+        Av = [[rng.randint(-128, 127) for _ in range(K)] for _ in range(M)]
+        Bv = [[rng.randint(-128, 127) for _ in range(N)] for _ in range(K)]
+        C0v = [[rng.randint(-1000, 1000) for _ in range(N)] for _ in range(M)]
+        alpha, beta = 3, -2
+        A, B = np.array(Av, np.int8), np.array(Bv, np.int8)
+        C0 = np.full((M, N + pad), 0x7F7F7F7F, np.int32)
+        C0[:, :N] = np.array(C0v, np.int32)
+    else:
+        Av = [[rng.randint(-32, 32) / 8 for _ in range(K)] for _ in range(M)]
+        Bv = [[rng.randint(-32, 32) / 8 for _ in range(N)] for _ in range(K)]
+        C0v = [[rng.randint(-64, 64) / 16 for _ in range(N)] for _ in range(M)]
+        alpha, beta = -0.5, 0.75
+        A, B = encode(dtype, Av), encode(dtype, Bv)
+        C0 = np.full((M, N + pad), np.nan, np.float32)
+        C0[:, :N] = np.array(C0v, np.float32)
+    rows = [22, 0, 1, 2, 9, 15, 16, 5]
+    part = oracle.gemm(dtype, M, N, K, alpha, A, B, beta, C0, rows=rows)
+    ref = exact_gemm(M, N, K, alpha, Av, Bv, beta, C0v)
+    for r, i in enumerate(rows):
+        for j in range(N):
+            want = ref[i][j]
+            assert (int(part[r, j]) == int(want)) if dtype == "i8" else (Fraction(float(part[r, j])) == want), (i, j)
+    full = oracle.gemm(dtype, M, N, K, alpha, A, B, beta, C0)
+    assert np.array_equal(part, full[rows])
+
+
 def test_rejects_bad_arguments():
     a = np.zeros((2, 2), np.float32)
     with pytest.raises(ValueError):
