@@ -438,6 +438,94 @@ def _graph_us(lib, torch, op, A, B, C, p):
     return e0.elapsed_time(e1) / 250 * 1e3
 
 
+CEILING_ITERS = {"f32": 1024, "f16": 8192, "bf16": 8192, "i8": 8192}
+# (workload, tile, stages): the tile classes of the 4096^3 plans, and the bf16
+# 256 x 256 x 32 class at each ring depth
+STREAM_POINTS = (("bf16", (256, 256, 64), 2), ("f16", (256, 256, 64), 2), ("i8", (256, 256, 128), 2),
+                 ("f32", (128, 64, 16), 2), ("f32", (256, 256, 32), 2), ("bf16", (256, 256, 32), 2),
+                 ("bf16", (256, 256, 32), 3), ("bf16", (256, 256, 32), 4))
+
+
+def ceilings(lib, torch):
+    """The two diagnostics that bound the GEMM (pgemm_diag_*): the matrix
+    cores alone on random and on zero operands (% of dense peak), and the
+    producer alone -- the LDS-DMA pieces of a tile class on the 4096^3
+    workload with no arithmetic -- as LDS bytes per second and as the GEMM
+    rate it could feed (2MNK over its time)."""
+    out = {"mfma_only": {}, "lds_stream": {}}
+    grid = 256
+    buf = torch.zeros(grid * 8, dtype=torch.float32, device="cuda")
+    for dt in ("f32", "f16", "bf16", "i8"):
+        row = {}
+        for zero in (0, 1):
+            box = {}
+
+            def call():
+                r, box["flops"] = lib.pgemm_diag_mfma_ceiling(dt, zero, CEILING_ITERS[dt], grid, 12345, buf)
+                if r != 0:
+                    raise lib.PgemmError(r)
+
+            ms = time_calls(call)
+            t = box["flops"] / (ms * 1e-3) / 1e12
+            row["zero" if zero else "random"] = {"tflops": round(t, 1), "pct_peak": round(100 * t / PEAK[dt], 1)}
+        out["mfma_only"][dt] = row
+    for wl, tile, S in STREAM_POINTS:
+        op = workload_operands(wl)
+        A, B = op.A.cuda(), op.B.cuda()
+        box = {}
+
+        def call():
+            r, box["bytes"] = lib.pgemm_diag_lds_stream(op.M, op.N, op.K, A, op.lda, B, op.ldb, op.dtype, tile, S)
+            if r != 0:
+                raise lib.PgemmError(r)
+
+        ms = time_calls(call)
+        t = tflops(op.M, op.N, op.K, ms)
+        out["lds_stream"]["%s %dx%dx%d s%d" % (op.dtype, tile[0], tile[1], tile[2], S)] = {
+            "us": round(ms * 1e3, 2), "TBs": round(box["bytes"] / (ms * 1e-3) / 1e12, 2),
+            "gemm_tflops_fed": round(t, 1), "pct_peak_fed": round(100 * t / PEAK[op.dtype], 1)}
+        del A, B
+    return out
+
+
+# (workload, tile): the planner's 4096^3 classes, profiled at one and two stages
+PROFILE_POINTS = (("bf16", (256, 256, 64)), ("f16", (256, 256, 64)), ("i8", (256, 256, 128)), ("f32", (128, 64, 16)),
+                  ("f32", (256, 256, 32)))
+
+
+def wait_profile(lib, torch, runs=20):
+    """Where the waves of a ready edge wait (pgemm_diag_wait_profile: the
+    GEMM kernel built with clock stamps around its waits), at one and two
+    stages of each 4096^3 class: the share of the K loop's wave-cycles spent
+    in the vmcnt wait for the K tile's loads, and in the workgroup barrier
+    after it.  The last of `runs` back-to-back launches is read (clock
+    settled)."""
+    out = {}
+    for wl, tile in PROFILE_POINTS:
+        op = workload_operands(wl)
+        A, B, C = op.A.cuda(), op.B.cuda(), op.C.cuda()
+        tiles = -(-op.M // tile[0]) * -(-op.N // tile[1])
+        grid = -(-tiles // 8) * 8
+        nw = 8 if tile[0] * tile[1] >= 256 * 256 else 4
+        buf = torch.zeros(grid * nw * 4, dtype=torch.int64, device="cuda")
+        for S in (1, 2):
+            for _ in range(runs):
+                r = lib.pgemm_diag_wait_profile(op.M, op.N, op.K, A, op.lda, B, op.ldb, C, op.ldc, op.dtype, tile, S,
+                                                buf, buf.numel())
+                if r != 0:
+                    raise lib.PgemmError(r)
+            torch.cuda.synchronize()
+            v = buf.view(grid, nw, 4)[:tiles].cpu().double()
+            vm, bar, n, loop = (float(v[..., i].sum()) for i in range(4))
+            out["%s %dx%dx%d s%d" % (op.dtype, tile[0], tile[1], tile[2], S)] = {
+                "vmcnt_wait_share": round(vm / loop, 4), "barrier_wait_share": round(bar / loop, 4),
+                "ready_edges_per_wave": round(n / (tiles * nw), 2),
+                "vmcnt_cycles_per_edge": round(vm / max(n, 1), 1), "barrier_cycles_per_edge": round(bar / max(n, 1), 1),
+                "loop_cycles_per_edge": round(loop / max(n, 1), 1)}
+        del A, B, C, buf
+    return out
+
+
 def run_reports(lib, torch):
     pts = report_points(lib)
     rep = {}
@@ -490,6 +578,8 @@ def run_reports(lib, torch):
                                         "auto_vs_best": round(t / row[best]["tflops"], 3)}
     ops.clear()
     rep["pages_context"] = pages_context(rep)
+    rep["ceilings"] = ceilings(lib, torch)
+    rep["wait_profile"] = wait_profile(lib, torch)
     return rep
 
 

@@ -289,6 +289,62 @@ int pgemm_hazard_copy_reduce(const int32_t* X, int64_t rows, int64_t cols, int64
                              int32_t* row_sums, int reuse_wait, int delay_wave, int delay_cycles,
                              int64_t* trace, int64_t trace_len, int trace_wg, void* stream);
 
+/* Diagnostics that bound the GEMM from above (page "Software pipelines and
+ * asynchronous copies", section "Worked example: Choosing between two and
+ * four stages", last point: a timing difference alone does not show the
+ * cause).  Neither is part of the GEMM path.
+ *
+ * pgemm_diag_mfma_ceiling: the matrix cores alone.  `grid` workgroups of
+ * eight waves (one workgroup per CU, two waves per SIMD) each run `iters`
+ * rounds of 16 independent MFMA blocks of the dtype (bf16/fp16
+ * 16x16x32, int8 16x16x64, fp32 four 16x16x4) on operands drawn from a
+ * hash of `seed` and the lane (random values in [-1, 1), or any int8), or on
+ * zeros when zero_operands = 1.  No memory traffic besides one float per wave
+ * written to out[grid * 8] (device memory owned by the caller, 4-byte
+ * aligned), which keeps the accumulators live.  *flops (optional) receives
+ * the flops of the launch.  Asynchronous on `stream`.  Errors:
+ * UNSUPPORTED_DTYPE; INVALID_ARG for iters outside 0..2^24, grid outside
+ * 1..65536 or a bad `out`; HIP for a rejected launch.
+ *
+ * pgemm_diag_lds_stream: the producer alone.  For the compiled stream of tile
+ * class (tile_m, tile_n, tile_k) at ring depth `stages` it issues exactly the
+ * LDS-DMA pieces the GEMM's DIRECT producer would for C = A*B with these
+ * operands (same workgroup raster, 1-KiB blocks, one ready barrier per K
+ * tile, stages - 1 K tiles in flight) and does no arithmetic.  A and B follow
+ * the GEMM's layout rules and must meet the 16-byte rules for both operands
+ * (pgemm_producer); they are only read.  *lds_bytes (optional) receives the
+ * LDS bytes the launch fills.  Asynchronous on `stream`.  Errors:
+ * UNSUPPORTED_DTYPE; INVALID_ARG (sizes, leading dimensions, alignment);
+ * TOO_LARGE (32-bit tile addressing); INFEASIBLE_PLAN when no stream of that
+ * class and depth is compiled (bf16 256x256x64 S2 and 256x256x32 S2..4,
+ * fp16 256x256x64 S2, int8 256x256x128 S2, fp32 128x64x16 S2 and
+ * 256x256x32 S2); HIP for a rejected launch. */
+/* pgemm_diag_wait_profile: C = A*B (alpha = 1, beta = 0, same layout rules
+ * and results as pgemm_gemm) with a wait-profile build of the DIRECT variant
+ * of tile class (tile_m, tile_n, tile_k) at ring depth `stages`: the same
+ * kernel with shader-clock stamps around the two waits of every ready edge.
+ * For each wave w of each workgroup b that has a tile, out[(b*W + w)*4 + i]
+ * (W = waves per workgroup) receives, in shader clocks: i = 0 the time in the
+ * vmcnt wait (the K tile's loads landing), 1 the time from there through the
+ * workgroup barrier (every other wave arriving; for one stage also the reuse
+ * barrier), 2 the number of ready edges, 3 the whole K loop.  `out` is device
+ * memory owned by the caller, 8-byte aligned, out_len >= grid * W * 4
+ * entries with grid = ceil(tiles / 8) * 8.  Both operands must meet the
+ * 16-byte rules (pgemm_producer).  Asynchronous on `stream`.  Errors:
+ * UNSUPPORTED_DTYPE; INVALID_ARG; TOO_LARGE; INFEASIBLE_PLAN when no profile
+ * build of that class and depth is compiled (bf16 256x256x64 S1/S2,
+ * 256x256x32 S1..S4; fp16 256x256x64 S1/S2; int8 256x256x128 S1/S2; fp32
+ * 128x64x16 S1/S2, 256x256x32 S1/S2); HIP for a rejected launch. */
+int pgemm_diag_wait_profile(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                            const void* B, int64_t ldb, void* C, int64_t ldc, int dtype,
+                            int tile_m, int tile_n, int tile_k, int stages, int64_t* out,
+                            int64_t out_len, void* stream);
+int pgemm_diag_mfma_ceiling(int dtype, int zero_operands, int iters, int grid, uint32_t seed,
+                            float* out, int64_t* flops, void* stream);
+int pgemm_diag_lds_stream(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                          const void* B, int64_t ldb, int dtype, int tile_m, int tile_n,
+                          int tile_k, int stages, int64_t* lds_bytes, void* stream);
+
 /* ABI version: major*10000 + minor*100 + patch (a library convention, not
  * from the pages). */
 int pgemm_version(void);

@@ -85,6 +85,7 @@ struct KernelArgs {
     int ialpha, ibeta;      // int8
     int beta_nonzero;
     int dbg_sleep;          // test hook: wave (t % NW) sleeps dbg_sleep x 8128 cycles per K tile (0 = off)
+    long long* probe;       // wait-profile builds only (ProbeCfg): per-wave clock totals, else unused
 };
 
 // Test hook for stress runs: skew one wave per K tile (rotating) so that the
@@ -301,6 +302,9 @@ struct Cfg {
     static_assert(S >= 1 && S <= 4, "1..4 stages");
     static_assert(LPS * (S > 2 ? S - 2 : 0) <= 63, "vmcnt is a 6-bit counter");
     static_assert(P >= PROD_DIRECT && P <= PROD_STAGED_B, "unknown producer");
+    // Wait-profile builds (ProbeCfg) stamp the shader clock around the waits
+    // of every ready edge; the GEMM's own variants never do.
+    static constexpr bool PROBE = false;
     static_assert(!MIXED || S == 2, "one producer per operand runs a two-stage ring");
 };
 
@@ -324,8 +328,26 @@ PGEMM_HD void b_chunk(int wave, int lane, int q, int& krow, int& nel) {
     nel = (pc ^ b_swz<C::Dt, C::NCH>(krow)) * C::EPC;
 }
 
+// A wait-profile build of tile configuration C: the same kernel, with shader
+// clock stamps around the vmcnt wait and the barrier of each ready edge
+// (sync_ring), summed per wave.
+template <class Base>
+struct ProbeCfg : Base {
+    static constexpr bool PROBE = true;
+};
+
+// Per-wave clock totals of a wait-profile build: cycles spent in the vmcnt
+// wait of the ready edges, cycles from there through the barrier, and the
+// number of ready edges.
+template <bool P>
+struct ProbeSlots {};
+template <>
+struct ProbeSlots<true> {
+    long long vm = 0, bar = 0, n = 0;
+};
+
 template <class C>
-struct Staging {
+struct Staging : ProbeSlots<C::PROBE> {
     i32x4 a[C::A_INSTR];
     i32x4 b[C::B_INSTR];
 };
@@ -760,14 +782,58 @@ __device__ __forceinline__ void mfma_step(typename C::T::Acc (&acc)[C::FM][C::FN
 // LDS-DMA pieces and then the register loads of the slot after it, so when
 // slot t+1's pieces must have landed only those register loads may still be
 // in flight: vmcnt(STAGED_LOADS), and they are waited for after the barrier.
-template <class C>
-__device__ __forceinline__ void sync_ring() {
-    if constexpr (C::P == PROD_DIRECT) {
-        wait_barrier<C::LPS * (C::S - 2)>();
-    } else if constexpr (C::MIXED) {
-        wait_barrier<C::STAGED_LOADS>();
+// A workgroup barrier after s_waitcnt vmcnt(VM) lgkmcnt(0) (VM < 0: lgkmcnt
+// only); in a wait-profile build, with the clock stamps described at
+// ProbeCfg.  READY: the barrier is a ready edge (counted in st.n).
+template <class C, int VM, bool READY = true>
+__device__ __forceinline__ void probed_barrier(Staging<C>& st) {
+    if constexpr (C::PROBE) {
+        // the same waits, split by clock stamps: vmcnt (with lgkmcnt), then
+        // the barrier; each stamp's own latency lands in the second part
+        lgkm_drain();
+        const long long t0 = (long long)__builtin_amdgcn_s_memtime();
+        if constexpr (VM >= 0)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" : : "n"(VM) : "memory");
+        else
+            asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+        const long long t1 = (long long)__builtin_amdgcn_s_memtime();
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+        const long long t2 = (long long)__builtin_amdgcn_s_memtime();
+        st.vm += t1 - t0;
+        st.bar += t2 - t1;
+        st.n += READY ? 1 : 0;
+    } else if constexpr (VM >= 0) {
+        wait_barrier<(VM >= 0 ? VM : 0)>();
     } else {
         lgkm_barrier();
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void sync_ring(Staging<C>& st) {
+    probed_barrier<C, C::P == PROD_DIRECT ? C::LPS * (C::S - 2) : C::MIXED ? C::STAGED_LOADS : -1>(st);
+}
+
+// Start of a K loop, and its end: a wait-profile build writes the wave's
+// totals (vmcnt cycles, barrier cycles, ready edges, cycles of the whole
+// loop) to g.probe[(workgroup * waves + wave) * 4 ...].
+template <class C>
+__device__ __forceinline__ long long probe_start() {
+    if constexpr (C::PROBE) return (long long)__builtin_amdgcn_s_memtime();
+    return 0;
+}
+template <class C>
+__device__ __forceinline__ void probe_end(const KernelArgs& g, const Staging<C>& st, long long t_begin, int wave,
+                                          int lane) {
+    if constexpr (C::PROBE) {
+        const long long t_end = (long long)__builtin_amdgcn_s_memtime();
+        if (lane == 0) {
+            long long* o = g.probe + ((int64_t)blockIdx.x * C::NW + wave) * 4;
+            o[0] = st.vm;
+            o[1] = st.bar;
+            o[2] = st.n;
+            o[3] = t_end - t_begin;
+        }
     }
 }
 
@@ -871,7 +937,7 @@ __device__ __forceinline__ void tile_body(const KernelArgs& g, const Cursor& dc,
         if (ks + 1 < NKS) {
             mfma_step<C, true, false>(acc, use, nxt, cstage, ks + 1, g, none, wave, lane, wm0, wn0);
         } else {
-            sync_ring<C>();  // B_{s+1}: slot s+1 ready, stage of slot s free
+            sync_ring<C>(st);  // B_{s+1}: slot s+1 ready, stage of slot s free
             debug_skew(g, s, wave, C::NW);
             const char PGEMM_LDS* rstage = smem + nstage * C::STAGE_BYTES;
             char PGEMM_LDS* freed = smem + cur * C::STAGE_BYTES;
@@ -921,6 +987,7 @@ __device__ __forceinline__ void pertile_loop(const KernelArgs& g, int m0, int n0
     constexpr int LD = C::LA_DMA, LR = C::LA_REG;
     Staging<C> st;
     Frags<C> f[2];
+    const long long t_begin = probe_start<C>();
     // Prologue: K tiles 0 .. S-2 into stages 0 .. S-2.
 #pragma unroll
     for (int p = 0; p < C::S - 1; ++p) {
@@ -929,7 +996,7 @@ __device__ __forceinline__ void pertile_loop(const KernelArgs& g, int m0, int n0
         if constexpr (C::ANY_STAGED) store_tile<C>(smem + p * C::STAGE_BYTES, st, wave, lane);
     }
     if constexpr (C::ANY_STAGED) issue_regs<C>(g, m0, n0, C::S - 1, st, wave, lane);
-    sync_ring<C>();  // B_0
+    sync_ring<C>(st);  // B_0
     // Stage S-1 has never been used: K tile S-1 goes there now (the staged
     // operand from registers, then the LDS-DMA pieces), then K tile S into
     // registers -- the order of every slot of the loop.
@@ -971,6 +1038,7 @@ __device__ __forceinline__ void pertile_loop(const KernelArgs& g, int m0, int n0
     }
     // No load may still be writing LDS when the workgroup retires.
     __builtin_amdgcn_s_waitcnt(0);
+    probe_end<C>(g, st, t_begin, wave, lane);
 }
 
 // The S >= 2 pipeline over all K-tile slots of the workgroup's tiles: one
@@ -991,6 +1059,7 @@ __device__ __forceinline__ void stream_loop(const KernelArgs& g, const WgTiles& 
     constexpr int LA = C::ANY_STAGED ? LR : LD;
     Staging<C> st;
     Frags<C> f[2];
+    const long long t_begin = probe_start<C>();
     // Prologue: slots 0 .. S-2 into stages 0 .. S-2.
 #pragma unroll
     for (int p = 0; p < C::S - 1; ++p) {
@@ -1003,7 +1072,7 @@ __device__ __forceinline__ void stream_loop(const KernelArgs& g, const WgTiles& 
         const Cursor c = cursor_at<C>(g, w, nK, C::S - 1);
         issue_regs<C>(g, c.m0, c.n0, c.kt, st, wave, lane);  // slot S-1 into registers
     }
-    sync_ring<C>();  // B_0
+    sync_ring<C>(st);  // B_0
     // Stage S-1 has never been used: slot S-1 goes there now (the staged
     // operand from registers, then the LDS-DMA pieces), then slot S into
     // registers -- the order of every slot of the loop.
@@ -1062,6 +1131,7 @@ __device__ __forceinline__ void stream_loop(const KernelArgs& g, const WgTiles& 
     }
     // No load may still be writing LDS when the workgroup retires.
     __builtin_amdgcn_s_waitcnt(0);
+    probe_end<C>(g, st, t_begin, wave, lane);
 }
 
 // MFMA work on one stage with the fragments of step ks+1 read under step ks.
@@ -1088,27 +1158,29 @@ __device__ __forceinline__ void single_buffer_loop(const KernelArgs& g, int m0, 
                                                    typename C::T::Acc (&acc)[C::FM][C::FN], int wave, int lane,
                                                    int wm0, int wn0) {
     Staging<C> st;
+    const long long t_begin = probe_start<C>();
     if constexpr (C::P == PROD_DIRECT) {
         for (int t = 0; t < nK; ++t) {
             issue_tile<C>(g, m0, n0, t, smem, st, wave, lane);
-            wait_barrier<0>();  // ready
+            probed_barrier<C, 0>(st);          // ready
             debug_skew(g, t, wave, C::NW);
             compute_stage<C>(smem, wm0, wn0, lane, acc);
-            lgkm_barrier();     // reuse
+            probed_barrier<C, -1, false>(st);  // reuse
         }
     } else {
         issue_tile<C>(g, m0, n0, 0, smem, st, wave, lane);
         store_tile<C>(smem, st, wave, lane);
         for (int t = 0; t < nK; ++t) {
-            lgkm_barrier();  // ready
+            probed_barrier<C, -1>(st);  // ready
             debug_skew(g, t, wave, C::NW);
             const bool more = t + 1 < nK;
             if (more) issue_tile<C>(g, m0, n0, t + 1, smem, st, wave, lane);
             compute_stage<C>(smem, wm0, wn0, lane, acc);
-            lgkm_barrier();  // reuse
+            probed_barrier<C, -1, false>(st);  // reuse
             if (more) store_tile<C>(smem, st, wave, lane);
         }
     }
+    probe_end<C>(g, st, t_begin, wave, lane);
 }
 
 // ---- epilogue: C = alpha*acc + beta*C (fused, as in the pages' kernel) -------------

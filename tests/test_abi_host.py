@@ -214,6 +214,28 @@ def test_torch_wrapper_validates_before_any_launch():
         lib.gemm(A.to(f32), B.to(f32), C, K=17)                     # K beyond A's columns
 
 
+def test_diagnostics_refuse_bad_arguments_before_any_launch():
+    """The two ceiling diagnostics validate everything on the host: dtype,
+    counts, output buffer, sizes, alignment and the compiled stream classes.
+    The pointers are never dereferenced."""
+    assert lib.pgemm_diag_mfma_ceiling(7, 0, 16, 256, 1, FAKE, stream=0)[0] == -2
+    assert lib.pgemm_diag_mfma_ceiling("bf16", 2, 16, 256, 1, FAKE, stream=0)[0] == -1
+    assert lib.pgemm_diag_mfma_ceiling("bf16", 0, -1, 256, 1, FAKE, stream=0)[0] == -1
+    assert lib.pgemm_diag_mfma_ceiling("bf16", 0, 16, 0, 1, FAKE, stream=0)[0] == -1
+    assert lib.pgemm_diag_mfma_ceiling("bf16", 0, 16, 256, 1, 0, stream=0)[0] == -1
+    assert lib.pgemm_diag_mfma_ceiling("bf16", 0, 16, 256, 1, FAKE + 2, stream=0)[0] == -1
+    ok = dict(M=4096, N=4096, K=4096, A=FAKE, lda=4096, B=FAKE, ldb=4096, dtype="bf16", tile=(256, 256, 64), stages=2)
+
+    def stream(**kw):
+        a = dict(ok, **kw)
+        return lib.pgemm_diag_lds_stream(a["M"], a["N"], a["K"], a["A"], a["lda"], a["B"], a["ldb"], a["dtype"],
+                                         a["tile"], a["stages"], stream=0)[0]
+    assert stream(dtype=9) == -2
+    assert stream(K=0) == -1 and stream(lda=4095) == -1 and stream(A=FAKE + 2) == -1 and stream(N=4092) == -1
+    assert stream(tile=(128, 128, 64)) == -4 and stream(stages=3) == -4
+    assert stream(lda=1 << 24) == -7
+
+
 def test_strerror_covers_every_status():
     for code in range(0, -8, -1):
         assert lib.pgemm_strerror(code) != "unknown status"

@@ -1,0 +1,95 @@
+"""The ceiling diagnostics (pgemm_diag_*) on the GPU: they run, and the MFMA
+kernel's accumulators hold what its operands make them.
+
+These kernels are measurement tools, not part of the GEMM path; the bench's
+"ceilings" report times them.  Zero operands must leave every accumulator at
+zero; random operands give finite sums (bf16/fp16/fp32, values in [-1, 1))
+that differ between seeds.  The LDS stream moves exactly the bytes it reports
+and reads only inside the operands (it runs on the 4096^3 workload and on a
+ragged-free small one)."""
+import math
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from software_pipelined_tiled_loop_amd import binding
+    return binding
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_mfma_ceiling_runs_and_keeps_its_accumulators(lib, dtype):
+    print("[case] mfma ceiling", dtype, flush=True)
+    grid = 256
+    out = torch.full((grid * 8,), float("nan"), dtype=torch.float32, device="cuda")
+    r, flops = lib.pgemm_diag_mfma_ceiling(dtype, 1, 64, grid, 7, out)
+    assert r == 0
+    torch.cuda.synchronize()
+    zeros = bool((out == 0).all().item())
+    assert zeros
+    per_block = {"f32": 8192, "f16": 16384, "bf16": 16384, "i8": 32768}[dtype]
+    assert flops == grid * 8 * 64 * 16 * per_block
+    sums = []
+    for seed in (7, 8):
+        r, _ = lib.pgemm_diag_mfma_ceiling(dtype, 0, 64, grid, seed, out)
+        assert r == 0
+        torch.cuda.synchronize()
+        sums.append(out.cpu())
+    assert bool(torch.isfinite(sums[0]).all())
+    assert not torch.equal(sums[0], sums[1])
+
+
+@pytest.mark.parametrize("dtype,tile,stages", [("bf16", (256, 256, 64), 2), ("bf16", (256, 256, 32), 4),
+                                               ("i8", (256, 256, 128), 2), ("f32", (128, 64, 16), 2)])
+def test_lds_stream_runs_and_counts_its_bytes(lib, dtype, tile, stages):
+    M, N, K = 1024, 768, 640
+    print("[case] lds stream", dtype, tile, stages, flush=True)
+    es = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}[dtype]
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}[dtype]
+    A = torch.zeros(M, K, dtype=dt, device="cuda")
+    B = torch.zeros(K, N, dtype=dt, device="cuda")
+    r, nbytes = lib.pgemm_diag_lds_stream(M, N, K, A, K, B, N, dtype, tile, stages)
+    assert r == 0, lib.pgemm_strerror(r)
+    torch.cuda.synchronize()
+    tiles = math.ceil(M / tile[0]) * math.ceil(N / tile[1])
+    assert nbytes == tiles * math.ceil(K / tile[2]) * (tile[0] + tile[1]) * tile[2] * es
+
+
+@pytest.mark.parametrize("dtype,tile,stages", [("bf16", (256, 256, 64), 1), ("bf16", (256, 256, 64), 2),
+                                               ("bf16", (256, 256, 32), 4), ("i8", (256, 256, 128), 2),
+                                               ("f32", (128, 64, 16), 2), ("f16", (256, 256, 64), 1)])
+def test_wait_profile_is_the_gemm_with_clock_stamps(lib, dtype, tile, stages):
+    """The wait-profile build computes exactly what the GEMM's own DIRECT
+    variant computes (same bits), and its totals are consistent: every wave
+    passes one ready edge per K tile (plus the prologue's at two or more
+    stages), and its waits fit inside its K loop."""
+    from software_pipelined_tiled_loop_amd import inputs
+    M, N, K = 3 * tile[0] + 5, 2 * tile[1] + 16, 5 * tile[2]
+    print("[case] wait profile", dtype, tile, stages, (M, N, K), flush=True)
+    op = inputs.make_operands(dtype, M, N, K, seed=321, alpha=1.0, beta=0.0)
+    A, B = op.A.cuda(), op.B.cuda()
+    C1, C2 = op.C.cuda(), op.C.cuda()
+    tiles = math.ceil(M / tile[0]) * math.ceil(N / tile[1])
+    grid = math.ceil(tiles / 8) * 8
+    nw = 8 if tile[0] * tile[1] >= 256 * 256 else 4
+    buf = torch.full((grid * nw * 4,), -1, dtype=torch.int64, device="cuda")
+    assert lib.pgemm_diag_wait_profile(M, N, K, A, op.lda, B, op.ldb, C1, op.ldc, dtype, tile, stages, buf,
+                                       buf.numel() - 1) == -1        # out too short: refused
+    r = lib.pgemm_diag_wait_profile(M, N, K, A, op.lda, B, op.ldb, C1, op.ldc, dtype, tile, stages, buf, buf.numel())
+    assert r == 0, lib.pgemm_strerror(r)
+    r = lib.pgemm_gemm_ex(M, N, K, 1.0, A, op.lda, B, op.ldb, 0.0, C2, op.ldc, dtype, stages,
+                          lib._opts("direct", tile), None)
+    assert r == 0
+    torch.cuda.synchronize()
+    same = bool(torch.equal(C1.view(torch.int32), C2.view(torch.int32)))
+    assert same
+    v = buf.view(grid, nw, 4)[:tiles].cpu()
+    nK = math.ceil(K / tile[2])
+    assert bool((v[..., 2] == (nK if stages == 1 else nK + 1)).all())
+    assert bool((v[..., 0] >= 0).all()) and bool((v[..., 1] > 0).all())
+    assert bool((v[..., 0] + v[..., 1] < v[..., 3]).all())
+    assert bool((buf.view(grid, nw, 4)[tiles:] == -1).all())         # idle workgroups write nothing
