@@ -206,6 +206,13 @@ def cpu_baseline(target_s=12.0):
                       % rows}
 
 
+def planner_tables_current(src_hash):
+    """Whether the planner's measured tables were taken on these kernel
+    sources (False: re-run bench.py --retune)."""
+    from software_pipelined_tiled_loop_amd import build
+    return build.load_tables().get("kernel_source_hash") == src_hash
+
+
 def load_traffic(kernel_key, src_hash):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None
     when missing or taken on another version of the kernel sources."""
@@ -218,6 +225,171 @@ def load_traffic(kernel_key, src_hash):
     if not e or e.get("kernel_source_hash") != src_hash:
         return None
     return e.get("bytes_per_launch")
+
+
+# ---- the re-run tile and depth search (planner_tables.json) ------------------------
+
+# Shapes the planner's picks are checked on: the benchmark's, squares, tall,
+# wide and short-K problems per dtype.
+CHECK_SHAPES = (
+    ("f32", 4096, 4096, 4096), ("f16", 4096, 4096, 4096), ("bf16", 4096, 4096, 4096), ("i8", 4096, 4096, 4096),
+    ("bf16", 3000, 3000, 3000), ("bf16", 6144, 6144, 6144), ("bf16", 5120, 5120, 5120), ("bf16", 2048, 2048, 2048),
+    ("f32", 1024, 1024, 1024), ("f32", 2048, 2048, 2048), ("f16", 4096, 4096, 256), ("i8", 2560, 2560, 2560),
+    ("f32", 8192, 8192, 1024), ("f32", 4096, 4096, 512), ("f32", 8192, 4096, 4096), ("f32", 8192, 8192, 64),
+    ("f32", 4096, 4096, 32), ("bf16", 4096, 4096, 32), ("bf16", 4096, 4096, 256), ("bf16", 4096, 4096, 1024),
+    ("i8", 8192, 8192, 1024), ("f16", 1024, 8192, 4096),
+)
+
+
+def _tflops_of(lib, op, A, B, C, stages=0, producer=None, tile=None):
+    return tflops(op.M, op.N, op.K, time_gemm(lib, op, A, B, C, stages=stages, producer=producer, tile=tile))
+
+
+def _device(op):
+    return op.A.cuda(), op.B.cuda(), op.C.cuda()
+
+
+def _variants_of(lib, dt):
+    return [v for v in (lib.pgemm_variant_info(i) for i in range(lib.pgemm_num_variants())) if v["dtype"] == dt]
+
+
+def _misaligned_problem(dt, which):
+    """The problem register-staged producers are measured on: the ragged
+    4000 x 3968 x 4001 shape with A misaligned (lda = K = 4001) for GENERIC
+    and STAGED_A, or 4000 x 3969 x 4000 with B misaligned (ldb = N = 3969)
+    for STAGED_B."""
+    from software_pipelined_tiled_loop_amd import inputs
+    if which == "a":
+        return inputs.make_operands(dt, 4000, 3968, 4001, seed=inputs.seed_for("bf16_k_sweep", 9), lda=4001, ldb=3968)
+    return inputs.make_operands(dt, 4000, 3969, 4000, seed=inputs.seed_for("bf16_k_sweep", 11), lda=4000, ldb=3969)
+
+
+def retune(lib, torch, out_path):
+    """Time every compiled variant on the problems behind each planner
+    constant and write planner_tables.json to out_path (copy it into the
+    package and rebuild)."""
+    from software_pipelined_tiled_loop_amd import build as bld
+    from software_pipelined_tiled_loop_amd import inputs
+    old = bld.load_tables()
+    log = {}
+    # Per DIRECT tile class: the cost of a K tile, the fixed cost of the
+    # first round of workgroups (prologue with cold first loads, epilogue and
+    # C store) and of each later round (whose start overlaps the previous
+    # round's tail), from three problems -- 4096 x 4096 outputs at K = 4096
+    # and K = 256, 8192 x 8192 at K = 128 -- each with the depth the planner
+    # gives the class; the model is
+    #   cycles = first_round + (rounds - 1) * round + units * (2*BM*BN*K) / (eff * dense flops per CU-clock)
+    # (the partial-round cost lam from one workgroup per CU against a full
+    # round of co-resident ones, at the shallowest ring that lets two or more
+    # share a CU).
+    classes = []
+    for dt in ("f32", "f16", "bf16", "i8"):
+        by_class = {}
+        op = workload_operands(dt)
+        A, B, C = _device(op)
+        for v in _variants_of(lib, dt):
+            if v["producer"] != "direct":
+                continue
+            tile = (v["tile_m"], v["tile_n"], v["tile_k"])
+            by_class.setdefault(tile, {})[v["stages"]] = _tflops_of(lib, op, A, B, C, v["stages"], "direct", tile)
+        del A, B, C
+        short = inputs.make_operands(dt, 4096, 4096, 256, seed=inputs.seed_for("bf16_k_sweep", 5))
+        wide = inputs.make_operands(dt, 8192, 8192, 128, seed=inputs.seed_for("bf16_k_sweep", 6))
+        probs = [(o,) + _device(o) for o in (op, short, wide)]
+        import numpy as np
+        for tile, by_s in sorted(by_class.items()):
+            pts = []
+            for o, a, b, c in probs:
+                ms = time_gemm(lib, o, a, b, c, producer="direct", tile=tile)
+                p = plan_of(lib, dt, o.M, o.N, o.K, 0, "direct", tile)
+                n = -(-(-(-o.M // tile[0]) * -(-o.N // tile[1])) // 256)   # tiles on the busiest CU
+                occ = p["wg_per_cu"]
+                r = -(-n // occ)
+                full, part = n // occ, n % occ
+                lam_guess = 0.0
+                units = full * occ + (part + lam_guess * (occ - part) if part else 0)
+                pts.append((o.K, ms * 1e-3 * 2.4e9, r, units))
+            # t = units * k * c + first + (rounds - 1) * later, at the three points
+            mat = np.array([[u * k, 1.0, r - 1.0] for k, t, r, u in pts])
+            rhs = np.array([t for k, t, r, u in pts])
+            c_k, first, later = np.linalg.solve(mat, rhs)
+            first, round_cycles = max(0.0, float(first)), max(0.0, float(later))
+            (k1, t1, r1, u1), (k2, t2, r2, u2) = pts[:2]
+            fpc = {"f32": 64.0, "i8": 2048.0}.get(dt, 1024.0)
+            eff = 2.0 * tile[0] * tile[1] / (c_k * 4.0 * fpc)
+            lam, occ, s_lam = 0.0, 1, min(by_s)
+            for S in sorted(by_s):
+                r, p1 = lib.pgemm_plan(16 * tile[0], 16 * tile[1], 4096, dt, S, 1, {"tile": tile, "producer": "direct"})
+                if S > 1 and p1["wg_per_cu"] >= 2:
+                    occ, s_lam = p1["wg_per_cu"], S
+                    break
+            if occ >= 2:
+                t = {}
+                for rows in (16 * tile[0], 16 * tile[0] * occ):
+                    o = inputs.make_operands(dt, rows, 16 * tile[1], 4096, seed=77)
+                    a, b, c = _device(o)
+                    t[rows] = time_gemm(lib, o, a, b, c, stages=s_lam, producer="direct", tile=tile)
+                    del a, b, c
+                lam = min(1.0, max(0.0, (occ * t[16 * tile[0]] / t[16 * tile[0] * occ] - 1.0) / (occ - 1)))
+            classes.append({"dtype": dt, "tile": list(tile), "eff": round(min(eff, 1.0), 4), "lam": round(lam, 3),
+                            "first_round_cycles": round(first, 0), "round_cycles": round(round_cycles, 0)})
+            log["%s %dx%dx%d" % (dt, *tile)] = {"tflops_4096_by_depth": {k: round(v, 1) for k, v in sorted(by_s.items())},
+                                               "fit_points_K_cycles_rounds_units": [[k, round(t), r, u] for k, t, r, u in pts],
+                                               "partial_round": {"workgroups_per_cu": occ, "stages": s_lam}}
+        del probs
+    # register-staged variants
+    staged = []
+    for dt in ("f32", "f16", "bf16", "i8"):
+        vs = [v for v in _variants_of(lib, dt) if v["producer"] != "direct"]
+        groups = {"register": workload_operands(dt), "a": _misaligned_problem(dt, "a"), "b": _misaligned_problem(dt, "b")}
+        for key, op in groups.items():
+            A, B, C = _device(op)
+            for v in vs:
+                want = {"register": ("register",), "a": ("generic", "staged_a"), "b": ("staged_b",)}[key]
+                if v["producer"] not in want:
+                    continue
+                tile = (v["tile_m"], v["tile_n"], v["tile_k"])
+                t = _tflops_of(lib, op, A, B, C, v["stages"], v["producer"], tile)
+                staged.append({"dtype": dt, "tile": list(tile), "stages": v["stages"], "producer": v["producer"],
+                               "eff": round(t / PEAK[dt], 4)})
+            del A, B, C
+    # load latency: the single-buffer kernels' vmcnt wait per K tile
+    prof = wait_profile(lib, torch, runs=10)
+    latency = max(v["vmcnt_cycles_per_edge"] for k, v in prof.items() if k.endswith(" s1") and "256x256" in k)
+    tables = {"_about": old["_about"], "kernel_source_hash": kernel_source_hash(),
+              "load_latency_cycles": round(float(latency), 1), "prologue_cycles": old["prologue_cycles"],
+              "tie_margin": old["tie_margin"],
+              "class_model": classes, "staged_efficiency": staged}
+    bld.dump_tables(tables, out_path)
+    log["load_latency_from"] = {k: v["vmcnt_cycles_per_edge"] for k, v in prof.items() if k.endswith(" s1")}
+    return log
+
+
+def planner_check(lib, torch):
+    """For each check shape: the planner's plan against every DIRECT tile
+    class (each at the depth the planner gives it), best measured over
+    planner's pick."""
+    from software_pipelined_tiled_loop_amd import inputs
+    out = {}
+    for dt, M, N, K in CHECK_SHAPES:
+        op = inputs.make_operands(dt, M, N, K, seed=1000 + M % 997 + K % 89)
+        A, B, C = _device(op)
+        auto = _tflops_of(lib, op, A, B, C)
+        plan = plan_label(plan_of(lib, dt, M, N, K))
+        best, best_label = 0.0, None
+        tiles = sorted({(v["tile_m"], v["tile_n"], v["tile_k"]) for v in _variants_of(lib, dt) if v["producer"] == "direct"})
+        per = {}
+        for tile in tiles:
+            t = _tflops_of(lib, op, A, B, C, 0, "direct", tile)
+            lab = plan_label(plan_of(lib, dt, M, N, K, 0, "direct", tile))
+            per[lab] = round(t, 1)
+            if t > best:
+                best, best_label = t, lab
+        out["%s %dx%dx%d" % (dt, M, N, K)] = {"planner": plan, "planner_tflops": round(auto, 1), "best": best_label,
+                                              "best_tflops": round(best, 1), "best_over_planner": round(best / auto, 3),
+                                              "classes": per}
+        del A, B, C
+    return out
 
 
 def main():
@@ -234,6 +406,11 @@ def main():
     ap.add_argument("--tile", default=None, help="BMxBNxBK, e.g. 256x256x32")
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed calls before the warm-up, for this long, so the clock has settled (0 = off)")
+    ap.add_argument("--retune", action="store_true",
+                    help="re-run the tile/depth search and write the planner's tables (--retune-out)")
+    ap.add_argument("--retune-out", default=os.path.join(ROOT, "gpurun_out", "planner_tables.json"))
+    ap.add_argument("--planner-check", action="store_true",
+                    help="time every tile class on the check shapes against the planner's pick")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (scales HBM counters)")
     args = ap.parse_args()
@@ -251,6 +428,16 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     src_hash = kernel_source_hash()
+    if args.retune or args.planner_check:
+        rep = {}
+        if args.retune:
+            os.makedirs(os.path.dirname(os.path.abspath(args.retune_out)), exist_ok=True)
+            rep["retune"] = retune(lib, torch, args.retune_out)
+            rep["retune"]["written"] = args.retune_out
+        if args.planner_check:
+            rep["planner_check"] = planner_check(lib, torch)
+        print(json.dumps(rep))
+        return
 
     # ---- timed workload (default: fp32 SGEMM 4096^3, alpha=1, beta=0.5) ----
     w = WORKLOADS[args.workload]
@@ -334,7 +521,7 @@ def main():
         "config": {"workload": w["name"], "M": M, "N": N, "K": K,
                    "pct_of_peak": round(100.0 * value / PEAK[dt], 2), "plan": plan,
                    "wall_s_timed_region": round(t_wall, 4), "clock_settle_calls": settle_calls,
-                   "kernel_source_hash": src_hash},
+                   "kernel_source_hash": src_hash, "planner_tables_current": planner_tables_current(src_hash)},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline and args.workload == "f32":

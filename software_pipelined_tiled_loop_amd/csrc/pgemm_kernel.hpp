@@ -941,6 +941,11 @@ __device__ __forceinline__ void tile_body(const KernelArgs& g, const Cursor& dc,
             debug_skew(g, s, wave, C::NW);
             const char PGEMM_LDS* rstage = smem + nstage * C::STAGE_BYTES;
             char PGEMM_LDS* freed = smem + cur * C::STAGE_BYTES;
+            // The LDS-DMA descriptors of slot s+S are formed after the
+            // barrier: formed before it (measured), they delay the last wave
+            // to arrive, whose arrival sets the K tile's period, and the
+            // loop ran 1 % slower.
+            const DmaTile d = C::ANY_DMA ? dma_setup<C>(g, dc.m0, dc.n0, dc.kt, freed, wave) : none;
             if constexpr (C::ANY_STAGED) {
                 // Spread over the MFMA groups: after group 0 the staged
                 // operand of slot s+S (in registers since B_s) is written to
@@ -948,15 +953,13 @@ __device__ __forceinline__ void tile_body(const KernelArgs& g, const Cursor& dc,
                 // any) follow in the first groups, and after group REG_GROUP
                 // the register loads of slot s+S+1 -- behind every piece, so
                 // the next barrier waits for the pieces only.
-                const DmaTile d = C::ANY_DMA ? dma_setup<C>(g, dc.m0, dc.n0, dc.kt, freed, wave) : none;
                 auto staged = [&](int gi) {
                     if (gi == 0) store_tile<C>(freed, st, wave, lane);
                     if (gi == C::REG_GROUP) issue_regs<C>(g, rc.m0, rc.n0, rc.kt, st, wave, lane);
                 };
                 mfma_step<C, true, C::ANY_DMA, FULL>(acc, use, nxt, rstage, 0, g, d, wave, lane, wm0, wn0, staged);
             } else {
-                const DmaTile d = dma_setup<C>(g, dc.m0, dc.n0, dc.kt, freed, wave);  // slot s+S (maybe none)
-                mfma_step<C, true, true, FULL>(acc, use, nxt, rstage, 0, g, d, wave, lane, wm0, wn0);
+                mfma_step<C, true, true, FULL>(acc, use, nxt, rstage, 0, g, d, wave, lane, wm0, wn0);  // slot s+S
             }
         }
     }

@@ -40,7 +40,8 @@ def test_abi_host_paths_under_sanitizers(tmp_path):
     except RuntimeError:
         pytest.skip("hipcc not available")
     csrc = build.CSRC
-    flags = [f for f in build.HIPCC_FLAGS if f != "-O3"] + ["-O1", "-g"]
+    build.generate_tables()
+    flags = [f for f in build.HIPCC_FLAGS if f != "-O3"] + ["-O1", "-g", "-I" + build.GEN_DIR]
     objs = []
     for name in ("kern_f32.hip", "kern_f16.hip", "kern_bf16.hip", "kern_i8.hip"):
         built = os.path.join(build.BUILD_DIR, name + ".o")
