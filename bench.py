@@ -680,13 +680,26 @@ PROFILE_POINTS = (("bf16", (256, 256, 64)), ("f16", (256, 256, 64)), ("i8", (256
                   ("f32", (256, 256, 32)))
 
 
+def _warm_then_run(call, torch, runs):
+    """Run `call` for about WARMUP_MS (the clock settles under load), then
+    `runs` more times; the output of the last one is what is read."""
+    t_end = time.perf_counter() + WARMUP_MS / 1e3
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+    for _ in range(runs):
+        call()
+    torch.cuda.synchronize()
+
+
 def wait_profile(lib, torch, runs=20):
     """Where the waves of a ready edge wait (pgemm_diag_wait_profile: the
     GEMM kernel built with clock stamps around its waits), at one and two
     stages of each 4096^3 class: the share of the K loop's wave-cycles spent
     in the vmcnt wait for the K tile's loads, and in the workgroup barrier
-    after it.  The last of `runs` back-to-back launches is read (clock
-    settled)."""
+    after it.  The last of `runs` back-to-back launches after the warm-up
+    is read (clock settled)."""
     out = {}
     for wl, tile in PROFILE_POINTS:
         op = workload_operands(wl)
@@ -694,21 +707,68 @@ def wait_profile(lib, torch, runs=20):
         tiles = -(-op.M // tile[0]) * -(-op.N // tile[1])
         grid = -(-tiles // 8) * 8
         nw = 8 if tile[0] * tile[1] >= 256 * 256 else 4
-        buf = torch.zeros(grid * nw * 4, dtype=torch.int64, device="cuda")
+        buf = torch.zeros(grid * nw * 8, dtype=torch.int64, device="cuda")
         for S in (1, 2):
-            for _ in range(runs):
+            def call():
                 r = lib.pgemm_diag_wait_profile(op.M, op.N, op.K, A, op.lda, B, op.ldb, C, op.ldc, op.dtype, tile, S,
                                                 buf, buf.numel())
                 if r != 0:
                     raise lib.PgemmError(r)
-            torch.cuda.synchronize()
-            v = buf.view(grid, nw, 4)[:tiles].cpu().double()
+            _warm_then_run(call, torch, runs)
+            v = buf.view(grid, nw, 8)[:tiles].cpu().double()
             vm, bar, n, loop = (float(v[..., i].sum()) for i in range(4))
             out["%s %dx%dx%d s%d" % (op.dtype, tile[0], tile[1], tile[2], S)] = {
                 "vmcnt_wait_share": round(vm / loop, 4), "barrier_wait_share": round(bar / loop, 4),
                 "ready_edges_per_wave": round(n / (tiles * nw), 2),
                 "vmcnt_cycles_per_edge": round(vm / max(n, 1), 1), "barrier_cycles_per_edge": round(bar / max(n, 1), 1),
                 "loop_cycles_per_edge": round(loop / max(n, 1), 1)}
+        del A, B, C, buf
+    return out
+
+
+# (label, workload, tile, stages): the short-K point with the plan the
+# planner picks and the designs with more, smaller tiles per CU
+TIMELINE_POINTS = (("256x256x64 s2 (planner)", "bf16_k1024", (256, 256, 64), 2),
+                   ("128x128x64 s2", "bf16_k1024", (128, 128, 64), 2),
+                   ("128x128x64 s3", "bf16_k1024", (128, 128, 64), 3),
+                   ("256x256x64 s2 at K=4096", "bf16", (256, 256, 64), 2))
+
+
+def timeline(lib, torch, runs=20):
+    """Per-workgroup timeline of a launch on the GPU's 100 MHz clock (the
+    wait-profile build): for each workgroup its start, the end of its
+    prologue (first ready edge), the end of its K loop and the completion of
+    its C stores (wave 0 of each workgroup).  Reported as the launch's span
+    and the median / extreme phase times over workgroups, in microseconds:
+    where a short-K launch spends its time (page "Software pipelines and
+    asynchronous copies", section "Worked example": prologue and epilogue
+    occupy a large fraction at short K)."""
+    import numpy as np
+    out = {}
+    for label, wl, tile, S in TIMELINE_POINTS:
+        op = workload_operands(wl)
+        A, B, C = op.A.cuda(), op.B.cuda(), op.C.cuda()
+        tiles = -(-op.M // tile[0]) * -(-op.N // tile[1])
+        grid = -(-tiles // 8) * 8
+        nw = 8 if tile[0] * tile[1] >= 256 * 256 else 4
+        buf = torch.zeros(grid * nw * 8, dtype=torch.int64, device="cuda")
+        def call():
+            r = lib.pgemm_diag_wait_profile(op.M, op.N, op.K, A, op.lda, B, op.ldb, C, op.ldc, op.dtype, tile, S,
+                                            buf, buf.numel())
+            if r != 0:
+                raise lib.PgemmError(r)
+        _warm_then_run(call, torch, runs)
+        v = buf.view(grid, nw, 8)[:tiles, 0].cpu().numpy().astype(np.float64) / 100.0  # 100 MHz ticks -> us
+        start, loop_end, store_end, ready0 = v[:, 4], v[:, 5], v[:, 6], v[:, 7]
+        t0 = start.min()
+        med = lambda x: round(float(np.median(x)), 2)
+        out[label] = {"M": op.M, "N": op.N, "K": op.K, "workgroups": tiles,
+                      "span_us": round(float(store_end.max() - t0), 2),
+                      "median_prologue_us": med(ready0 - start), "median_k_loop_us": med(loop_end - ready0),
+                      "median_store_us": med(store_end - loop_end),
+                      "start_us": [round(float(start.min() - t0), 2), round(float(start.max() - t0), 2)],
+                      "k_loop_end_us": [round(float(loop_end.min() - t0), 2), round(float(loop_end.max() - t0), 2)],
+                      "store_end_us": [round(float(store_end.min() - t0), 2), round(float(store_end.max() - t0), 2)]}
         del A, B, C, buf
     return out
 
@@ -767,6 +827,7 @@ def run_reports(lib, torch):
     rep["pages_context"] = pages_context(rep)
     rep["ceilings"] = ceilings(lib, torch)
     rep["wait_profile"] = wait_profile(lib, torch)
+    rep["timeline"] = timeline(lib, torch)
     return rep
 
 

@@ -323,18 +323,21 @@ int pgemm_hazard_copy_reduce(const int32_t* X, int64_t rows, int64_t cols, int64
  * and results as pgemm_gemm) with a wait-profile build of the DIRECT variant
  * of tile class (tile_m, tile_n, tile_k) at ring depth `stages`: the same
  * kernel with shader-clock stamps around the two waits of every ready edge.
- * For each wave w of each workgroup b that has a tile, out[(b*W + w)*4 + i]
- * (W = waves per workgroup) receives, in shader clocks: i = 0 the time in the
- * vmcnt wait (the K tile's loads landing), 1 the time from there through the
- * workgroup barrier (every other wave arriving; for one stage also the reuse
- * barrier), 2 the number of ready edges, 3 the whole K loop.  `out` is device
- * memory owned by the caller, 8-byte aligned, out_len >= grid * W * 4
- * entries with grid = ceil(tiles / 8) * 8.  Both operands must meet the
+ * For each wave w of each workgroup b that has a tile, out[(b*W + w)*8 + i]
+ * (W = waves per workgroup) receives: in shader clocks, i = 0 the time in
+ * the vmcnt wait (the K tile's loads landing), 1 the time from there through
+ * the workgroup barrier (every other wave arriving; for one stage also the
+ * reuse barrier), 2 the number of ready edges, 3 the whole K loop; and on the
+ * GPU's constant 100 MHz clock (s_memrealtime), the wave's timeline: 4 its
+ * start, 7 the first ready edge passed (end of the prologue), 5 the end of
+ * the K loop, 6 its C stores complete.  `out` is device memory owned by the
+ * caller, 8-byte aligned, out_len >= grid * W * 8 entries with
+ * grid = ceil(tiles / 8) * 8.  Both operands must meet the
  * 16-byte rules (pgemm_producer).  Asynchronous on `stream`.  Errors:
  * UNSUPPORTED_DTYPE; INVALID_ARG; TOO_LARGE; INFEASIBLE_PLAN when no profile
  * build of that class and depth is compiled (bf16 256x256x64 S1/S2,
- * 256x256x32 S1..S4; fp16 256x256x64 S1/S2; int8 256x256x128 S1/S2; fp32
- * 128x64x16 S1/S2, 256x256x32 S1/S2); HIP for a rejected launch. */
+ * 256x256x32 S1..S4, 128x128x64 S2/S3; fp16 256x256x64 S1/S2; int8
+ * 256x256x128 S1/S2; fp32 128x64x16 S1/S2, 256x256x32 S1/S2); HIP for a rejected launch. */
 int pgemm_diag_wait_profile(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                             const void* B, int64_t ldb, void* C, int64_t ldc, int dtype,
                             int tile_m, int tile_n, int tile_k, int stages, int64_t* out,

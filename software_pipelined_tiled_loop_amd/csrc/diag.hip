@@ -175,6 +175,7 @@ static const ProbeVariant k_probes[] = {
     PGEMM_PROBE(DT_BF16, 256, 256, 64, 1, 2, 4), PGEMM_PROBE(DT_BF16, 256, 256, 64, 2, 2, 4),
     PGEMM_PROBE(DT_BF16, 256, 256, 32, 1, 2, 4), PGEMM_PROBE(DT_BF16, 256, 256, 32, 2, 2, 4),
     PGEMM_PROBE(DT_BF16, 256, 256, 32, 3, 2, 4), PGEMM_PROBE(DT_BF16, 256, 256, 32, 4, 2, 4),
+    PGEMM_PROBE(DT_BF16, 128, 128, 64, 2, 2, 2), PGEMM_PROBE(DT_BF16, 128, 128, 64, 3, 2, 2),
     PGEMM_PROBE(DT_F16, 256, 256, 64, 1, 2, 4),  PGEMM_PROBE(DT_F16, 256, 256, 64, 2, 2, 4),
     PGEMM_PROBE(DT_I8, 256, 256, 128, 1, 2, 4),  PGEMM_PROBE(DT_I8, 256, 256, 128, 2, 2, 4),
     PGEMM_PROBE(DT_F32, 128, 64, 16, 1, 2, 2),   PGEMM_PROBE(DT_F32, 128, 64, 16, 2, 2, 2),
@@ -284,8 +285,8 @@ extern "C" int pgemm_diag_wait_profile(int64_t M, int64_t N, int64_t K, const vo
     const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
     if (tiles > 0x7ffffff0) return PGEMM_ERR_TOO_LARGE;
     const int grid = (int)((tiles + 7) / 8 * 8);
-    // every workgroup with a tile writes four totals per wave; idle ones write nothing
-    if (out_len < (int64_t)grid * v->nw * 4) return PGEMM_ERR_INVALID_ARG;
+    // every workgroup with a tile writes kProbeWords entries per wave; idle ones write nothing
+    if (out_len < (int64_t)grid * v->nw * kProbeWords) return PGEMM_ERR_INVALID_ARG;
     a.probe = reinterpret_cast<long long*>(out);
     void* args[] = {&a};
     const hipError_t e = hipLaunchKernel(v->fn, dim3(grid), dim3(v->threads), args, 0, (hipStream_t)stream);

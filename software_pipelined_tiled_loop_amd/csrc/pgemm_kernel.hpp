@@ -337,14 +337,18 @@ struct ProbeCfg : Base {
 };
 
 // Per-wave clock totals of a wait-profile build: cycles spent in the vmcnt
-// wait of the ready edges, cycles from there through the barrier, and the
-// number of ready edges.
+// wait of the ready edges, cycles from there through the barrier, the
+// number of ready edges, and the time (100 MHz clock) the first ready edge
+// (the end of the prologue) was passed.
 template <bool P>
 struct ProbeSlots {};
 template <>
 struct ProbeSlots<true> {
-    long long vm = 0, bar = 0, n = 0;
+    long long vm = 0, bar = 0, n = 0, rt_ready0 = 0;
 };
+
+// Entries per wave of the wait-profile output.
+constexpr int kProbeWords = 8;
 
 template <class C>
 struct Staging : ProbeSlots<C::PROBE> {
@@ -801,6 +805,7 @@ __device__ __forceinline__ void probed_barrier(Staging<C>& st) {
         const long long t2 = (long long)__builtin_amdgcn_s_memtime();
         st.vm += t1 - t0;
         st.bar += t2 - t1;
+        if (READY && st.n == 0) st.rt_ready0 = (long long)__builtin_amdgcn_s_memrealtime();
         st.n += READY ? 1 : 0;
     } else if constexpr (VM >= 0) {
         wait_barrier<(VM >= 0 ? VM : 0)>();
@@ -815,8 +820,10 @@ __device__ __forceinline__ void sync_ring(Staging<C>& st) {
 }
 
 // Start of a K loop, and its end: a wait-profile build writes the wave's
-// totals (vmcnt cycles, barrier cycles, ready edges, cycles of the whole
-// loop) to g.probe[(workgroup * waves + wave) * 4 ...].
+// totals to g.probe[(workgroup * waves + wave) * kProbeWords + i]: i = 0
+// vmcnt cycles, 1 barrier cycles, 2 ready edges, 3 shader cycles of the
+// whole loop, 7 the 100 MHz time of the first ready edge (the kernel writes
+// 4..6, see probe_times).
 template <class C>
 __device__ __forceinline__ long long probe_start() {
     if constexpr (C::PROBE) return (long long)__builtin_amdgcn_s_memtime();
@@ -828,11 +835,12 @@ __device__ __forceinline__ void probe_end(const KernelArgs& g, const Staging<C>&
     if constexpr (C::PROBE) {
         const long long t_end = (long long)__builtin_amdgcn_s_memtime();
         if (lane == 0) {
-            long long* o = g.probe + ((int64_t)blockIdx.x * C::NW + wave) * 4;
+            long long* o = g.probe + ((int64_t)blockIdx.x * C::NW + wave) * kProbeWords;
             o[0] = st.vm;
             o[1] = st.bar;
             o[2] = st.n;
             o[3] = t_end - t_begin;
+            o[7] = st.rt_ready0;
         }
     }
 }
@@ -1270,6 +1278,7 @@ __global__ void __launch_bounds__(C::NT) gemm_kernel(KernelArgs g) {
     __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_BYTES];
     char PGEMM_LDS* smem = (char PGEMM_LDS*)smem_raw;
 
+    const long long rt_start = C::PROBE ? (long long)__builtin_amdgcn_s_memrealtime() : 0;
     const WgTiles w = wg_tiles(g);
     if (w.count == 0) return;  // more workgroups than tiles in this XCD's range
     const int lane = threadIdx.x & 63;
@@ -1296,7 +1305,20 @@ __global__ void __launch_bounds__(C::NT) gemm_kernel(KernelArgs g) {
             else
                 pertile_loop<C>(g, m0, n0, nK, smem, acc, wave, lane, wm0, wn0);
         }
+        const long long rt_loop = C::PROBE ? (long long)__builtin_amdgcn_s_memrealtime() : 0;
         store_c<C>(g, m0, n0, wm0, wn0, lane, acc);
+        if constexpr (C::PROBE) {
+            // the wave's timeline on the 100 MHz clock: start, end of the K
+            // loop, and its C stores complete
+            __builtin_amdgcn_s_waitcnt(0);
+            const long long rt_end = (long long)__builtin_amdgcn_s_memrealtime();
+            if (lane == 0) {
+                long long* o = g.probe + ((int64_t)blockIdx.x * C::NW + wave) * kProbeWords;
+                o[4] = rt_start;
+                o[5] = rt_loop;
+                o[6] = rt_end;
+            }
+        }
     } else {
         // Persistent with one ring slot (S = 1), or K = 0: tile by tile.
         for (int i = 0; i < w.count; ++i) {

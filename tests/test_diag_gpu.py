@@ -61,7 +61,8 @@ def test_lds_stream_runs_and_counts_its_bytes(lib, dtype, tile, stages):
 
 @pytest.mark.parametrize("dtype,tile,stages", [("bf16", (256, 256, 64), 1), ("bf16", (256, 256, 64), 2),
                                                ("bf16", (256, 256, 32), 4), ("i8", (256, 256, 128), 2),
-                                               ("f32", (128, 64, 16), 2), ("f16", (256, 256, 64), 1)])
+                                               ("f32", (128, 64, 16), 2), ("f16", (256, 256, 64), 1),
+                                               ("bf16", (128, 128, 64), 3)])
 def test_wait_profile_is_the_gemm_with_clock_stamps(lib, dtype, tile, stages):
     """The wait-profile build computes exactly what the GEMM's own DIRECT
     variant computes (same bits), and its totals are consistent: every wave
@@ -76,7 +77,7 @@ def test_wait_profile_is_the_gemm_with_clock_stamps(lib, dtype, tile, stages):
     tiles = math.ceil(M / tile[0]) * math.ceil(N / tile[1])
     grid = math.ceil(tiles / 8) * 8
     nw = 8 if tile[0] * tile[1] >= 256 * 256 else 4
-    buf = torch.full((grid * nw * 4,), -1, dtype=torch.int64, device="cuda")
+    buf = torch.full((grid * nw * 8,), -1, dtype=torch.int64, device="cuda")
     assert lib.pgemm_diag_wait_profile(M, N, K, A, op.lda, B, op.ldb, C1, op.ldc, dtype, tile, stages, buf,
                                        buf.numel() - 1) == -1        # out too short: refused
     r = lib.pgemm_diag_wait_profile(M, N, K, A, op.lda, B, op.ldb, C1, op.ldc, dtype, tile, stages, buf, buf.numel())
@@ -87,9 +88,12 @@ def test_wait_profile_is_the_gemm_with_clock_stamps(lib, dtype, tile, stages):
     torch.cuda.synchronize()
     same = bool(torch.equal(C1.view(torch.int32), C2.view(torch.int32)))
     assert same
-    v = buf.view(grid, nw, 4)[:tiles].cpu()
+    v = buf.view(grid, nw, 8)[:tiles].cpu()
     nK = math.ceil(K / tile[2])
     assert bool((v[..., 2] == (nK if stages == 1 else nK + 1)).all())
     assert bool((v[..., 0] >= 0).all()) and bool((v[..., 1] > 0).all())
     assert bool((v[..., 0] + v[..., 1] < v[..., 3]).all())
-    assert bool((buf.view(grid, nw, 4)[tiles:] == -1).all())         # idle workgroups write nothing
+    # timeline on the 100 MHz clock: start <= first ready edge <= K loop end <= stores complete
+    assert bool((v[..., 4] <= v[..., 7]).all()) and bool((v[..., 7] <= v[..., 5]).all())
+    assert bool((v[..., 5] <= v[..., 6]).all()) and bool((v[..., 4] > 0).all())
+    assert bool((buf.view(grid, nw, 8)[tiles:] == -1).all())         # idle workgroups write nothing
