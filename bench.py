@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 PEAK = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6, "i8": 5033.2}  # dense TFLOP/s (TOP/s), MI355X
 HBM_PEAK_GBS = 8000.0
+CLOCK_GHZ = 2.4  # the clock the dense peaks are quoted at
 PAGE_SGEMM_GFLOPS = 32107.5  # 2-stage SGEMM 4096^3 on the first page's (unnamed NVIDIA) GPU
 
 
@@ -642,19 +643,22 @@ def ceilings(lib, torch):
     out = {"mfma_only": {}, "lds_stream": {}}
     grid = 256
     buf = torch.zeros(grid * 8, dtype=torch.float32, device="cuda")
+    clock = torch.zeros(grid * 4, dtype=torch.int64, device="cuda")
     for dt in ("f32", "f16", "bf16", "i8"):
         row = {}
         for zero in (0, 1):
             box = {}
 
             def call():
-                r, box["flops"] = lib.pgemm_diag_mfma_ceiling(dt, zero, CEILING_ITERS[dt], grid, 12345, buf)
+                r, box["flops"] = lib.pgemm_diag_mfma_ceiling(dt, zero, CEILING_ITERS[dt], grid, 12345, buf,
+                                                              clock=clock)
                 if r != 0:
                     raise lib.PgemmError(r)
 
             ms = time_calls(call)
             t = box["flops"] / (ms * 1e-3) / 1e12
-            row["zero" if zero else "random"] = {"tflops": round(t, 1), "pct_peak": round(100 * t / PEAK[dt], 1)}
+            row["zero" if zero else "random"] = {"tflops": round(t, 1), "pct_peak": round(100 * t / PEAK[dt], 1),
+                                                 "clock_ghz": clock_ghz(clock, grid)}
         out["mfma_only"][dt] = row
     for wl, tile, S in STREAM_POINTS:
         op = workload_operands(wl)
@@ -672,6 +676,51 @@ def ceilings(lib, torch):
             "us": round(ms * 1e3, 2), "TBs": round(box["bytes"] / (ms * 1e-3) / 1e12, 2),
             "gemm_tflops_fed": round(t, 1), "pct_peak_fed": round(100 * t / PEAK[op.dtype], 1)}
         del A, B
+    return out
+
+
+def clock_ghz(clock, n):
+    """Mean shader clock (GHz) over the first n workgroups of a diagnostic's
+    clock stamps: shader-clock span over the 100 MHz span of each."""
+    c = clock.view(-1, 4)[:n].cpu().double()
+    return round(float(((c[:, 2] - c[:, 0]) / ((c[:, 3] - c[:, 1]) / 100e6)).mean()) / 1e9, 3)
+
+
+# The parts ladder (pgemm_diag_parts): the steps, each adding one part of the
+# K loop's steady state, and the planner's 4096^3 class of each dtype at two
+# stages.
+PARTS_LADDER = (("mfma only", 0), ("+ A reads", 4), ("B reads only", 8), ("+ A and B reads", 12),
+                ("+ barrier", 14), ("+ LDS-DMA (the GEMM)", 15))
+PARTS_POINTS = (("bf16", (256, 256, 64)), ("f16", (256, 256, 64)), ("i8", (256, 256, 128)), ("f32", (128, 64, 16)))
+
+
+def parts_ladder(lib, torch):
+    """The GEMM kernel of each 4096^3 class built with parts of its K loop
+    left out (pgemm_diag_parts), from the MFMAs alone to the whole loop: the
+    rate of each step, the shader clock it ran at (stamped by the kernel),
+    and its MFMA share at that clock (rate over the dense peak scaled to the
+    clock).  What each part costs, in rate and in clock."""
+    out = {}
+    for wl, tile in PARTS_POINTS:
+        op = workload_operands(wl)
+        A, B, C = op.A.cuda(), op.B.cuda(), op.C.cuda()
+        tiles = -(-op.M // tile[0]) * -(-op.N // tile[1])
+        grid = -(-tiles // 8) * 8
+        clock = torch.zeros(grid * 4, dtype=torch.int64, device="cuda")
+        row = {}
+        for label, parts in PARTS_LADDER:
+            def call():
+                r = lib.pgemm_diag_parts(op.M, op.N, op.K, A, op.lda, B, op.ldb, C, op.ldc, op.dtype, tile, 2, parts,
+                                         clock, clock.numel())
+                if r != 0:
+                    raise lib.PgemmError(r)
+            ms = time_calls(call)
+            t = tflops(op.M, op.N, op.K, ms)
+            ghz = clock_ghz(clock, tiles)
+            row[label] = {"us": round(ms * 1e3, 2), "tflops": round(t, 1), "pct_peak": round(100 * t / PEAK[wl], 1),
+                          "clock_ghz": ghz, "mfma_share_at_clock": round(t / (PEAK[wl] * ghz / CLOCK_GHZ), 3)}
+        out["%s %dx%dx%d s2" % (op.dtype, tile[0], tile[1], tile[2])] = row
+        del A, B, C, clock
     return out
 
 
@@ -826,6 +875,7 @@ def run_reports(lib, torch):
     ops.clear()
     rep["pages_context"] = pages_context(rep)
     rep["ceilings"] = ceilings(lib, torch)
+    rep["parts_ladder"] = parts_ladder(lib, torch)
     rep["wait_profile"] = wait_profile(lib, torch)
     rep["timeline"] = timeline(lib, torch)
     return rep

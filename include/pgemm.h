@@ -302,9 +302,13 @@ int pgemm_hazard_copy_reduce(const int32_t* X, int64_t rows, int64_t cols, int64
  * zeros when zero_operands = 1.  No memory traffic besides one float per wave
  * written to out[grid * 8] (device memory owned by the caller, 4-byte
  * aligned), which keeps the accumulators live.  *flops (optional) receives
- * the flops of the launch.  Asynchronous on `stream`.  Errors:
- * UNSUPPORTED_DTYPE; INVALID_ARG for iters outside 0..2^24, grid outside
- * 1..65536 or a bad `out`; HIP for a rejected launch.
+ * the flops of the launch.  `clock` (optional, device memory, 8-byte
+ * aligned, grid * 4 entries) receives per workgroup the shader clock and
+ * the constant 100 MHz clock (s_memtime, s_memrealtime) of wave 0 at its
+ * start, then both at its end: the shader clock's rate under this load.
+ * Asynchronous on `stream`.  Errors: UNSUPPORTED_DTYPE; INVALID_ARG for
+ * iters outside 0..2^24, grid outside 1..65536 or a bad `out` or `clock`;
+ * HIP for a rejected launch.
  *
  * pgemm_diag_lds_stream: the producer alone.  For the compiled stream of tile
  * class (tile_m, tile_n, tile_k) at ring depth `stages` it issues exactly the
@@ -343,10 +347,53 @@ int pgemm_diag_wait_profile(int64_t M, int64_t N, int64_t K, const void* A, int6
                             int tile_m, int tile_n, int tile_k, int stages, int64_t* out,
                             int64_t out_len, void* stream);
 int pgemm_diag_mfma_ceiling(int dtype, int zero_operands, int iters, int grid, uint32_t seed,
-                            float* out, int64_t* flops, void* stream);
+                            float* out, int64_t* flops, int64_t* clock, void* stream);
 int pgemm_diag_lds_stream(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                           const void* B, int64_t ldb, int dtype, int tile_m, int tile_n,
                           int tile_k, int stages, int64_t* lds_bytes, void* stream);
+
+/* pgemm_diag_parts: the parts ladder (page "Software pipelines and
+ * asynchronous copies", section "Worked example: Choosing between two and
+ * four stages", last point, as above).  The GEMM kernel of the DIRECT
+ * variant of tile class (tile_m, tile_n, tile_k) at ring depth `stages`,
+ * built with only the steady-state parts in `parts` (a set of pgemm_part
+ * bits; PGEMM_PART_ALL is the GEMM itself):
+ *   PGEMM_PART_DMA      the LDS-DMA pieces of the K tiles after the prologue;
+ *                       without them the two stages keep the prologue's K
+ *                       tiles, so the matrix cores still multiply operand
+ *                       data;
+ *   PGEMM_PART_BARRIER  the workgroup barrier of each ready edge (its waits
+ *                       stay); the prologue keeps its barrier;
+ *   PGEMM_PART_AREADS   the A fragment reads from LDS;
+ *   PGEMM_PART_BREADS   the B fragment (transposing) reads from LDS; a
+ *                       left-out read leaves the previous fragment in place
+ *                       (both fragment register sets start from operand
+ *                       data: K steps 0 and 1 of the first K tile).
+ * The MFMAs and the C store always run.  C receives A*B only for
+ * PGEMM_PART_ALL; otherwise C receives values of no meaning.  Wave 0 of each
+ * workgroup b with a tile writes clock[b*4 + i]: i = 0 the shader clock
+ * (s_memtime) and 1 the 100 MHz clock (s_memrealtime) at its start, 2 and 3
+ * the same after its last store; dividing the shader-clock span by the
+ * 100 MHz span gives the clock the launch ran at.  Layout and alignment
+ * rules as for pgemm_diag_wait_profile; `clock` is device memory owned by
+ * the caller, 8-byte aligned, clock_len >= grid * 4 with
+ * grid = ceil(tiles / 8) * 8.  Asynchronous on `stream`.  Errors:
+ * UNSUPPORTED_DTYPE; INVALID_ARG (including `parts` outside 0..15);
+ * TOO_LARGE; INFEASIBLE_PLAN unless the class is bf16 or fp16 256x256x64
+ * S2, int8 256x256x128 S2 or fp32 128x64x16 S2 and `parts` is one of 0,
+ * AREADS, BREADS, AREADS|BREADS, AREADS|BREADS|BARRIER, ALL; HIP for a
+ * rejected launch. */
+enum pgemm_part {
+    PGEMM_PART_DMA = 1,
+    PGEMM_PART_BARRIER = 2,
+    PGEMM_PART_AREADS = 4,
+    PGEMM_PART_BREADS = 8,
+    PGEMM_PART_ALL = 15
+};
+int pgemm_diag_parts(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, void* C, int64_t ldc, int dtype, int tile_m, int tile_n,
+                     int tile_k, int stages, int parts, int64_t* clock, int64_t clock_len,
+                     void* stream);
 
 /* ABI version: major*10000 + minor*100 + patch (a library convention, not
  * from the pages). */

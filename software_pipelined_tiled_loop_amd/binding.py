@@ -89,7 +89,7 @@ _lib.pgemm_model_compute_load_ratio.argtypes = [_int, _int, _int, _int]
 _lib.pgemm_model_compute_load_ratio.restype = _dbl
 _lib.pgemm_hazard_copy_reduce.argtypes = [_vp, _i64, _i64, _i64, _vp, _int, _int, _int, _vp, _i64, _int, _vp]
 _lib.pgemm_hazard_copy_reduce.restype = _int
-_lib.pgemm_diag_mfma_ceiling.argtypes = [_int, _int, _int, _int, ctypes.c_uint32, _vp, ctypes.POINTER(_i64), _vp]
+_lib.pgemm_diag_mfma_ceiling.argtypes = [_int, _int, _int, _int, ctypes.c_uint32, _vp, ctypes.POINTER(_i64), _vp, _vp]
 _lib.pgemm_diag_mfma_ceiling.restype = _int
 _lib.pgemm_diag_lds_stream.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _int, _int, _int, _int, _int,
                                        ctypes.POINTER(_i64), _vp]
@@ -97,11 +97,17 @@ _lib.pgemm_diag_lds_stream.restype = _int
 _lib.pgemm_diag_wait_profile.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int, _int, _int, _int,
                                          _int, _vp, _i64, _vp]
 _lib.pgemm_diag_wait_profile.restype = _int
+_lib.pgemm_diag_parts.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int, _int, _int, _int, _int,
+                                  _int, _vp, _i64, _vp]
+_lib.pgemm_diag_parts.restype = _int
+
+# Steady-state parts of a parts-ladder build (enum pgemm_part).
+PART_DMA, PART_BARRIER, PART_AREADS, PART_BREADS, PART_ALL = 1, 2, 4, 8, 15
 
 EXPORTED = ("pgemm_gemm", "pgemm_gemm_ex", "pgemm_plan", "pgemm_strerror", "pgemm_num_variants",
             "pgemm_variant_info", "pgemm_version", "pgemm_model_uncovered_cycles", "pgemm_model_lds_bytes",
             "pgemm_model_global_loads_per_output", "pgemm_model_compute_load_ratio", "pgemm_hazard_copy_reduce",
-            "pgemm_diag_mfma_ceiling", "pgemm_diag_lds_stream", "pgemm_diag_wait_profile")
+            "pgemm_diag_mfma_ceiling", "pgemm_diag_lds_stream", "pgemm_diag_wait_profile", "pgemm_diag_parts")
 
 
 class PgemmError(RuntimeError):
@@ -253,11 +259,12 @@ def pgemm_hazard_copy_reduce(X, rows, cols, ldx, row_sums, reuse_wait, delay_wav
                                          _stream(stream))
 
 
-def pgemm_diag_mfma_ceiling(dtype, zero_operands, iters, grid, seed, out, stream=None):
+def pgemm_diag_mfma_ceiling(dtype, zero_operands, iters, grid, seed, out, clock=None, stream=None):
     """Returns (status, flops of the launch)."""
     fl = _i64(0)
     r = _lib.pgemm_diag_mfma_ceiling(DTYPE_CODE.get(dtype, dtype), int(zero_operands), int(iters), int(grid),
-                                     int(seed) & 0xFFFFFFFF, _ptr(out), ctypes.byref(fl), _stream(stream))
+                                     int(seed) & 0xFFFFFFFF, _ptr(out), ctypes.byref(fl), _ptr(clock),
+                                     _stream(stream))
     return r, fl.value
 
 
@@ -274,3 +281,9 @@ def pgemm_diag_wait_profile(M, N, K, A, lda, B, ldb, C, ldc, dtype, tile, stages
     return _lib.pgemm_diag_wait_profile(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, DTYPE_CODE.get(dtype, dtype),
                                         int(tile[0]), int(tile[1]), int(tile[2]), int(stages), _ptr(out),
                                         int(out_len), _stream(stream))
+
+
+def pgemm_diag_parts(M, N, K, A, lda, B, ldb, C, ldc, dtype, tile, stages, parts, clock, clock_len, stream=None):
+    return _lib.pgemm_diag_parts(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, DTYPE_CODE.get(dtype, dtype),
+                                 int(tile[0]), int(tile[1]), int(tile[2]), int(stages), int(parts), _ptr(clock),
+                                 int(clock_len), _stream(stream))

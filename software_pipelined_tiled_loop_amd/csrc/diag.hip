@@ -75,7 +75,10 @@ struct DiagCfg {
 };
 
 template <int D>
-__global__ void __launch_bounds__(kThreads) mfma_ceiling_kernel(int iters, uint32_t seed, int zero, float* out) {
+__global__ void __launch_bounds__(kThreads) mfma_ceiling_kernel(int iters, uint32_t seed, int zero, float* out,
+                                                                long long* clock) {
+    const long long rt0 = (long long)__builtin_amdgcn_s_memrealtime();
+    const long long cy0 = (long long)__builtin_amdgcn_s_memtime();
     // 96 KiB of LDS that nothing but an impossible branch touches: it keeps
     // one workgroup per CU, so every SIMD holds exactly two of these waves.
     __shared__ char hold[98304];
@@ -105,6 +108,16 @@ __global__ void __launch_bounds__(kThreads) mfma_ceiling_kernel(int iters, uint3
 #pragma unroll
         for (int e = 0; e < 4; ++e) s += (float)acc[j][e];
     if ((threadIdx.x & 63) == 0) out[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = s;
+    if (clock != nullptr && threadIdx.x == 0) {
+        // wave 0's shader and 100 MHz clocks at its start and end
+        const long long cy1 = (long long)__builtin_amdgcn_s_memtime();
+        const long long rt1 = (long long)__builtin_amdgcn_s_memrealtime();
+        long long* o = clock + (int64_t)blockIdx.x * kClockWords;
+        o[0] = cy0;
+        o[1] = rt0;
+        o[2] = cy1;
+        o[3] = rt1;
+    }
 }
 
 // Flops of one mfma_block call.
@@ -182,6 +195,36 @@ static const ProbeVariant k_probes[] = {
     PGEMM_PROBE(DT_F32, 256, 256, 32, 1, 2, 4),  PGEMM_PROBE(DT_F32, 256, 256, 32, 2, 2, 4),
 };
 
+// The parts ladder: the GEMM kernel of a DIRECT class built with parts of
+// its steady state left out (PartsCfg), from the matrix cores alone up to
+// the whole K loop.
+struct PartsVariant {
+    int dtype, bm, bn, bk, stages, parts;
+    const void* fn;
+    int threads;
+};
+
+#define PGEMM_PARTS1(D, BM, BN, BK, S, WGM, WGN, PT)                                                              \
+    PartsVariant {                                                                                                 \
+        D, BM, BN, BK, S, PT,                                                                                      \
+            reinterpret_cast<const void*>(&gemm_kernel<PartsCfg<Cfg<D, BM, BN, BK, S, WGM, WGN, PROD_DIRECT>, PT>, false>), \
+            Cfg<D, BM, BN, BK, S, WGM, WGN, PROD_DIRECT>::NT                                                       \
+    }
+#define PGEMM_PARTS(D, BM, BN, BK, S, WGM, WGN)                                                                    \
+    PGEMM_PARTS1(D, BM, BN, BK, S, WGM, WGN, 0), PGEMM_PARTS1(D, BM, BN, BK, S, WGM, WGN, PART_AREADS),           \
+        PGEMM_PARTS1(D, BM, BN, BK, S, WGM, WGN, PART_BREADS),                                                     \
+        PGEMM_PARTS1(D, BM, BN, BK, S, WGM, WGN, PART_AREADS | PART_BREADS),                                       \
+        PGEMM_PARTS1(D, BM, BN, BK, S, WGM, WGN, PART_AREADS | PART_BREADS | PART_BARRIER),                        \
+        PGEMM_PARTS1(D, BM, BN, BK, S, WGM, WGN, PART_ALL)
+
+// The planner's 4096^3 classes.
+static const PartsVariant k_parts[] = {
+    PGEMM_PARTS(DT_BF16, 256, 256, 64, 2, 2, 4),
+    PGEMM_PARTS(DT_F16, 256, 256, 64, 2, 2, 4),
+    PGEMM_PARTS(DT_I8, 256, 256, 128, 2, 2, 4),
+    PGEMM_PARTS(DT_F32, 128, 64, 16, 2, 2, 2),
+};
+
 }  // namespace diag
 }  // namespace pgemm
 
@@ -189,17 +232,18 @@ using namespace pgemm;
 using namespace pgemm::diag;
 
 extern "C" int pgemm_diag_mfma_ceiling(int dtype, int zero_operands, int iters, int grid, uint32_t seed, float* out,
-                                       int64_t* flops, void* stream) {
+                                       int64_t* flops, int64_t* clock, void* stream) {
     if (dtype < 0 || dtype > 3) return PGEMM_ERR_UNSUPPORTED_DTYPE;
     if ((zero_operands != 0 && zero_operands != 1) || iters < 0 || iters > (1 << 24) || grid < 1 || grid > 65536 ||
-        out == nullptr || ((uintptr_t)out & 3) != 0)
+        out == nullptr || ((uintptr_t)out & 3) != 0 || ((uintptr_t)clock & 7) != 0)
         return PGEMM_ERR_INVALID_ARG;
     const void* fn = dtype == PGEMM_F32    ? reinterpret_cast<const void*>(&mfma_ceiling_kernel<DT_F32>)
                      : dtype == PGEMM_F16  ? reinterpret_cast<const void*>(&mfma_ceiling_kernel<DT_F16>)
                      : dtype == PGEMM_BF16 ? reinterpret_cast<const void*>(&mfma_ceiling_kernel<DT_BF16>)
                                            : reinterpret_cast<const void*>(&mfma_ceiling_kernel<DT_I8>);
     if (flops) *flops = (int64_t)grid * (kThreads / 64) * iters * kAcc * block_flops(dtype);
-    void* args[] = {&iters, &seed, &zero_operands, &out};
+    long long* clk = reinterpret_cast<long long*>(clock);
+    void* args[] = {&iters, &seed, &zero_operands, &out, &clk};
     const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, (hipStream_t)stream);
     if (e != hipSuccess) {
         std::fprintf(stderr, "pgemm: launch of the MFMA ceiling kernel failed: %s (%d)\n", hipGetErrorString(e), (int)e);
@@ -292,6 +336,57 @@ extern "C" int pgemm_diag_wait_profile(int64_t M, int64_t N, int64_t K, const vo
     const hipError_t e = hipLaunchKernel(v->fn, dim3(grid), dim3(v->threads), args, 0, (hipStream_t)stream);
     if (e != hipSuccess) {
         std::fprintf(stderr, "pgemm: launch of the wait-profile kernel failed: %s (%d)\n", hipGetErrorString(e),
+                     (int)e);
+        return PGEMM_ERR_HIP;
+    }
+    return PGEMM_OK;
+}
+
+extern "C" int pgemm_diag_parts(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                                int64_t ldb, void* C, int64_t ldc, int dtype, int tile_m, int tile_n, int tile_k,
+                                int stages, int parts, int64_t* clock, int64_t clock_len, void* stream) {
+    if (dtype < 0 || dtype > 3) return PGEMM_ERR_UNSUPPORTED_DTYPE;
+    if (M <= 0 || N <= 0 || K <= 0 || !A || !B || !C || lda < K || ldb < N || ldc < N || !clock ||
+        ((uintptr_t)clock & 7) != 0 || parts < 0 || parts > PART_ALL)
+        return PGEMM_ERR_INVALID_ARG;
+    const int es = dtype == PGEMM_F32 ? 4 : dtype == PGEMM_I8 ? 1 : 2;
+    if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || ((uintptr_t)C & 3) || (lda * es) % 16 || (ldb * es) % 16 ||
+        (K * es) % 16 || (N * es) % 16)
+        return PGEMM_ERR_INVALID_ARG;
+    if (M > 0x7fffff00 || N > 0x7fffff00 || K > 0x7fffff00 || (double)lda * es * 256.0 >= 2147483648.0 ||
+        (double)ldb * es * 128.0 >= 2147483648.0 || (double)ldc * 4.0 * 256.0 >= 2147483648.0)
+        return PGEMM_ERR_TOO_LARGE;
+    const PartsVariant* v = nullptr;
+    for (const PartsVariant& p : k_parts)
+        if (p.dtype == dtype && p.bm == tile_m && p.bn == tile_n && p.bk == tile_k && p.stages == stages &&
+            p.parts == parts)
+            v = &p;
+    if (!v) return PGEMM_ERR_INFEASIBLE_PLAN;
+    KernelArgs a{};
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.tiles_m = (int)((M + v->bm - 1) / v->bm);
+    a.tiles_n = (int)((N + v->bn - 1) / v->bn);
+    a.group_m = 4;
+    a.alpha = 1.0f;
+    a.ialpha = 1;
+    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+    if (tiles > 0x7ffffff0) return PGEMM_ERR_TOO_LARGE;
+    const int grid = (int)((tiles + 7) / 8 * 8);
+    // every workgroup with a tile writes kClockWords entries; idle ones write nothing
+    if (clock_len < (int64_t)grid * kClockWords) return PGEMM_ERR_INVALID_ARG;
+    a.probe = reinterpret_cast<long long*>(clock);
+    void* args[] = {&a};
+    const hipError_t e = hipLaunchKernel(v->fn, dim3(grid), dim3(v->threads), args, 0, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        std::fprintf(stderr, "pgemm: launch of the parts-ladder kernel failed: %s (%d)\n", hipGetErrorString(e),
                      (int)e);
         return PGEMM_ERR_HIP;
     }

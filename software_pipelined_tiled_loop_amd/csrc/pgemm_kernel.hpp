@@ -72,6 +72,10 @@ namespace pgemm {
 
 enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3 };
 enum Producer : int { PROD_DIRECT = 1, PROD_REGISTER = 2, PROD_GENERIC = 3, PROD_STAGED_A = 4, PROD_STAGED_B = 5 };
+// Parts of the steady state that a parts-ladder build (PartsCfg) can leave
+// out: the LDS-DMA pieces, the ready-edge barrier, the A and the B fragment
+// reads.
+enum Part : int { PART_DMA = 1, PART_BARRIER = 2, PART_AREADS = 4, PART_BREADS = 8, PART_ALL = 15 };
 
 struct KernelArgs {
     const void* A;
@@ -305,6 +309,11 @@ struct Cfg {
     // Wait-profile builds (ProbeCfg) stamp the shader clock around the waits
     // of every ready edge; the GEMM's own variants never do.
     static constexpr bool PROBE = false;
+    // Parts-ladder builds (PartsCfg) leave parts of the K loop out and stamp
+    // the clocks at the start and end of each workgroup; the GEMM's own
+    // variants run every part and stamp nothing.
+    static constexpr int PARTS = PART_ALL;
+    static constexpr bool CLOCK = false;
     static_assert(!MIXED || S == 2, "one producer per operand runs a two-stage ring");
 };
 
@@ -327,6 +336,26 @@ PGEMM_HD void b_chunk(int wave, int lane, int q, int& krow, int& nel) {
     const int pc = (lds_off % (C::BN * C::ES)) >> 4;
     nel = (pc ^ b_swz<C::Dt, C::NCH>(krow)) * C::EPC;
 }
+
+// A parts-ladder build of tile configuration C: the same kernel with parts
+// of its steady state left out (PARTS, a set of Part bits), for measuring
+// what each part costs.  Left-out LDS-DMA pieces leave the two stages holding
+// the prologue's K tiles (real operand data, so the matrix cores see the
+// same kind of values); left-out fragment reads leave the registers holding
+// the previous step's fragments (both fragment buffers start from operand
+// data); a left-out barrier keeps its s_waitcnt.
+// The prologue's ready edge always keeps its barrier.  Results are correct
+// only with every part in.  Wave 0 of each workgroup stamps the shader and
+// 100 MHz clocks at its start and after its last store (kClockWords).
+template <class Base, int PARTS_>
+struct PartsCfg : Base {
+    static constexpr int PARTS = PARTS_;
+    static constexpr bool CLOCK = true;
+};
+
+// Entries per workgroup of a parts-ladder build's clock output: shader clock
+// and 100 MHz clock at the start, then both after the last store.
+constexpr int kClockWords = 4;
 
 // A wait-profile build of tile configuration C: the same kernel, with shader
 // clock stamps around the vmcnt wait and the barrier of each ready edge
@@ -700,6 +729,14 @@ __device__ __forceinline__ void read_item(const char PGEMM_LDS* stage, int ks, i
     }
 }
 
+// Whether fragment read item r (read_item's order: items 0 and 2 .. FN are B
+// fragments, the others A) belongs to a part the build runs.
+template <class C>
+PGEMM_HD constexpr bool item_in_parts(int r) {
+    const bool is_b = r == 0 || (r >= 2 && r <= C::FN);
+    return (C::PARTS & (is_b ? PART_BREADS : PART_AREADS)) != 0;
+}
+
 template <class C>
 __device__ __forceinline__ void mfma_block(typename C::T::Acc& acc, const i32x4& a, const i32x4& b) {
     constexpr int D = C::Dt;
@@ -762,7 +799,7 @@ __device__ __forceinline__ void mfma_step(typename C::T::Acc (&acc)[C::FM][C::FN
 #pragma unroll
         for (int m = gi * GS; m < (gi + 1) * GS; ++m) mfma_block<C>(acc[m / C::FN][m % C::FN], use.a[m / C::FN], use.b[m % C::FN]);
         hook(gi);
-        if constexpr (DMA) {
+        if constexpr (DMA && (C::PARTS & PART_DMA) != 0) {
 #pragma unroll
             for (int p = gi * PPG; p < (gi + 1) * PPG; ++p)
                 if (p < NP) dma_piece<C, FULL>(g, d, C::DMA_P0 + p, wave, lane);
@@ -770,7 +807,7 @@ __device__ __forceinline__ void mfma_step(typename C::T::Acc (&acc)[C::FM][C::FN
         if constexpr (READS) {
 #pragma unroll
             for (int r = gi * RPG; r < (gi + 1) * RPG; ++r)
-                if (r < NR) read_item<C>(rstage, rks, r, wm0, wn0, lane, nxt);
+                if (r < NR && item_in_parts<C>(r)) read_item<C>(rstage, rks, r, wm0, wn0, lane, nxt);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -807,6 +844,13 @@ __device__ __forceinline__ void probed_barrier(Staging<C>& st) {
         st.bar += t2 - t1;
         if (READY && st.n == 0) st.rt_ready0 = (long long)__builtin_amdgcn_s_memrealtime();
         st.n += READY ? 1 : 0;
+    } else if constexpr ((C::PARTS & PART_BARRIER) == 0) {
+        // parts-ladder build without the barrier: the waits alone
+        lgkm_drain();
+        if constexpr (VM >= 0)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" : : "n"(VM) : "memory");
+        else
+            asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
     } else if constexpr (VM >= 0) {
         wait_barrier<(VM >= 0 ? VM : 0)>();
     } else {
@@ -1008,6 +1052,7 @@ __device__ __forceinline__ void pertile_loop(const KernelArgs& g, int m0, int n0
     }
     if constexpr (C::ANY_STAGED) issue_regs<C>(g, m0, n0, C::S - 1, st, wave, lane);
     sync_ring<C>(st);  // B_0
+    if constexpr ((C::PARTS & PART_BARRIER) == 0) lgkm_barrier();  // parts build: the prologue keeps its barrier
     // Stage S-1 has never been used: K tile S-1 goes there now (the staged
     // operand from registers, then the LDS-DMA pieces), then K tile S into
     // registers -- the order of every slot of the loop.
@@ -1015,6 +1060,11 @@ __device__ __forceinline__ void pertile_loop(const KernelArgs& g, int m0, int n0
     if constexpr (C::ANY_DMA) issue_dma<C>(g, m0, n0, C::S - 1, smem + (C::S - 1) * C::STAGE_BYTES, wave, lane);
     if constexpr (C::ANY_STAGED) issue_regs<C>(g, m0, n0, C::S, st, wave, lane);
     read_frags<C>(smem, 0, wm0, wn0, lane, f[0]);
+    // Parts build without some fragment reads: both fragment buffers start
+    // from operand data (K steps 0 and 1 of the first K tile), so the steps
+    // that keep stale fragments still multiply operand values, never
+    // uninitialised registers.
+    if constexpr (C::PARTS != PART_ALL) read_frags<C>(smem, 1 % NKS, wm0, wn0, lane, f[1]);
     int cur = 0;
     // Slots t < nfull load a whole K tile of a whole output tile by LDS-DMA
     // (issued without per-lane range selects); the rest, up to LD + 1 of
@@ -1278,7 +1328,8 @@ __global__ void __launch_bounds__(C::NT) gemm_kernel(KernelArgs g) {
     __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_BYTES];
     char PGEMM_LDS* smem = (char PGEMM_LDS*)smem_raw;
 
-    const long long rt_start = C::PROBE ? (long long)__builtin_amdgcn_s_memrealtime() : 0;
+    const long long rt_start = C::PROBE || C::CLOCK ? (long long)__builtin_amdgcn_s_memrealtime() : 0;
+    const long long cy_start = C::CLOCK ? (long long)__builtin_amdgcn_s_memtime() : 0;
     const WgTiles w = wg_tiles(g);
     if (w.count == 0) return;  // more workgroups than tiles in this XCD's range
     const int lane = threadIdx.x & 63;
@@ -1307,6 +1358,19 @@ __global__ void __launch_bounds__(C::NT) gemm_kernel(KernelArgs g) {
         }
         const long long rt_loop = C::PROBE ? (long long)__builtin_amdgcn_s_memrealtime() : 0;
         store_c<C>(g, m0, n0, wm0, wn0, lane, acc);
+        if constexpr (C::CLOCK) {
+            // parts-ladder build: wave 0's clocks at its start and after its stores
+            __builtin_amdgcn_s_waitcnt(0);
+            const long long cy_end = (long long)__builtin_amdgcn_s_memtime();
+            const long long rt_end = (long long)__builtin_amdgcn_s_memrealtime();
+            if (wave == 0 && lane == 0) {
+                long long* o = g.probe + (int64_t)blockIdx.x * kClockWords;
+                o[0] = cy_start;
+                o[1] = rt_start;
+                o[2] = cy_end;
+                o[3] = rt_end;
+            }
+        }
         if constexpr (C::PROBE) {
             // the wave's timeline on the 100 MHz clock: start, end of the K
             // loop, and its C stores complete

@@ -218,8 +218,8 @@ def test_torch_wrapper_validates_before_any_launch():
 
 
 def test_diagnostics_refuse_bad_arguments_before_any_launch():
-    """The two ceiling diagnostics validate everything on the host: dtype,
-    counts, output buffer, sizes, alignment and the compiled stream classes.
+    """The diagnostics validate everything on the host: dtype, counts, output
+    buffers, sizes, alignment and the compiled classes and ladder steps.
     The pointers are never dereferenced."""
     assert lib.pgemm_diag_mfma_ceiling(7, 0, 16, 256, 1, FAKE, stream=0)[0] == -2
     assert lib.pgemm_diag_mfma_ceiling("bf16", 2, 16, 256, 1, FAKE, stream=0)[0] == -1
@@ -237,6 +237,20 @@ def test_diagnostics_refuse_bad_arguments_before_any_launch():
     assert stream(K=0) == -1 and stream(lda=4095) == -1 and stream(A=FAKE + 2) == -1 and stream(N=4092) == -1
     assert stream(tile=(128, 128, 64)) == -4 and stream(stages=3) == -4
     assert stream(lda=1 << 24) == -7
+    assert lib.pgemm_diag_mfma_ceiling("bf16", 0, 16, 256, 1, FAKE, clock=FAKE + 4, stream=0)[0] == -1
+
+    def parts(**kw):
+        a = dict(dict(ok, C=FAKE, ldc=4096, parts=lib.PART_ALL, clock=FAKE, clock_len=256 * 4), **kw)
+        return lib.pgemm_diag_parts(a["M"], a["N"], a["K"], a["A"], a["lda"], a["B"], a["ldb"], a["C"], a["ldc"],
+                                    a["dtype"], a["tile"], a["stages"], a["parts"], a["clock"], a["clock_len"],
+                                    stream=0)
+    assert parts(dtype=9) == -2
+    assert parts(K=0) == -1 and parts(ldc=4095) == -1 and parts(C=FAKE + 2) == -1 and parts(clock=0) == -1
+    assert parts(clock=FAKE + 4) == -1 and parts(parts=16) == -1 and parts(parts=-1) == -1
+    assert parts(clock_len=256 * 4 - 1) == -1                   # one word short of grid * 4
+    assert parts(parts=lib.PART_DMA) == -4                       # not a compiled ladder step
+    assert parts(tile=(256, 256, 32)) == -4 and parts(stages=3) == -4
+    assert parts(lda=1 << 24) == -7
 
 
 def test_strerror_covers_every_status():

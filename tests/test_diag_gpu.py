@@ -6,7 +6,8 @@ These kernels are measurement tools, not part of the GEMM path; the bench's
 zero; random operands give finite sums (bf16/fp16/fp32, values in [-1, 1))
 that differ between seeds.  The LDS stream moves exactly the bytes it reports
 and reads only inside the operands (it runs on the 4096^3 workload and on a
-ragged-free small one)."""
+ragged-free small one).  The parts ladder's whole build computes exactly what
+the GEMM computes, and every step of the ladder runs and stamps its clocks."""
 import math
 
 import pytest
@@ -41,6 +42,13 @@ def test_mfma_ceiling_runs_and_keeps_its_accumulators(lib, dtype):
         sums.append(out.cpu())
     assert bool(torch.isfinite(sums[0]).all())
     assert not torch.equal(sums[0], sums[1])
+    clock = torch.zeros(grid * 4, dtype=torch.int64, device="cuda")
+    r, _ = lib.pgemm_diag_mfma_ceiling(dtype, 0, 4096, grid, 7, out, clock=clock)
+    assert r == 0
+    torch.cuda.synchronize()
+    c = clock.view(grid, 4).cpu().double()
+    ghz = (c[:, 2] - c[:, 0]) / ((c[:, 3] - c[:, 1]) / 100e6) / 1e9
+    assert bool((c[:, 3] > c[:, 1]).all()) and 0.3 < float(ghz.mean()) < 3.0
 
 
 @pytest.mark.parametrize("dtype,tile,stages", [("bf16", (256, 256, 64), 2), ("bf16", (256, 256, 32), 4),
@@ -97,3 +105,40 @@ def test_wait_profile_is_the_gemm_with_clock_stamps(lib, dtype, tile, stages):
     assert bool((v[..., 4] <= v[..., 7]).all()) and bool((v[..., 7] <= v[..., 5]).all())
     assert bool((v[..., 5] <= v[..., 6]).all()) and bool((v[..., 4] > 0).all())
     assert bool((buf.view(grid, nw, 8)[tiles:] == -1).all())         # idle workgroups write nothing
+
+
+LADDER = [0, 4, 8, 12, 14, 15]  # MFMA only, + A reads, B reads only, + both, + barrier, + LDS-DMA (the GEMM)
+
+
+@pytest.mark.parametrize("dtype,tile", [("bf16", (256, 256, 64)), ("f16", (256, 256, 64)), ("i8", (256, 256, 128)),
+                                        ("f32", (128, 64, 16))])
+def test_parts_ladder_whole_build_is_the_gemm_and_every_step_runs(lib, dtype, tile):
+    """The parts-ladder build with every part in computes exactly what the
+    GEMM's own DIRECT variant computes (same bits, on a shape with edge tiles
+    and several K tiles); every other step runs to completion on the same
+    operands and stamps a start and an end clock for each workgroup."""
+    from software_pipelined_tiled_loop_amd import inputs
+    M, N, K = 3 * tile[0] + 5, 2 * tile[1] + 16, 6 * tile[2]
+    print("[case] parts ladder", dtype, tile, (M, N, K), flush=True)
+    op = inputs.make_operands(dtype, M, N, K, seed=322, alpha=1.0, beta=0.0)
+    A, B = op.A.cuda(), op.B.cuda()
+    C1, C2 = op.C.cuda(), op.C.cuda()
+    tiles = math.ceil(M / tile[0]) * math.ceil(N / tile[1])
+    grid = math.ceil(tiles / 8) * 8
+    clock = torch.full((grid * 4,), -1, dtype=torch.int64, device="cuda")
+    r = lib.pgemm_gemm_ex(M, N, K, 1.0, A, op.lda, B, op.ldb, 0.0, C2, op.ldc, dtype, 2, lib._opts("direct", tile),
+                          None)
+    assert r == 0
+    for parts in LADDER:
+        print("[case] parts", parts, flush=True)
+        clock.fill_(-1)
+        r = lib.pgemm_diag_parts(M, N, K, A, op.lda, B, op.ldb, C1, op.ldc, dtype, tile, 2, parts, clock,
+                                 clock.numel())
+        assert r == 0, lib.pgemm_strerror(r)
+        torch.cuda.synchronize()
+        c = clock.view(grid, 4).cpu()
+        assert bool((c[:tiles, 2] > c[:tiles, 0]).all()) and bool((c[:tiles, 3] >= c[:tiles, 1]).all())
+        assert bool((c[tiles:] == -1).all())                         # idle workgroups write nothing
+        if parts == lib.PART_ALL:
+            same = bool(torch.equal(C1.view(torch.int32), C2.view(torch.int32)))
+            assert same
