@@ -807,7 +807,8 @@ def timeline(lib, torch, runs=20):
             if r != 0:
                 raise lib.PgemmError(r)
         _warm_then_run(call, torch, runs)
-        v = buf.view(grid, nw, 8)[:tiles, 0].cpu().numpy().astype(np.float64) / 100.0  # 100 MHz ticks -> us
+        raw = buf.view(grid, nw, 8)[:tiles, 0].cpu().numpy().astype(np.float64)
+        v = raw / 100.0  # 100 MHz ticks -> us
         start, loop_end, store_end, ready0 = v[:, 4], v[:, 5], v[:, 6], v[:, 7]
         t0 = start.min()
         med = lambda x: round(float(np.median(x)), 2)
@@ -818,6 +819,18 @@ def timeline(lib, torch, runs=20):
                       "start_us": [round(float(start.min() - t0), 2), round(float(start.max() - t0), 2)],
                       "k_loop_end_us": [round(float(loop_end.min() - t0), 2), round(float(loop_end.max() - t0), 2)],
                       "store_end_us": [round(float(store_end.min() - t0), 2), round(float(store_end.max() - t0), 2)]}
+        if tiles % 8 == 0:
+            # workgroup b runs on XCD b % 8: the same phases per XCD, and the
+            # shader clock over the K loop (shader cycles of the loop over its
+            # 100 MHz span, which starts at the wave's start)
+            ghz = raw[:, 3] / ((raw[:, 5] - raw[:, 4]) / 100e6) / 1e9
+            xcd = np.arange(tiles) % 8
+            out[label]["per_xcd"] = [
+                {"xcd": x, "median_prologue_us": med((ready0 - start)[xcd == x]),
+                 "median_k_loop_us": med((loop_end - ready0)[xcd == x]),
+                 "median_store_us": med((store_end - loop_end)[xcd == x]),
+                 "last_store_end_us": round(float(store_end[xcd == x].max() - t0), 2),
+                 "clock_ghz": round(float(np.mean(ghz[xcd == x])), 3)} for x in range(8)]
         del A, B, C, buf
     return out
 
