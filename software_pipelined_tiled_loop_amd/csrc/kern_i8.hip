@@ -19,6 +19,7 @@ static const VariantDesc k_table[] = {
     V(256, 256, 64, 1, 2, 4, PROD_GENERIC), V(256, 256, 64, 2, 2, 4, PROD_GENERIC),
     // one producer per operand: the misaligned operand through registers, the other by LDS-DMA
     V(256, 256, 64, 2, 2, 4, PROD_STAGED_A),  V(256, 256, 64, 2, 2, 4, PROD_STAGED_B),
+    V(256, 256, 128, 2, 2, 4, PROD_STAGED_A), V(256, 256, 128, 2, 2, 4, PROD_STAGED_B),
 };
 #undef V
 
