@@ -265,6 +265,15 @@ def _misaligned_problem(dt, which):
     return inputs.make_operands(dt, 4000, 3969, 4000, seed=inputs.seed_for("bf16_k_sweep", 11), lda=4000, ldb=3969)
 
 
+def rounds_units(lib, dt, o, tile, S):
+    """Rounds of co-resident workgroups and workgroup-units on the busiest CU
+    for problem o with DIRECT tile class `tile` at depth S."""
+    p = plan_of(lib, dt, o.M, o.N, o.K, S, "direct", tile)
+    n = -(-(-(-o.M // tile[0]) * -(-o.N // tile[1])) // 256)   # tiles on the busiest CU
+    occ = p["wg_per_cu"]
+    return -(-n // occ), (n // occ) * occ + n % occ
+
+
 def retune(lib, torch, out_path):
     """Time every compiled variant on the problems behind each planner
     constant and write planner_tables.json to out_path (copy it into the
@@ -273,16 +282,15 @@ def retune(lib, torch, out_path):
     from software_pipelined_tiled_loop_amd import inputs
     old = bld.load_tables()
     log = {}
-    # Per DIRECT tile class: the cost of a K tile, the fixed cost of the
-    # first round of workgroups (prologue with cold first loads, epilogue and
-    # C store) and of each later round (whose start overlaps the previous
-    # round's tail), from three problems -- 4096 x 4096 outputs at K = 4096
-    # and K = 256, 8192 x 8192 at K = 128 -- each with the depth the planner
-    # gives the class; the model is
+    # Per DIRECT tile class: the fixed cost of the first round of workgroups
+    # (prologue with cold first loads, epilogue and C store) and of each later
+    # round (whose start overlaps the previous round's tail), fitted at the
+    # class's fastest depth from three problems -- 4096 x 4096 outputs at
+    # K = 4096 and K = 256, 8192 x 8192 at K = 128; per ring depth of the
+    # class, the cost of a K tile from that depth's 4096^3 time; the model is
     #   cycles = first_round + (rounds - 1) * round + units * (2*BM*BN*K) / (eff * dense flops per CU-clock)
     # (the partial-round cost lam from one workgroup per CU against a full
-    # round of co-resident ones, at the shallowest ring that lets two or more
-    # share a CU).
+    # round of co-resident ones, at that depth, when two or more fit).
     classes = []
     for dt in ("f32", "f16", "bf16", "i8"):
         by_class = {}
@@ -298,45 +306,50 @@ def retune(lib, torch, out_path):
         wide = inputs.make_operands(dt, 8192, 8192, 128, seed=inputs.seed_for("bf16_k_sweep", 6))
         probs = [(o,) + _device(o) for o in (op, short, wide)]
         import numpy as np
-        for tile, by_s in sorted(by_class.items()):
+        fpc = {"f32": 64.0, "i8": 2048.0}.get(dt, 1024.0)
+
+        def fit_points(tile, S):
             pts = []
             for o, a, b, c in probs:
-                ms = time_gemm(lib, o, a, b, c, producer="direct", tile=tile)
-                p = plan_of(lib, dt, o.M, o.N, o.K, 0, "direct", tile)
-                n = -(-(-(-o.M // tile[0]) * -(-o.N // tile[1])) // 256)   # tiles on the busiest CU
-                occ = p["wg_per_cu"]
-                r = -(-n // occ)
-                full, part = n // occ, n % occ
-                lam_guess = 0.0
-                units = full * occ + (part + lam_guess * (occ - part) if part else 0)
-                pts.append((o.K, ms * 1e-3 * 2.4e9, r, units))
-            # t = units * k * c + first + (rounds - 1) * later, at the three points
+                ms = time_gemm(lib, o, a, b, c, stages=S, producer="direct", tile=tile)
+                pts.append((o.K, ms * 1e-3 * 2.4e9) + rounds_units(lib, dt, o, tile, S))
+            return pts
+
+        for tile, by_s in sorted(by_class.items()):
+            # fixed costs from the depth that runs 4096^3 fastest: three
+            # problems, t = units * K * c + first + (rounds - 1) * later
+            s_ref = max(by_s, key=lambda S: by_s[S])
+            pts = fit_points(tile, s_ref)
             mat = np.array([[u * k, 1.0, r - 1.0] for k, t, r, u in pts])
             rhs = np.array([t for k, t, r, u in pts])
             c_k, first, later = np.linalg.solve(mat, rhs)
             first, round_cycles = max(0.0, float(first)), max(0.0, float(later))
-            (k1, t1, r1, u1), (k2, t2, r2, u2) = pts[:2]
-            fpc = {"f32": 64.0, "i8": 2048.0}.get(dt, 1024.0)
-            eff = 2.0 * tile[0] * tile[1] / (c_k * 4.0 * fpc)
-            lam, occ, s_lam = 0.0, 1, min(by_s)
             for S in sorted(by_s):
+                # each depth's K-tile cost from its own 4096^3 time, with the
+                # class's fixed costs
+                r4, u4 = rounds_units(lib, dt, op, tile, S)
+                t4 = 2.0 * op.M * op.N * op.K / (by_s[S] * 1e12) * 2.4e9
+                c_s = (t4 - first - (r4 - 1) * round_cycles) / (u4 * op.K)
+                eff = 2.0 * tile[0] * tile[1] / (max(c_s, 1e-9) * 4.0 * fpc)
+                # partial last round: one workgroup per CU against a full
+                # round of co-resident ones at this depth
                 r, p1 = lib.pgemm_plan(16 * tile[0], 16 * tile[1], 4096, dt, S, 1, {"tile": tile, "producer": "direct"})
-                if S > 1 and p1["wg_per_cu"] >= 2:
-                    occ, s_lam = p1["wg_per_cu"], S
-                    break
-            if occ >= 2:
-                t = {}
-                for rows in (16 * tile[0], 16 * tile[0] * occ):
-                    o = inputs.make_operands(dt, rows, 16 * tile[1], 4096, seed=77)
-                    a, b, c = _device(o)
-                    t[rows] = time_gemm(lib, o, a, b, c, stages=s_lam, producer="direct", tile=tile)
-                    del a, b, c
-                lam = min(1.0, max(0.0, (occ * t[16 * tile[0]] / t[16 * tile[0] * occ] - 1.0) / (occ - 1)))
-            classes.append({"dtype": dt, "tile": list(tile), "eff": round(min(eff, 1.0), 4), "lam": round(lam, 3),
-                            "first_round_cycles": round(first, 0), "round_cycles": round(round_cycles, 0)})
-            log["%s %dx%dx%d" % (dt, *tile)] = {"tflops_4096_by_depth": {k: round(v, 1) for k, v in sorted(by_s.items())},
-                                               "fit_points_K_cycles_rounds_units": [[k, round(t), r, u] for k, t, r, u in pts],
-                                               "partial_round": {"workgroups_per_cu": occ, "stages": s_lam}}
+                occ, lam = p1["wg_per_cu"], 0.0
+                if occ >= 2:
+                    t = {}
+                    for rows in (16 * tile[0], 16 * tile[0] * occ):
+                        o = inputs.make_operands(dt, rows, 16 * tile[1], 4096, seed=77)
+                        a, b, c = _device(o)
+                        t[rows] = time_gemm(lib, o, a, b, c, stages=S, producer="direct", tile=tile)
+                        del a, b, c
+                    lam = min(1.0, max(0.0, (occ * t[16 * tile[0]] / t[16 * tile[0] * occ] - 1.0) / (occ - 1)))
+                classes.append({"dtype": dt, "tile": list(tile), "stages": S, "eff": round(min(max(eff, 0.06), 1.0), 4),
+                                "lam": round(lam, 3), "first_round_cycles": round(first, 0),
+                                "round_cycles": round(round_cycles, 0)})
+                log["%s %dx%dx%d s%d" % (dt, *tile, S)] = {"tflops_4096": round(by_s[S], 1),
+                                                          "partial_round_workgroups_per_cu": occ}
+            log["%s %dx%dx%d" % (dt, *tile)] = {"fit_depth": s_ref,
+                                               "fit_points_K_cycles_rounds_units": [[k, round(t), r, u] for k, t, r, u in pts]}
         del probs
     # register-staged variants
     staged = []
@@ -367,8 +380,8 @@ def retune(lib, torch, out_path):
 
 
 def planner_check(lib, torch):
-    """For each check shape: the planner's plan against every DIRECT tile
-    class (each at the depth the planner gives it), best measured over
+    """For each check shape: the planner's plan against every compiled DIRECT
+    variant (every tile class at every ring depth), best measured over the
     planner's pick."""
     from software_pipelined_tiled_loop_amd import inputs
     out = {}
@@ -378,11 +391,14 @@ def planner_check(lib, torch):
         auto = _tflops_of(lib, op, A, B, C)
         plan = plan_label(plan_of(lib, dt, M, N, K))
         best, best_label = 0.0, None
-        tiles = sorted({(v["tile_m"], v["tile_n"], v["tile_k"]) for v in _variants_of(lib, dt) if v["producer"] == "direct"})
+        variants = sorted({((v["tile_m"], v["tile_n"], v["tile_k"]), v["stages"]) for v in _variants_of(lib, dt)
+                           if v["producer"] == "direct"})
         per = {}
-        for tile in tiles:
-            t = _tflops_of(lib, op, A, B, C, 0, "direct", tile)
-            lab = plan_label(plan_of(lib, dt, M, N, K, 0, "direct", tile))
+        for tile, S in variants:
+            lab = plan_label(plan_of(lib, dt, M, N, K, S, "direct", tile))
+            if lab in per:
+                continue  # a depth beyond the number of K tiles runs as a shallower one
+            t = _tflops_of(lib, op, A, B, C, S, "direct", tile)
             per[lab] = round(t, 1)
             if t > best:
                 best, best_label = t, lab
