@@ -419,7 +419,7 @@ def main():
     ap.add_argument("--workload", default="f32", choices=sorted(WORKLOADS),
                     help="timed workload (default: the fp32 4096^3 headline); others are for profiling")
     ap.add_argument("--stages", type=int, default=0, help="ring depth (0 = planner)")
-    ap.add_argument("--producer", default=None, choices=[None, "direct", "register", "generic"])
+    ap.add_argument("--producer", default=None, choices=[None, "direct", "register", "generic", "staged_a", "staged_b"])
     ap.add_argument("--tile", default=None, help="BMxBNxBK, e.g. 256x256x32")
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed calls before the warm-up, for this long, so the clock has settled (0 = off)")
