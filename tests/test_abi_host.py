@@ -399,3 +399,15 @@ def test_planner_tables_cover_every_compiled_variant():
         assert r["round_cycles"] >= 0 and r["first_round_cycles"] >= 0, r
     inc = open(os.path.join(build.GEN_DIR, "planner_tables.inc")).read()
     assert inc == build.tables_include(t)
+
+
+def test_planner_tables_were_measured_on_these_kernel_sources():
+    """planner_tables.json records the kernel source hash (kernel code,
+    comments stripped, and the code-generation flags) it was measured on;
+    after any kernel change the tables must be measured again (bench.py
+    --retune) before they are trusted, as page "Double Buffering: Software
+    Pipelining the K-Loop", section "What Could Be Improved", asks of the
+    tile search."""
+    import bench
+    from software_pipelined_tiled_loop_amd import build
+    assert build.load_tables()["kernel_source_hash"] == bench.kernel_source_hash()
