@@ -652,7 +652,8 @@ STREAM_POINTS = (("bf16", (256, 256, 64), 2), ("f16", (256, 256, 64), 2), ("i8",
 
 def ceilings(lib, torch):
     """The two diagnostics that bound the GEMM (pgemm_diag_*): the matrix
-    cores alone on random and on zero operands (% of dense peak), and the
+    cores alone on random and on zero operands (% of dense peak; also with
+    one wave per SIMD and with 32x32 blocks), and the
     producer alone -- the LDS-DMA pieces of a tile class on the 4096^3
     workload with no arithmetic -- as LDS bytes per second and as the GEMM
     rate it could feed (2MNK over its time)."""
@@ -676,6 +677,26 @@ def ceilings(lib, torch):
             row["zero" if zero else "random"] = {"tflops": round(t, 1), "pct_peak": round(100 * t / PEAK[dt], 1),
                                                  "clock_ghz": clock_ghz(clock, grid)}
         out["mfma_only"][dt] = row
+    # one wave per SIMD against two, 16x16 blocks against 32x32 ones: what a
+    # single issuing wave keeps busy, and what each block shape costs in clock
+    out["mfma_issue"] = {}
+    for dt in ("f16", "bf16", "i8"):
+        row = {}
+        for waves, blk in ((2, 16), (1, 16), (2, 32), (1, 32)):
+            for zero in (0, 1):
+                box = {}
+
+                def call():
+                    r, box["flops"] = lib.pgemm_diag_mfma_ceiling(dt, zero, CEILING_ITERS[dt], grid, 12345, buf,
+                                                                  clock=clock, waves_per_simd=waves, block=blk)
+                    if r != 0:
+                        raise lib.PgemmError(r)
+
+                ms = time_calls(call)
+                t = box["flops"] / (ms * 1e-3) / 1e12
+                row["%dx%d %d wave%s/SIMD %s" % (blk, blk, waves, "s" if waves > 1 else "", "zero" if zero else "random")] = {
+                    "tflops": round(t, 1), "pct_peak": round(100 * t / PEAK[dt], 1), "clock_ghz": clock_ghz(clock, grid)}
+        out["mfma_issue"][dt] = row
     for wl, tile, S in STREAM_POINTS:
         op = workload_operands(wl)
         A, B = op.A.cuda(), op.B.cuda()

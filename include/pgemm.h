@@ -294,21 +294,24 @@ int pgemm_hazard_copy_reduce(const int32_t* X, int64_t rows, int64_t cols, int64
  * four stages", last point: a timing difference alone does not show the
  * cause).  Neither is part of the GEMM path.
  *
- * pgemm_diag_mfma_ceiling: the matrix cores alone.  `grid` workgroups of
- * eight waves (one workgroup per CU, two waves per SIMD) each run `iters`
- * rounds of 16 independent MFMA blocks of the dtype (bf16/fp16
- * 16x16x32, int8 16x16x64, fp32 four 16x16x4) on operands drawn from a
- * hash of `seed` and the lane (random values in [-1, 1), or any int8), or on
- * zeros when zero_operands = 1.  No memory traffic besides one float per wave
- * written to out[grid * 8] (device memory owned by the caller, 4-byte
- * aligned), which keeps the accumulators live.  *flops (optional) receives
- * the flops of the launch.  `clock` (optional, device memory, 8-byte
- * aligned, grid * 4 entries) receives per workgroup the shader clock and
- * the constant 100 MHz clock (s_memtime, s_memrealtime) of wave 0 at its
- * start, then both at its end: the shader clock's rate under this load.
- * Asynchronous on `stream`.  Errors: UNSUPPORTED_DTYPE; INVALID_ARG for
- * iters outside 0..2^24, grid outside 1..65536 or a bad `out` or `clock`;
- * HIP for a rejected launch.
+ * pgemm_diag_mfma_ceiling: the matrix cores alone.  `grid` workgroups
+ * (one per CU) of waves_per_simd (1 or 2) waves per SIMD each run `iters`
+ * rounds of independent MFMA blocks of the dtype: block = 16 gives sixteen
+ * 16x16 blocks per round, the GEMM's own (bf16/fp16 16x16x32, int8 16x16x64,
+ * fp32 four 16x16x4); block = 32 gives eight 32x32 blocks of the same flops
+ * (bf16/fp16 32x32x16, int8 32x32x32; not for fp32).  Operands come from a
+ * hash of `seed` and the lane (random values in [-1, 1), or any int8), or
+ * are zeros when zero_operands = 1.  No memory traffic besides one float per
+ * wave written to out[grid * 4 * waves_per_simd] (device memory owned by
+ * the caller, 4-byte aligned), which keeps the accumulators live.  *flops
+ * (optional) receives the flops of the launch.  `clock` (optional, device
+ * memory, 8-byte aligned, grid * 4 entries) receives per workgroup the
+ * shader clock and the constant 100 MHz clock (s_memtime, s_memrealtime) of
+ * wave 0 at its start, then both at its end: the shader clock's rate under
+ * this load.  Asynchronous on `stream`.  Errors: UNSUPPORTED_DTYPE;
+ * INVALID_ARG for waves_per_simd not 1 or 2, block not 16 or 32 (or 32 for
+ * fp32), iters outside 0..2^24, grid outside 1..65536 or a bad `out` or
+ * `clock`; HIP for a rejected launch.
  *
  * pgemm_diag_lds_stream: the producer alone.  For the compiled stream of tile
  * class (tile_m, tile_n, tile_k) at ring depth `stages` it issues exactly the
@@ -346,8 +349,9 @@ int pgemm_diag_wait_profile(int64_t M, int64_t N, int64_t K, const void* A, int6
                             const void* B, int64_t ldb, void* C, int64_t ldc, int dtype,
                             int tile_m, int tile_n, int tile_k, int stages, int64_t* out,
                             int64_t out_len, void* stream);
-int pgemm_diag_mfma_ceiling(int dtype, int zero_operands, int iters, int grid, uint32_t seed,
-                            float* out, int64_t* flops, int64_t* clock, void* stream);
+int pgemm_diag_mfma_ceiling(int dtype, int zero_operands, int waves_per_simd, int block, int iters,
+                            int grid, uint32_t seed, float* out, int64_t* flops, int64_t* clock,
+                            void* stream);
 int pgemm_diag_lds_stream(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                           const void* B, int64_t ldb, int dtype, int tile_m, int tile_n,
                           int tile_k, int stages, int64_t* lds_bytes, void* stream);

@@ -89,7 +89,8 @@ _lib.pgemm_model_compute_load_ratio.argtypes = [_int, _int, _int, _int]
 _lib.pgemm_model_compute_load_ratio.restype = _dbl
 _lib.pgemm_hazard_copy_reduce.argtypes = [_vp, _i64, _i64, _i64, _vp, _int, _int, _int, _vp, _i64, _int, _vp]
 _lib.pgemm_hazard_copy_reduce.restype = _int
-_lib.pgemm_diag_mfma_ceiling.argtypes = [_int, _int, _int, _int, ctypes.c_uint32, _vp, ctypes.POINTER(_i64), _vp, _vp]
+_lib.pgemm_diag_mfma_ceiling.argtypes = [_int, _int, _int, _int, _int, _int, ctypes.c_uint32, _vp, ctypes.POINTER(_i64),
+                                         _vp, _vp]
 _lib.pgemm_diag_mfma_ceiling.restype = _int
 _lib.pgemm_diag_lds_stream.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _int, _int, _int, _int, _int,
                                        ctypes.POINTER(_i64), _vp]
@@ -259,12 +260,13 @@ def pgemm_hazard_copy_reduce(X, rows, cols, ldx, row_sums, reuse_wait, delay_wav
                                          _stream(stream))
 
 
-def pgemm_diag_mfma_ceiling(dtype, zero_operands, iters, grid, seed, out, clock=None, stream=None):
+def pgemm_diag_mfma_ceiling(dtype, zero_operands, iters, grid, seed, out, clock=None, stream=None, waves_per_simd=2,
+                            block=16):
     """Returns (status, flops of the launch)."""
     fl = _i64(0)
-    r = _lib.pgemm_diag_mfma_ceiling(DTYPE_CODE.get(dtype, dtype), int(zero_operands), int(iters), int(grid),
-                                     int(seed) & 0xFFFFFFFF, _ptr(out), ctypes.byref(fl), _ptr(clock),
-                                     _stream(stream))
+    r = _lib.pgemm_diag_mfma_ceiling(DTYPE_CODE.get(dtype, dtype), int(zero_operands), int(waves_per_simd), int(block),
+                                     int(iters), int(grid), int(seed) & 0xFFFFFFFF, _ptr(out), ctypes.byref(fl),
+                                     _ptr(clock), _stream(stream))
     return r, fl.value
 
 

@@ -7,11 +7,14 @@
 // difference alone does not show the cause; these measure the two resources
 // whose limits set the GEMM's ceiling on this part:
 //
-//   mfma_ceiling_kernel  the matrix cores alone: every SIMD runs two waves of
-//                        back-to-back MFMAs on 16 independent accumulators,
-//                        operands from random (or zero) register data, no
-//                        memory traffic.  Random operands draw more power than
-//                        zeros, and the part lowers its clock for them.
+//   mfma_ceiling_kernel  the matrix cores alone: every SIMD runs two waves (or
+//                        one) of back-to-back MFMAs on independent
+//                        accumulators, 16x16 blocks (the GEMM's) or 32x32
+//                        blocks, operands from random (or zero) register
+//                        data, no memory traffic.  Random operands draw more
+//                        power than zeros, and the part lowers its clock for
+//                        them; one wave per SIMD shows what a single issuing
+//                        wave can keep busy.
 //   lds_stream_kernel    the producer alone: the exact LDS-DMA pieces of a
 //                        GEMM tile class (same raster, same 1-KiB blocks,
 //                        same ring depth and ready barrier per K tile), no
@@ -33,8 +36,7 @@
 namespace pgemm {
 namespace diag {
 
-constexpr int kThreads = 512;  // eight waves: two per SIMD
-constexpr int kAcc = 16;       // independent accumulators per wave
+constexpr int kAcc = 16;  // independent 16x16 accumulators per wave (eight 32x32 ones: the same flops)
 
 // 32-bit integer mixing function (the MurmurHash3 finalizer).
 __device__ __forceinline__ uint32_t mix32(uint32_t x) {
@@ -74,13 +76,41 @@ struct DiagCfg {
     typedef Traits<D> T;
 };
 
+// Accumulator of a 32x32 MFMA block: 16 values per lane.
 template <int D>
-__global__ void __launch_bounds__(kThreads) mfma_ceiling_kernel(int iters, uint32_t seed, int zero, float* out,
-                                                                long long* clock) {
+struct Acc32 {
+    typedef __attribute__((ext_vector_type(16))) float T;
+};
+template <>
+struct Acc32<DT_I8> {
+    typedef __attribute__((ext_vector_type(16))) int T;
+};
+
+// One 32x32 MFMA block (K 16 for fp16/bf16, 32 for int8): twice the flops of
+// the 16x16 block of mfma_block.
+template <int D>
+__device__ __forceinline__ void mfma_block32(typename Acc32<D>::T& acc, const i32x4& a, const i32x4& b) {
+    if constexpr (D == DT_BF16) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc, 0,
+                                                      0, 0);
+    } else if constexpr (D == DT_F16) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0, 0,
+                                                     0);
+    } else {
+        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc, 0, 0, 0);
+    }
+}
+
+// NT threads (NT / 256 waves per SIMD), BLK: 16 (sixteen 16x16 accumulators)
+// or 32 (eight 32x32 ones, fp16/bf16/int8 only).
+template <int D, int NT, int BLK>
+__global__ void __launch_bounds__(NT) mfma_ceiling_kernel(int iters, uint32_t seed, int zero, float* out,
+                                                          long long* clock) {
     const long long rt0 = (long long)__builtin_amdgcn_s_memrealtime();
     const long long cy0 = (long long)__builtin_amdgcn_s_memtime();
     // 96 KiB of LDS that nothing but an impossible branch touches: it keeps
-    // one workgroup per CU, so every SIMD holds exactly two of these waves.
+    // one workgroup per CU, so every SIMD holds exactly NT / 256 of these
+    // waves.
     __shared__ char hold[98304];
     if (iters < 0) hold[threadIdx.x] = 0;
     typedef typename Traits<D>::Acc Acc;
@@ -94,20 +124,35 @@ __global__ void __launch_bounds__(kThreads) mfma_ceiling_kernel(int iters, uint3
             a[q][e] = zero ? 0 : operand_word<D>(mix32(k), mix32(k ^ 0x5bd1e995u));
             b[q][e] = zero ? 0 : operand_word<D>(mix32(k + 1u), mix32((k + 1u) ^ 0x5bd1e995u));
         }
-    Acc acc[kAcc];
-#pragma unroll
-    for (int j = 0; j < kAcc; ++j) acc[j] = Acc{0, 0, 0, 0};
-    for (int it = 0; it < iters; ++it) {
-#pragma unroll
-        for (int j = 0; j < kAcc; ++j) mfma_block<DiagCfg<D>>(acc[j], a[j & 3], b[j >> 2]);
-    }
-    // keep every accumulator live: one value per wave
     float s = 0.0f;
+    if constexpr (BLK == 16) {
+        Acc acc[kAcc];
 #pragma unroll
-    for (int j = 0; j < kAcc; ++j)
+        for (int j = 0; j < kAcc; ++j) acc[j] = Acc{0, 0, 0, 0};
+        for (int it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s += (float)acc[j][e];
-    if ((threadIdx.x & 63) == 0) out[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = s;
+            for (int j = 0; j < kAcc; ++j) mfma_block<DiagCfg<D>>(acc[j], a[j & 3], b[j >> 2]);
+        }
+        // keep every accumulator live: one value per wave
+#pragma unroll
+        for (int j = 0; j < kAcc; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s += (float)acc[j][e];
+    } else {
+        typedef typename Acc32<D>::T A32;
+        A32 acc[kAcc / 2];
+#pragma unroll
+        for (int j = 0; j < kAcc / 2; ++j) acc[j] = A32{};
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < kAcc / 2; ++j) mfma_block32<D>(acc[j], a[j & 3], b[j >> 2]);
+        }
+#pragma unroll
+        for (int j = 0; j < kAcc / 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s += (float)acc[j][e];
+    }
+    if ((threadIdx.x & 63) == 0) out[blockIdx.x * (NT / 64) + (threadIdx.x >> 6)] = s;
     if (clock != nullptr && threadIdx.x == 0) {
         // wave 0's shader and 100 MHz clocks at its start and end
         const long long cy1 = (long long)__builtin_amdgcn_s_memtime();
@@ -231,20 +276,38 @@ static const PartsVariant k_parts[] = {
 using namespace pgemm;
 using namespace pgemm::diag;
 
-extern "C" int pgemm_diag_mfma_ceiling(int dtype, int zero_operands, int iters, int grid, uint32_t seed, float* out,
-                                       int64_t* flops, int64_t* clock, void* stream) {
+template <int D, int NT>
+static const void* ceiling_fn(int block) {
+    if constexpr (D == DT_F32) {
+        return reinterpret_cast<const void*>(&mfma_ceiling_kernel<D, NT, 16>);
+    } else {
+        return block == 32 ? reinterpret_cast<const void*>(&mfma_ceiling_kernel<D, NT, 32>)
+                           : reinterpret_cast<const void*>(&mfma_ceiling_kernel<D, NT, 16>);
+    }
+}
+
+template <int NT>
+static const void* ceiling_fn(int dtype, int block) {
+    return dtype == PGEMM_F32    ? ceiling_fn<DT_F32, NT>(block)
+           : dtype == PGEMM_F16  ? ceiling_fn<DT_F16, NT>(block)
+           : dtype == PGEMM_BF16 ? ceiling_fn<DT_BF16, NT>(block)
+                                 : ceiling_fn<DT_I8, NT>(block);
+}
+
+extern "C" int pgemm_diag_mfma_ceiling(int dtype, int zero_operands, int waves_per_simd, int block, int iters,
+                                       int grid, uint32_t seed, float* out, int64_t* flops, int64_t* clock,
+                                       void* stream) {
     if (dtype < 0 || dtype > 3) return PGEMM_ERR_UNSUPPORTED_DTYPE;
-    if ((zero_operands != 0 && zero_operands != 1) || iters < 0 || iters > (1 << 24) || grid < 1 || grid > 65536 ||
-        out == nullptr || ((uintptr_t)out & 3) != 0 || ((uintptr_t)clock & 7) != 0)
+    if ((zero_operands != 0 && zero_operands != 1) || (waves_per_simd != 1 && waves_per_simd != 2) ||
+        (block != 16 && block != 32) || (block == 32 && dtype == PGEMM_F32) || iters < 0 || iters > (1 << 24) ||
+        grid < 1 || grid > 65536 || out == nullptr || ((uintptr_t)out & 3) != 0 || ((uintptr_t)clock & 7) != 0)
         return PGEMM_ERR_INVALID_ARG;
-    const void* fn = dtype == PGEMM_F32    ? reinterpret_cast<const void*>(&mfma_ceiling_kernel<DT_F32>)
-                     : dtype == PGEMM_F16  ? reinterpret_cast<const void*>(&mfma_ceiling_kernel<DT_F16>)
-                     : dtype == PGEMM_BF16 ? reinterpret_cast<const void*>(&mfma_ceiling_kernel<DT_BF16>)
-                                           : reinterpret_cast<const void*>(&mfma_ceiling_kernel<DT_I8>);
-    if (flops) *flops = (int64_t)grid * (kThreads / 64) * iters * kAcc * block_flops(dtype);
+    const int threads = 256 * waves_per_simd;
+    const void* fn = waves_per_simd == 1 ? ceiling_fn<256>(dtype, block) : ceiling_fn<512>(dtype, block);
+    if (flops) *flops = (int64_t)grid * (threads / 64) * iters * kAcc * block_flops(dtype);
     long long* clk = reinterpret_cast<long long*>(clock);
     void* args[] = {&iters, &seed, &zero_operands, &out, &clk};
-    const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, (hipStream_t)stream);
+    const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, (hipStream_t)stream);
     if (e != hipSuccess) {
         std::fprintf(stderr, "pgemm: launch of the MFMA ceiling kernel failed: %s (%d)\n", hipGetErrorString(e), (int)e);
         return PGEMM_ERR_HIP;

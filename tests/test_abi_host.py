@@ -235,6 +235,10 @@ def test_diagnostics_refuse_bad_arguments_before_any_launch():
     assert lib.pgemm_diag_mfma_ceiling("bf16", 0, 16, 0, 1, FAKE, stream=0)[0] == -1
     assert lib.pgemm_diag_mfma_ceiling("bf16", 0, 16, 256, 1, 0, stream=0)[0] == -1
     assert lib.pgemm_diag_mfma_ceiling("bf16", 0, 16, 256, 1, FAKE + 2, stream=0)[0] == -1
+    assert lib.pgemm_diag_mfma_ceiling("bf16", 0, 16, 256, 1, FAKE, stream=0, waves_per_simd=3)[0] == -1
+    assert lib.pgemm_diag_mfma_ceiling("bf16", 0, 16, 256, 1, FAKE, stream=0, waves_per_simd=0)[0] == -1
+    assert lib.pgemm_diag_mfma_ceiling("bf16", 0, 16, 256, 1, FAKE, stream=0, block=8)[0] == -1
+    assert lib.pgemm_diag_mfma_ceiling("f32", 0, 16, 256, 1, FAKE, stream=0, block=32)[0] == -1
     ok = dict(M=4096, N=4096, K=4096, A=FAKE, lda=4096, B=FAKE, ldb=4096, dtype="bf16", tile=(256, 256, 64), stages=2)
 
     def stream(**kw):

@@ -51,6 +51,30 @@ def test_mfma_ceiling_runs_and_keeps_its_accumulators(lib, dtype):
     assert bool((c[:, 3] > c[:, 1]).all()) and 0.3 < float(ghz.mean()) < 3.0
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("waves,block", [(1, 16), (2, 32), (1, 32)])
+def test_mfma_ceiling_variants_run_with_the_same_flops(lib, dtype, waves, block):
+    print("[case] mfma ceiling variant", dtype, waves, block, flush=True)
+    grid = 256
+    nw = grid * 4 * waves
+    out = torch.full((grid * 8,), float("nan"), dtype=torch.float32, device="cuda")
+    r, flops = lib.pgemm_diag_mfma_ceiling(dtype, 1, 64, grid, 7, out, waves_per_simd=waves, block=block)
+    assert r == 0
+    torch.cuda.synchronize()
+    host = out.cpu()
+    assert bool((host[:nw] == 0).all()) and bool(torch.isnan(host[nw:]).all())
+    per_block = {"f16": 16384, "bf16": 16384, "i8": 32768}[dtype]
+    assert flops == nw * 64 * 16 * per_block
+    sums = []
+    for seed in (7, 8):
+        r, _ = lib.pgemm_diag_mfma_ceiling(dtype, 0, 64, grid, seed, out, waves_per_simd=waves, block=block)
+        assert r == 0
+        torch.cuda.synchronize()
+        sums.append(out[:nw].cpu())
+    assert bool(torch.isfinite(sums[0]).all())
+    assert not torch.equal(sums[0], sums[1])
+
+
 @pytest.mark.parametrize("dtype,tile,stages", [("bf16", (256, 256, 64), 2), ("bf16", (256, 256, 32), 4),
                                                ("i8", (256, 256, 128), 2), ("f32", (128, 64, 16), 2)])
 def test_lds_stream_runs_and_counts_its_bytes(lib, dtype, tile, stages):
