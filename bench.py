@@ -98,14 +98,14 @@ def workload_operands(name):
 
 
 def is_aligned(name):
-    """The pgemm_aligned class of a workload: which operands meet the 16-byte
-    vector rules (device tensors start 256-byte aligned, so only the leading
-    dimension and the row length matter): 1 both, 2 A only, 3 B only, 0 none."""
+    """The pgemm_aligned class of a workload: which operands hold whole 16-byte
+    chunks per row (A: K elements, B: N elements) -- 1 both, 2 A only, 3 B
+    only, 0 none.  Row starts may have any element alignment."""
     from software_pipelined_tiled_loop_amd import inputs
     w = WORKLOADS[name]
     K, N, es = w["K"], w["N"], inputs.ELEM_BYTES[w["dtype"]]
-    a = K == 0 or (w.get("lda", K) * es % 16 == 0 and K * es % 16 == 0)
-    b = K == 0 or (w.get("ldb", N) * es % 16 == 0 and N * es % 16 == 0)
+    a = K == 0 or K * es % 16 == 0
+    b = K == 0 or N * es % 16 == 0
     return 1 if a and b else 2 if a else 3 if b else 0
 
 

@@ -28,10 +28,11 @@
  *   - C must not overlap A or B.
  *   - stream: a hipStream_t (NULL = the default stream).  The call only
  *     enqueues work and returns; completion is observed through the stream.
- *   - Misaligned pointers or leading dimensions are not an error: the
- *     misaligned operand goes through registers (16-byte loads wherever the
- *     bytes lie inside the matrix, element loads at its very end; slower, same
- *     results) and an aligned one keeps the direct copy (pgemm_producer).
+ *   - Misaligned pointers or leading dimensions are not an error: rows may
+ *     start at any element (the copies take element-aligned addresses), and
+ *     an operand whose rows are not whole 16-byte chunks is completed by
+ *     element loads (A's K tail) or goes through registers (B; slower, same
+ *     results) (pgemm_producer).
  *   - 32-bit tile addressing: M, N, K <= 2^31 - 256, lda * elem * 256, ldb *
  *     elem * 128 and ldc * 4 * 256 below 2^31 bytes; otherwise
  *     PGEMM_ERR_TOO_LARGE.
@@ -88,7 +89,11 @@ enum pgemm_status {
 /* Producer of a K tile (page "Double Buffering...", section "Two Stages, One
  * Barrier"; page "GPU-Kernel pipelinen", step 2):
  *   DIRECT   -- buffer_load ... lds: global memory straight into the LDS stage
- *               with no register involvement (the cp.async analogue).
+ *               with no register involvement (the cp.async analogue).  When
+ *               A's rows are not whole 16-byte chunks, the chunk of each row
+ *               that straddles the end of K is loaded element by element
+ *               (zero past K) and written to the stage, in the K tile that
+ *               holds the end of K.
  *   REGISTER -- global memory into VGPRs at the top of the iteration, written
  *               to the LDS stage after the iteration's MFMA work.
  *   GENERIC  -- as REGISTER, for any element-aligned layout: 16-byte loads;
@@ -100,15 +105,15 @@ enum pgemm_status {
  *   STAGED_B    (one operand copied asynchronously, the other staged through
  *               registers): STAGED_A moves A as GENERIC and B by LDS-DMA,
  *               STAGED_B moves A by LDS-DMA and B as GENERIC.  The operand
- *               that meets the 16-byte rules keeps the direct copy while the
- *               other, misaligned one goes through registers.  Two LDS stages.
+ *               that meets the chunk rule keeps the direct copy while the
+ *               other one goes through registers.  Two LDS stages.
  *
- * The 16-byte rules, per operand (K == 0 meets both):
- *   A: A 16-byte aligned, lda * elem and K * elem multiples of 16 bytes;
- *   B: B 16-byte aligned, ldb * elem and N * elem multiples of 16 bytes.
- * DIRECT and REGISTER need both, STAGED_A needs B's, STAGED_B needs A's,
- * GENERIC needs neither.  The planner (stages = 0, producer AUTO) picks
- * DIRECT when both hold and otherwise the fastest admissible variant by its
+ * The chunk rule, per operand (K == 0 meets both): A: K * elem is a multiple
+ * of 16 bytes; B: N * elem is a multiple of 16 bytes (each row is whole
+ * 16-byte chunks).  Pointers and leading dimensions need only element
+ * alignment.  DIRECT needs B's rule, REGISTER both, STAGED_A B's, STAGED_B
+ * A's, GENERIC neither.  The planner (stages = 0, producer AUTO) picks DIRECT
+ * when B's rule holds and otherwise the fastest admissible variant by its
  * measured efficiencies. */
 enum pgemm_producer {
     PGEMM_PRODUCER_AUTO = 0,
@@ -119,7 +124,7 @@ enum pgemm_producer {
     PGEMM_PRODUCER_STAGED_B = 5
 };
 
-/* Which operands meet the 16-byte rules above (pgemm_plan's `aligned`). */
+/* Which operands meet the chunk rule above (pgemm_plan's `aligned`). */
 enum pgemm_aligned {
     PGEMM_ALIGNED_NONE = 0,
     PGEMM_ALIGNED_BOTH = 1,
@@ -197,7 +202,7 @@ int pgemm_gemm_ex(int64_t M, int64_t N, int64_t K, double alpha,
  * stages": the ring depth balances the latency one K tile's arithmetic
  * covers against shared-memory use and resident workgroups, and is clipped
  * to the number of K tiles).  `aligned` (a pgemm_aligned value) says which
- * operands meet the 16-byte rules of pgemm_producer; any other value returns
+ * operands meet the chunk rule of pgemm_producer; any other value returns
  * PGEMM_ERR_INVALID_ARG.  Writes *out and touches no GPU state.
  * Returns PGEMM_OK or the error pgemm_gemm_ex would return for the same
  * sizes and options. */
@@ -318,8 +323,8 @@ int pgemm_hazard_copy_reduce(const int32_t* X, int64_t rows, int64_t cols, int64
  * LDS-DMA pieces the GEMM's DIRECT producer would for C = A*B with these
  * operands (same workgroup raster, 1-KiB blocks, one ready barrier per K
  * tile, stages - 1 K tiles in flight) and does no arithmetic.  A and B follow
- * the GEMM's layout rules and must meet the 16-byte rules for both operands
- * (pgemm_producer); they are only read.  *lds_bytes (optional) receives the
+ * the GEMM's layout rules, with both operands 16-byte aligned and lda, ldb,
+ * K and N whole 16-byte chunks (the aligned case); they are only read.  *lds_bytes (optional) receives the
  * LDS bytes the launch fills.  Asynchronous on `stream`.  Errors:
  * UNSUPPORTED_DTYPE; INVALID_ARG (sizes, leading dimensions, alignment);
  * TOO_LARGE (32-bit tile addressing); INFEASIBLE_PLAN when no stream of that
@@ -339,8 +344,8 @@ int pgemm_hazard_copy_reduce(const int32_t* X, int64_t rows, int64_t cols, int64
  * start, 7 the first ready edge passed (end of the prologue), 5 the end of
  * the K loop, 6 its C stores complete.  `out` is device memory owned by the
  * caller, 8-byte aligned, out_len >= grid * W * 8 entries with
- * grid = ceil(tiles / 8) * 8.  Both operands must meet the
- * 16-byte rules (pgemm_producer).  Asynchronous on `stream`.  Errors:
+ * grid = ceil(tiles / 8) * 8.  Both operands must be 16-byte aligned with
+ * lda, ldb, K and N whole 16-byte chunks (the aligned case).  Asynchronous on `stream`.  Errors:
  * UNSUPPORTED_DTYPE; INVALID_ARG; TOO_LARGE; INFEASIBLE_PLAN when no profile
  * build of that class and depth is compiled (bf16 256x256x64 S1/S2,
  * 256x256x32 S1..S4, 128x128x64 S2/S3; fp16 256x256x64 S1/S2; int8

@@ -37,7 +37,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 PGEMM_F32, PGEMM_F16, PGEMM_BF16, PGEMM_I8 = 0, 1, 2, 3
 DTYPE_CODE = {"f32": PGEMM_F32, "f16": PGEMM_F16, "bf16": PGEMM_BF16, "i8": PGEMM_I8}
 PRODUCER = {"auto": 0, "direct": 1, "register": 2, "generic": 3, "staged_a": 4, "staged_b": 5}
-# pgemm_aligned: which operands meet the 16-byte rules
+# pgemm_aligned: which operands meet the chunk rule (rows of whole 16-byte chunks)
 ALIGNED_NONE, ALIGNED_BOTH, ALIGNED_A, ALIGNED_B = 0, 1, 2, 3
 PRODUCER_NAME = {v: k for k, v in PRODUCER.items()}
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED_DTYPE", -3: "BAD_STAGES", -4: "INFEASIBLE_PLAN",

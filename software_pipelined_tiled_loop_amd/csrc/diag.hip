@@ -321,7 +321,7 @@ extern "C" int pgemm_diag_lds_stream(int64_t M, int64_t N, int64_t K, const void
     if (dtype < 0 || dtype > 3) return PGEMM_ERR_UNSUPPORTED_DTYPE;
     if (M <= 0 || N <= 0 || K <= 0 || !A || !B || lda < K || ldb < N) return PGEMM_ERR_INVALID_ARG;
     const int es = dtype == PGEMM_F32 ? 4 : dtype == PGEMM_I8 ? 1 : 2;
-    // the LDS-DMA producer's 16-byte rules, for both operands
+    // the aligned case: both operands 16-byte aligned, rows of whole 16-byte chunks
     if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || (lda * es) % 16 || (ldb * es) % 16 || (K * es) % 16 ||
         (N * es) % 16)
         return PGEMM_ERR_INVALID_ARG;

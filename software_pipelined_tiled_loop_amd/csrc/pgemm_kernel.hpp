@@ -501,13 +501,20 @@ __device__ __forceinline__ DmaTile dma_setup(const KernelArgs& g, int m0, int n0
 // (the select's destination would be a temporary register written right
 // under the MFMAs, which stalls the matrix pipe when the register was one of
 // their operands).
+//
+//
+// Only whole A chunks are moved: a chunk that straddles the end of K (K not
+// whole chunks, in the K tile that holds its end) would run past the row's K
+// elements, into the caller's padding or past the allocation.  Its lane
+// receives zeros like a lane outside the matrix, and dma_patch then writes
+// the chunk's elements before K over them.
 template <class C, bool FULL = false>
 __device__ __forceinline__ void dma_piece(const KernelArgs& g, const DmaTile& d, int q, int wave, int lane) {
     constexpr int ES = C::ES;
     if (q < C::A_INSTR) {
         int row, kel;
         a_chunk<C>(wave, lane, q, row, kel);
-        const bool ok = FULL || (row < d.rows_left && kel < d.k_left);
+        const bool ok = FULL || (row < d.rows_left && kel + C::EPC <= d.k_left);
         dma16(d.ra, ok ? (uint32_t)(row * (int)g.lda + kel) * ES : OOB, d.sa + (uint32_t)q * 1024u);
     } else {
         const int qb = q - C::A_INSTR;
@@ -527,6 +534,47 @@ __device__ __forceinline__ void issue_dma(const KernelArgs& g, int m0, int n0, i
     const DmaTile d = dma_setup<C>(g, m0, n0, kt, stage, wave);
 #pragma unroll
     for (int q = C::DMA_P0; q < C::DMA_P1; ++q) dma_piece<C, FULL>(g, d, q, wave, lane);
+    if constexpr (!FULL && C::P == PROD_DIRECT) {
+        if (tail_tile<C>(g, kt)) dma_patch<C>(g, m0, kt, stage, wave, lane);
+    }
+}
+
+// Whether K tile kt holds the end of a K that is not whole 16-byte chunks
+// (uniform): the one K tile whose A chunks can straddle the end of K.  Only
+// the DIRECT producer meets it: STAGED_B, the other one that moves A by
+// LDS-DMA, is admitted only when A's rows are whole chunks.
+template <class C>
+__device__ __forceinline__ bool tail_tile(const KernelArgs& g, int kt) {
+    const int k_left = g.K - kt * C::BK;
+    return C::P == PROD_DIRECT && k_left > 0 && k_left < C::BK && k_left % C::EPC != 0;
+}
+
+// The K tail of an A moved by LDS-DMA when K is not whole 16-byte chunks: in
+// the tail K tile each row's chunk that straddles K (zeros from dma_piece) is
+// loaded element by element, zero past K, and written over its place in the
+// stage.  Called after the tile's LDS-DMA pieces and before the barrier that
+// makes the stage ready.  Waiting for its own loads before the LDS writes, it
+// waits for every earlier load of the wave (vmcnt counts in order), so the
+// pieces' zeros have landed before they are overwritten.  Once per output
+// tile.
+template <class C>
+__device__ __forceinline__ void dma_patch(const KernelArgs& g, int m0, int kt, char PGEMM_LDS* stage, int wave,
+                                          int lane) {
+    if constexpr (C::A_DMA) {
+        const int k0 = kt * C::BK, k_left = g.K - k0;
+        const int rows_left = g.M - m0;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc((const char*)g.A + ((int64_t)m0 * g.lda + k0) * C::ES);
+#pragma unroll
+        for (int q = 0; q < C::A_INSTR; ++q) {
+            int row, kel;
+            a_chunk<C>(wave, lane, q, row, kel);
+            if (row < rows_left && kel < k_left && kel + C::EPC > k_left) {
+                const i32x4 v =
+                    load_chunk_elementwise<C::ES>(r, (uint32_t)(row * (int)g.lda + kel) * C::ES, k_left - kel);
+                *(i32x4 PGEMM_LDS*)(stage + (wave * C::A_INSTR + q) * 1024 + lane * 16) = v;
+            }
+        }
+    }
 }
 
 // Global loads of K tile `kt` for the register-staged operands, into the
@@ -1012,6 +1060,11 @@ __device__ __forceinline__ void tile_body(const KernelArgs& g, const Cursor& dc,
                 mfma_step<C, true, C::ANY_DMA, FULL>(acc, use, nxt, rstage, 0, g, d, wave, lane, wm0, wn0, staged);
             } else {
                 mfma_step<C, true, true, FULL>(acc, use, nxt, rstage, 0, g, d, wave, lane, wm0, wn0);  // slot s+S
+            }
+            // slot s+S holds the end of a K that is not whole chunks: its
+            // straddling A chunks are completed after the pieces
+            if constexpr (!FULL && C::P == PROD_DIRECT) {
+                if (tail_tile<C>(g, dc.kt)) dma_patch<C>(g, dc.m0, dc.kt, freed, wave, lane);
             }
         }
     }

@@ -273,6 +273,53 @@ static int check_whole_loads(const char* name) {
     return cases;
 }
 
+// DIRECT on a K that is not whole 16-byte chunks, in the K tile that holds
+// the end of K (k_left < BK, k_left % EPC != 0): LDS-DMA moves only whole A
+// chunks (every element it reads lies before k_left in a row that exists),
+// lanes with a straddling chunk receive zeros, and the tail patch writes the
+// chunk's elements before k_left over them.  The A region must then hold the
+// zero-padded tile exactly, as DIRECT would on a copy with K rounded up.
+template <class C>
+static int check_dma_tail(const char* name) {
+    constexpr int EPC = C::EPC, BK = C::BK;
+    int cases = 0;
+    for (int k_left = 1; k_left < BK; ++k_left) {
+        if (k_left % EPC == 0) continue;
+        for (int rows_left : {1, C::BM / 2 + 3, C::BM}) {
+            // element (row, k) of the global tile holds 1 + row * BK + k; -1 marks "never written"
+            std::vector<long> lds(C::A_BYTES / C::ES, -1);
+            for (int w = 0; w < C::NW; ++w)
+                for (int l = 0; l < 64; ++l)
+                    for (int q = 0; q < C::A_INSTR; ++q) {
+                        int row, kel;
+                        a_chunk<C>(w, l, q, row, kel);
+                        const long base = ((long)(w * C::A_INSTR + q) * 1024 + l * 16) / C::ES;
+                        const bool ok = row < rows_left && kel + EPC <= k_left;  // dma_piece
+                        for (int e = 0; e < EPC; ++e) {
+                            if (ok && kel + e >= k_left) FAIL("LDS-DMA reads past K: k %d k_left %d", kel + e, k_left);
+                            lds[base + e] = ok ? 1 + (long)row * BK + kel + e : 0;
+                        }
+                        // dma_patch (after the pieces have landed)
+                        if (row < rows_left && kel < k_left && kel + EPC > k_left)
+                            for (int e = 0; e < EPC; ++e) lds[base + e] = kel + e < k_left ? 1 + (long)row * BK + kel + e : 0;
+                    }
+            // compare with the zero-padded tile, placed by the A swizzle
+            for (int row = 0; row < C::BM; ++row)
+                for (int kc = 0; kc < C::KC; ++kc)
+                    for (int e = 0; e < EPC; ++e) {
+                        const int k = kc * EPC + e;
+                        const long want = row < rows_left && k < k_left ? 1 + (long)row * BK + k : 0;
+                        const long got = lds[a_off<C::KC>(row, kc) / C::ES + e];
+                        if (got != want)
+                            FAIL("tail tile: row %d k %d k_left %d rows_left %d holds %ld, want %ld", row, k, k_left,
+                                 rows_left, got, want);
+                    }
+            ++cases;
+        }
+    }
+    return cases;
+}
+
 // Hazard demonstrator indexing (hazard_demo.hpp), for the shapes and leading
 // dimensions the entry point admits: every global read (tiles 0, 1 and, per
 // iteration, t+2 or t) lies inside the caller's rows x cols, every LDS index
@@ -397,12 +444,13 @@ static int check_work_split() {
         wl += check_whole_loads<Cfg<D, BM, BN, BK, 2, WGM, WGN, PROD_GENERIC>>("whole_loads " #D); \
         wl += check_whole_loads<Cfg<D, BM, BN, BK, 2, WGM, WGN, PROD_STAGED_A>>("whole_loads staged A " #D); \
         wl += check_whole_loads<Cfg<D, BM, BN, BK, 2, WGM, WGN, PROD_STAGED_B>>("whole_loads staged B " #D); \
+        dt += check_dma_tail<Cfg<D, BM, BN, BK, 2, WGM, WGN, PROD_DIRECT>>("dma tail " #D);   \
         ++n;                                                                       \
         printf("class %d %d %d %d %d %d\n", D, BM, BN, BK, WGM, WGN);              \
     } while (0)
 
 int main() {
-    int n = 0, wl = 0;
+    int n = 0, wl = 0, dt = 0;
     CHECK(DT_BF16, 256, 256, 32, 2, 4);
     CHECK(DT_BF16, 256, 256, 64, 2, 4);
     CHECK(DT_BF16, 128, 128, 64, 2, 2);
@@ -416,6 +464,7 @@ int main() {
     CHECK(DT_F32, 256, 256, 32, 2, 4);
     CHECK(DT_F32, 128, 128, 32, 2, 2);
     printf("whole_loads %d cases\n", wl);
+    printf("dma_tail %d cases\n", dt);
     printf("chunk_fits %d cases\n", check_chunk_fits());
     printf("work_split %d cases\n", check_work_split());
     printf("hazard %d cases\n", check_hazard_indexing());

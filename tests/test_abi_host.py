@@ -311,7 +311,7 @@ def test_planner_honours_explicit_depth(dtype):
         r, p = lib.pgemm_plan(1024, 1024, 2048, dtype, S, 1)
         assert r == 0 and p["stages"] == S
     r, _ = lib.pgemm_plan(1024, 1024, 2048, dtype, 0, 0, {"producer": "direct"})
-    assert r == -4  # the direct producer needs the 16-byte rules
+    assert r == -4  # the direct producer needs B's chunk rule
     r, p = lib.pgemm_plan(1024, 1024, 2047, dtype, 0, 0)
     assert r == 0 and p["producer"] == "generic"
     r, _ = lib.pgemm_plan(1024, 1024, 2048, dtype, 0, 1, {"tile": (8, 8, 8)})
@@ -321,11 +321,12 @@ def test_planner_honours_explicit_depth(dtype):
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
 def test_planner_keeps_the_direct_copy_for_the_aligned_operand(dtype):
     """Per-operand producers: each forced producer is admitted exactly for the
-    alignment classes whose operands it moves by LDS-DMA or unchecked 16-byte
-    loads; with one operand aligned the planner picks among GENERIC and the
-    staged producer that keeps that operand on LDS-DMA; unknown classes are
-    argument errors."""
-    need = {"direct": {lib.ALIGNED_BOTH}, "register": {lib.ALIGNED_BOTH},
+    chunk-rule classes it can serve (DIRECT needs B's rule and completes A's
+    K tail by element loads; REGISTER needs both; each staged producer the
+    rule of the operand it keeps on LDS-DMA); with only B whole the planner
+    keeps DIRECT, with only A whole it picks among GENERIC and STAGED_B;
+    unknown classes are argument errors."""
+    need = {"direct": {lib.ALIGNED_BOTH, lib.ALIGNED_B}, "register": {lib.ALIGNED_BOTH},
             "staged_a": {lib.ALIGNED_BOTH, lib.ALIGNED_B}, "staged_b": {lib.ALIGNED_BOTH, lib.ALIGNED_A},
             "generic": {lib.ALIGNED_NONE, lib.ALIGNED_BOTH, lib.ALIGNED_A, lib.ALIGNED_B}}
     for prod, ok in need.items():
@@ -334,13 +335,10 @@ def test_planner_keeps_the_direct_copy_for_the_aligned_operand(dtype):
             assert (r == 0) == (cls in ok), (prod, cls, r)
             if r == 0:
                 assert p["producer"] == prod
-    for cls, allowed in ((lib.ALIGNED_A, {"generic", "staged_b"}), (lib.ALIGNED_B, {"generic", "staged_a"}),
+    for cls, allowed in ((lib.ALIGNED_A, {"generic", "staged_b"}), (lib.ALIGNED_B, {"direct"}),
                          (lib.ALIGNED_NONE, {"generic"})):
         r, p = lib.pgemm_plan(4000, 3968, 4001, dtype, 0, cls)
         assert r == 0 and p["producer"] in allowed, (cls, p)
-    # at the ragged benchmark size the staged producer wins over GENERIC
-    r, p = lib.pgemm_plan(4000, 3968, 4001, dtype, 0, lib.ALIGNED_B)
-    assert p["producer"] == "staged_a"
     for bad in (-1, 4, 7):
         assert lib.pgemm_plan(64, 64, 64, dtype, 0, bad)[0] == -1
 

@@ -71,10 +71,11 @@ def test_every_workload_has_a_plan():
     for name, w in bench.WORKLOADS.items():
         dt, M, N, K = w["dtype"], w["M"], w["N"], w["K"]
         assert bench.plan_of(lib, dt, M, N, K, aligned=bench.is_aligned(name)) is not None, name
-    # the ragged workload: lda = 4001 breaks A's rules only, so B keeps LDS-DMA
+    # the ragged workload: K = 4001 breaks A's chunk rule only, so both
+    # operands keep LDS-DMA and A's K tail is completed by element loads
     assert bench.is_aligned("ragged") == lib.ALIGNED_B
     p = bench.plan_of(lib, "bf16", 4000, 3968, 4001, aligned=lib.ALIGNED_B)
-    assert p["producer"] == "staged_a"
+    assert p["producer"] == "direct"
 
 
 def test_pages_context_ratios():

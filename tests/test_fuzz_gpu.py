@@ -6,8 +6,8 @@ none of them lists: every compiled variant (tile class, ring depth, producer)
 of every dtype, forced or left to the planner, on shapes that cut tiles and K
 tiles at random places, with padded or odd leading dimensions, nonzero beta,
 and sometimes persistent workgroups.  Tolerances are the benchmark's (see
-test_parity_gpu).  A forced producer the operands' 16-byte layout does not
-admit must be refused before launch with PGEMM_ERR_INFEASIBLE_PLAN, and the
+test_parity_gpu).  A forced producer the operands' chunk rule (rows of whole
+16-byte chunks) does not admit must be refused before launch with PGEMM_ERR_INFEASIBLE_PLAN, and the
 planner (pgemm_plan, same options and alignment class) must agree with the
 launch about every refusal.  Every case prints its parameters before it runs.
 """
@@ -34,18 +34,18 @@ def lib():
 
 
 def aligned_class(lib, dtype, K, N, lda, ldb):
-    """The pgemm_aligned class of operands that start 256-byte aligned (torch
-    allocations): which operands meet the 16-byte rules."""
+    """The pgemm_aligned class: which operands hold whole 16-byte chunks per
+    row (A: K elements, B: N elements); leading dimensions do not matter."""
     es = inputs.ELEM_BYTES[dtype]
-    a = K == 0 or (lda * es % 16 == 0 and K * es % 16 == 0)
-    b = K == 0 or (ldb * es % 16 == 0 and N * es % 16 == 0)
+    a = K == 0 or K * es % 16 == 0
+    b = K == 0 or N * es % 16 == 0
     return lib.ALIGNED_BOTH if a and b else lib.ALIGNED_A if a else lib.ALIGNED_B if b else lib.ALIGNED_NONE
 
 
 def admitted(lib, producer, cls):
     a = cls in (lib.ALIGNED_BOTH, lib.ALIGNED_A)
     b = cls in (lib.ALIGNED_BOTH, lib.ALIGNED_B)
-    return {"direct": a and b, "register": a and b, "staged_a": b, "staged_b": a, "generic": True}[producer]
+    return {"direct": b, "register": a and b, "staged_a": b, "staged_b": a, "generic": True}[producer]
 
 
 def draw_dim(rng, hi):

@@ -6,7 +6,9 @@ exactly once), the fragment reads with the probed lane semantics of
 ds_read_b128 / ds_read_b64_tr_b16 / ds_read_b64_tr_b8 / ds_read_b32 (every read
 inside its region), and the MFMA lane layouts, compared with a naive GEMM of
 the tile.  It also checks by brute force the generic producer's choice of
-whole 16-byte loads (every admitted read inside its matrix, none of A past K)
+whole 16-byte loads (every admitted read inside its matrix, none of A past K),
+the DIRECT producer's K tail (LDS-DMA of whole chunks plus the element-wise
+patch gives the zero-padded tile)
 and the hazard demonstrator's indexing (every read, LDS, row-sum and timeline
 index inside its buffer; each stage chunk produced and consumed exactly once).
 No GPU is used; hipcc only compiles host code here.
@@ -37,6 +39,7 @@ def test_emulated_data_path_matches_naive_gemm(tmp_path):
     assert re.search(r"^chunk_fits \d+ cases$", out, re.M), out[-2000:]
     assert re.search(r"^work_split \d+ cases$", out, re.M), out[-2000:]
     assert re.search(r"^whole_loads \d+ cases$", out, re.M), out[-2000:]
+    assert re.search(r"^dma_tail \d+ cases$", out, re.M), out[-2000:]
     assert re.search(r"^hazard \d+ cases$", out, re.M), out[-2000:]
     emulated = set(tuple(int(x) for x in m) for m in re.findall(r"^class (\d+) (\d+) (\d+) (\d+) (\d+) (\d+)$", out, re.M))
     # every tile class the library compiles is emulated

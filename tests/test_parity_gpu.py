@@ -333,11 +333,12 @@ def _device_copy(t, dev, offset_elems=0):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
 def test_one_operand_misaligned(lib, dtype):
-    """One producer per operand.  When only A breaks the 16-byte rules (an odd
-    lda, a K that is not whole 16-byte chunks, or an A pointer off 16-byte
-    alignment) the planner keeps LDS-DMA for B and stages A through registers
-    (STAGED_A); when only B does (odd ldb or N, or B's pointer), the reverse
-    (STAGED_B).  Each case is checked against the oracle, and -- since both
+    """One producer per operand.  STAGED_A keeps LDS-DMA for B and stages A
+    through registers, STAGED_B the reverse; each is forced on layouts where
+    the staged operand is awkward (an odd leading dimension, rows that are not
+    whole 16-byte chunks, a pointer off 16-byte alignment), and the planner's
+    own pick (DIRECT when B's rows are whole chunks) runs beside it.  Each
+    result is checked against the oracle, and the forced one -- since both
     producers of an operand fill the LDS stage with the same bytes -- must be
     bit-identical, in every stored column, to the DIRECT producer on a
     zero-padded aligned copy (K and N rounded up to whole chunks), with the
@@ -368,7 +369,7 @@ def test_one_operand_misaligned(lib, dtype):
                 B, keep_b = _device_copy(op.B, dev, c["off"] if prod == "staged_b" else 0)
                 cls = lib.ALIGNED_B if prod == "staged_a" else lib.ALIGNED_A
                 r, plan = lib.pgemm_plan(M, N, K, dtype, 0, cls, None)
-                assert r == 0 and plan["producer"] in (prod, "generic"), plan
+                assert r == 0 and plan["producer"] in ("direct", prod, "generic"), plan
                 outs = {}
                 for key, stages, producer, t in (("auto", 0, None, None), ("forced", 2, prod, tile)):
                     C = op.C.to(dev)
@@ -390,6 +391,63 @@ def test_one_operand_misaligned(lib, dtype):
                 got = outs["forced"][:, :N].contiguous()
                 assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), (prod, tile, c)
                 del A, B, keep_a, keep_b
+
+
+def direct_classes(lib, dtype):
+    out = {}
+    for i in range(lib.pgemm_num_variants()):
+        v = lib.pgemm_variant_info(i)
+        if v["dtype"] == dtype and v["producer"] == "direct":
+            out.setdefault((v["tile_m"], v["tile_n"], v["tile_k"]), []).append(v["stages"])
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_direct_unaligned_rows_and_k_tail(lib, dtype):
+    """DIRECT on rows that start anywhere (odd lda and ldb, pointers one
+    element off 16-byte alignment) and on a K that is not whole 16-byte
+    chunks: LDS-DMA takes the element-aligned rows as they are, and in the K
+    tile that holds the end of K the chunk of each row that straddles K is
+    loaded element by element, zero past K (in the loop, or in the prologue
+    when the ring holds every K tile).  Every compiled DIRECT variant, and
+    persistent workgroups, against the oracle and bit-identical to DIRECT on
+    a zero-padded aligned copy (K rounded up to whole chunks), same tile
+    class and depth: the stage holds the same bytes either way."""
+    es = inputs.ELEM_BYTES[dtype]
+    epc = 16 // es
+    dev = torch.device("cuda:0")
+    for tile, depths in sorted(direct_classes(lib, dtype).items()):
+        BM, BN, BK = tile
+        for S in sorted(depths):
+            cases = [dict(M=BM + 5, N=2 * BN - epc, K=3 * BK + 1, lda=3 * BK + 1, ldb=2 * BN - epc + 1, off=1, wg=0),
+                     dict(M=2 * BM + 3, N=BN + 2 * epc, K=S * BK - 3, lda=S * BK + 2, ldb=BN + 2 * epc, off=0, wg=0),
+                     dict(M=BM - 7, N=BN, K=BK // 2 + 1, lda=BK // 2 + 1, ldb=BN + 3, off=1, wg=0),
+                     dict(M=3 * BM + 1, N=2 * BN, K=4 * BK + epc - 1, lda=4 * BK + epc + 5, ldb=2 * BN, off=1,
+                          wg=8 if S > 1 else 0)]
+            for c in cases:
+                M, N, K = c["M"], c["N"], c["K"]
+                say("direct unaligned", dtype, tile, "S", S, c)
+                op = inputs.make_operands(dtype, M, N, K, seed=M + 3 * N + K, alpha=1.0, beta=0.0, lda=c["lda"],
+                                          ldb=c["ldb"])
+                A, keep_a = _device_copy(op.A, dev, c["off"])
+                B, keep_b = _device_copy(op.B, dev, c["off"])
+                C = op.C.to(dev)
+                rr = lib.pgemm_gemm_ex(M, N, K, 1.0, A, op.lda, B, op.ldb, 0.0, C, op.ldc, dtype, S,
+                                       lib._opts("direct", tile, workgroups=c["wg"]), None)
+                assert rr == 0, lib.pgemm_strerror(rr)
+                torch.cuda.synchronize()
+                got = C.cpu()
+                check(op, got)
+                padding_untouched(op, got)
+                Kp = -(-K // epc) * epc
+                pad = inputs.make_operands(dtype, M, N, Kp, seed=1, alpha=1.0, beta=0.0)
+                pad.A.zero_()
+                pad.B.zero_()
+                pad.A[:, :K] = op.A[:, :K]
+                pad.B[:K, :N] = op.B[:, :N]
+                ref = run_gpu(lib, pad, stages=S, producer="direct", tile=tile)[:, :N].contiguous()
+                assert torch.equal(got[:, :N].contiguous().view(torch.int32), ref.view(torch.int32)), (tile, S, c)
+                del A, B, C, keep_a, keep_b
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
