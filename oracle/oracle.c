@@ -154,7 +154,8 @@ int64_t oracle_gemm_i8(int64_t M, int64_t N, int64_t K, int64_t alpha,
         }
         for (int64_t j = 0; j < N; ++j) {
             if (s[j] < INT32_MIN || s[j] > INT32_MAX) n_acc_over++;
-            /* alpha*s and beta*C0 fit in int64: the caller keeps |alpha|,|beta| < 2^31. */
+            /* alpha*s and beta*C0 fit in int64: |alpha|, |beta| <= 2^31 (int32 values),
+             * |s| <= K * 2^14 and |C0| <= 2^31, so for K <= 2^16 the sum stays below 2^63. */
             int64_t v = alpha * s[j];
             if (beta != 0) v += beta * (int64_t)C0[i * ldc + j];
             if (v < INT32_MIN || v > INT32_MAX) n_out_over++;

@@ -213,6 +213,29 @@ def pgemm_model_compute_load_ratio(bm, bn, bk, elem_bytes):
     return _lib.pgemm_model_compute_load_ratio(bm, bn, bk, elem_bytes)
 
 
+def _regions_overlap(X, xr, xc, Y, yr, yc):
+    """Whether the first xr rows x xc columns of 2-D tensor X share a byte
+    with the first yr x yc of Y (rows at each tensor's row stride).  Exact
+    when both row strides in bytes are equal (slices of one matrix); with
+    different strides, any overlap of the two byte ranges counts."""
+    if not (xr and xc and yr and yc):
+        return False
+    sx, sy = X.stride(0) * X.element_size(), Y.stride(0) * Y.element_size()
+    wx, wy = xc * X.element_size(), yc * Y.element_size()
+    x0, y0 = X.data_ptr(), Y.data_ptr()
+    if x0 >= y0 + (yr - 1) * sy + wy or y0 >= x0 + (xr - 1) * sx + wx:
+        return False
+    if sx != sy or sx == 0:
+        return True
+    # row i of X and row j of Y meet iff -wy < d + (j - i) * s < wx, d = y0 - x0
+    d = y0 - x0
+    t0 = -d // sx
+    for t in range(t0 - 1, t0 + 3):
+        if -(xr - 1) <= t <= yr - 1 and -wy < d + t * sx < wx:
+            return True
+    return False
+
+
 def gemm(A, B, C, alpha=1.0, beta=0.0, stages=0, producer=None, tile=None, M=None, N=None, K=None,
          stream=None):
     """C = alpha*A@B + beta*C on torch tensors (2-D, row-major, unit column stride).
@@ -220,7 +243,9 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, stages=0, producer=None, tile=None, M=Non
     dtype is taken from A: float32 -> f32, float16 -> f16, bfloat16 -> bf16, int8 -> i8.
     B must have A's dtype; C is float32 (int32 for int8).  Sizes default to the
     logical shapes and must fit inside the tensors; leading dimensions are the
-    row strides.  All three tensors must live on one GPU.  Every check runs
+    row strides.  All three tensors must live on one GPU, and C must not
+    overlap A or B; the call runs on that GPU (torch's current stream there
+    unless `stream` is given).  Every check runs
     before anything reaches the library, so a bad call raises ValueError and
     launches nothing.
     """
@@ -243,11 +268,16 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, stages=0, producer=None, tile=None, M=Non
     for name, t, rows, cols in (("A", A, M, K), ("B", B, K, N), ("C", C, M, N)):
         if rows < 0 or cols < 0 or (rows and cols and (t.shape[0] < rows or t.shape[1] < cols)):
             raise ValueError("%s is %s, the call needs %d x %d" % (name, tuple(t.shape), rows, cols))
+    for name, t, rows, cols in (("A", A, M, K), ("B", B, K, N)):
+        if t.device == C.device and _regions_overlap(t, rows, cols, C, M, N):
+            raise ValueError("C overlaps %s: the output must not share memory with an input" % name)
     devs = {t.device for t in (A, B, C)}
     if len(devs) != 1 or next(iter(devs)).type != "cuda":
         raise ValueError("A, B and C must be GPU tensors on one device, got %s" % sorted(str(d) for d in devs))
-    r = pgemm_gemm_ex(M, N, K, alpha, A, max(A.stride(0), 1), B, max(B.stride(0), 1), beta, C,
-                      max(C.stride(0), 1), dt, stages, _opts(producer, tile), stream)
+    # the library launches on the current device: make it the tensors' one
+    with torch.cuda.device(C.device):
+        r = pgemm_gemm_ex(M, N, K, alpha, A, max(A.stride(0), 1), B, max(B.stride(0), 1), beta, C,
+                          max(C.stride(0), 1), dt, stages, _opts(producer, tile), stream)
     if r != 0:
         raise PgemmError(r)
     return C

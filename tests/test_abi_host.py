@@ -88,6 +88,16 @@ def test_option_errors_before_any_launch(opts):
     assert lib.pgemm_gemm_ex(8, 8, 8, 1.0, FAKE, 8, FAKE, 8, 0.0, FAKE, 8, "bf16", 0, o, 0) == -1
 
 
+@pytest.mark.parametrize("alpha,beta,code", [
+    (-2.0 ** 31, 0.0, 0), (2.0 ** 31 - 1, -2.0 ** 31, 0),          # the ends of int32 are accepted
+    (-2.0 ** 31 - 1, 0.0, -5), (2.0 ** 31, 0.0, -5), (1.0, 2.0 ** 31, -5), (float("inf"), 0.0, -5),
+])
+def test_int8_scalars_must_be_int32_integers(alpha, beta, code):
+    # M = 0: the scalars are checked, then the call is a no-op, so nothing is launched
+    r = lib._lib.pgemm_gemm(0, 8, 8, alpha, FAKE, 8, FAKE, 8, beta, FAKE, 8, lib.DTYPE_CODE["i8"], 0, None)
+    assert r == code, (alpha, beta, r)
+
+
 def test_ldc_beyond_32_bit_tile_addressing_is_rejected():
     r = lib._lib.pgemm_gemm(8, 8, 8, 1.0, FAKE, 8, FAKE, 8, 0.0, FAKE, 1 << 21, 2, 0, None)
     assert r == -7
@@ -223,6 +233,21 @@ def test_torch_wrapper_validates_before_any_launch():
         lib.gemm(A, B, C, M=9)                                      # M beyond A's rows
     with pytest.raises(ValueError):
         lib.gemm(A.to(f32), B.to(f32), C, K=17)                     # K beyond A's columns
+
+
+def test_torch_wrapper_refuses_output_overlapping_an_input():
+    """C must not share memory with A or B (the kernels read A and B while
+    C is written); the overlap check comes before the device check, so CPU
+    tensors show it without reaching the library."""
+    import torch
+    buf = torch.zeros(64, 64)
+    with pytest.raises(ValueError, match="overlaps A"):
+        lib.gemm(buf[:16, :16], torch.zeros(16, 16), buf[8:24, :16])
+    with pytest.raises(ValueError, match="overlaps B"):
+        lib.gemm(torch.zeros(16, 16), buf[:16, 32:48], buf[15:31, 47:63])
+    # side by side in one allocation, no shared element: only the device check remains
+    with pytest.raises(ValueError, match="GPU tensors"):
+        lib.gemm(buf[:16, :16], buf[:16, 16:32], buf[:16, 32:48])
 
 
 def test_diagnostics_refuse_bad_arguments_before_any_launch():
@@ -413,3 +438,33 @@ def test_planner_tables_were_measured_on_these_kernel_sources():
     import bench
     from software_pipelined_tiled_loop_amd import build
     assert build.load_tables()["kernel_source_hash"] == bench.kernel_source_hash()
+
+
+def test_overlap_check_against_brute_force():
+    """binding._regions_overlap against the sets of bytes two slices of one
+    buffer touch: exact for equal row strides, never a missed overlap
+    otherwise."""
+    import random
+
+    import torch
+    rng = random.Random(5)
+    for _ in range(3000):
+        w1, w2 = rng.choice([(16, 16), (16, 24), (24, 16)])
+        buf1, buf2 = torch.zeros(48 * w1), torch.zeros(48 * w2)
+        X = buf1.view(48, w1)
+        Y = (buf1.view(48, w1) if rng.random() < 0.7 else buf2.view(48, w2)) if w1 == w2 else buf1.view(-1, w2)
+        xr, xc, yr, yc = rng.randint(0, 6), rng.randint(0, 8), rng.randint(0, 6), rng.randint(0, 8)
+        xi, xj = rng.randint(0, 40), rng.randint(0, 8)
+        yi, yj = rng.randint(0, 40), rng.randint(0, 8)
+        Xs, Ys = X[xi:xi + xr, xj:xj + xc], Y[yi:yi + yr, yj:yj + yc]
+        xr, xc, yr, yc = Xs.shape[0], Xs.shape[1], Ys.shape[0], Ys.shape[1]
+
+        def cells(t, r, c):
+            return {t.data_ptr() + (i * t.stride(0) + j) * 4 + b for i in range(r) for j in range(c) for b in range(4)}
+
+        truth = bool(cells(Xs, xr, xc) & cells(Ys, yr, yc))
+        got = lib._regions_overlap(Xs, xr, xc, Ys, yr, yc)
+        if Xs.stride(0) == Ys.stride(0):
+            assert got == truth, (xi, xj, xr, xc, yi, yj, yr, yc)
+        else:
+            assert got or not truth

@@ -271,6 +271,17 @@ def test_alpha_scaling_is_exact(lib):
     assert torch.equal(c2, 2.0 * c1)
 
 
+@pytest.mark.parametrize("alpha,beta", [(-2 ** 31, 2 ** 31 - 1), (2 ** 31 - 1, -2 ** 31), (-3, -2 ** 31)])
+def test_int8_scalars_at_the_ends_of_int32(lib, alpha, beta):
+    """alpha and beta anywhere in int32: alpha*acc + beta*C0 wraps modulo
+    2^32 on both sides, so the result is still bit-exact."""
+    say("int8 scalars", alpha, beta)
+    op = inputs.make_operands("i8", 300, 272, 200, seed=12, alpha=float(alpha), beta=float(beta))
+    got = run_gpu(lib, op)
+    check(op, got)
+    assert oracle.gemm.last_overflow[0] > 0  # the exact result left int32: the wrap was exercised
+
+
 # ------------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
