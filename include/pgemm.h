@@ -20,7 +20,8 @@
  *   - dtype: PGEMM_F32 (A, B, C fp32), PGEMM_F16 and PGEMM_BF16 (A, B 16-bit,
  *     C fp32, fp32 accumulation), PGEMM_I8 (A, B int8, C int32, int32
  *     accumulation and int32 two's-complement epilogue; alpha and beta must be
- *     integers in int32 range).
+ *     integers in int32 range; sums, products and the result wrap modulo 2^32,
+ *     with no saturation, so C is the exact result reduced to int32).
  *   - Pointers A, B, C are device pointers owned by the caller.  The library
  *     allocates nothing and keeps no state besides constant tables.
  *   - beta == 0: C is written without being read (NaN/Inf in C do not

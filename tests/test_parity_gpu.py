@@ -282,6 +282,26 @@ def test_int8_scalars_at_the_ends_of_int32(lib, alpha, beta):
     assert oracle.gemm.last_overflow[0] > 0  # the exact result left int32: the wrap was exercised
 
 
+@pytest.mark.parametrize("K", [2 ** 17 + 2 ** 12, 2 ** 17 + 2 ** 12 - 56])
+def test_int8_accumulator_wraps_modulo_2_32(lib, K):
+    """K beyond 2^17 lets the int32 accumulators of a long int8 dot product
+    leave int32: rows of A = -128 against B of -128 (every seventh row -127)
+    sum to about 16384 * K > 2^31 - 1, rows of A = 127 to about -16250 * K <
+    -2^31, so every output's exact sum is outside int32.  The GPU's int32
+    accumulation wraps modulo 2^32 like the oracle's exact sum reduced to
+    int32 (no saturation), with a K tail that is not whole 16-byte chunks in
+    the second case."""
+    say("int8 accumulator wrap", K)
+    op = inputs.make_operands("i8", 40, 48, K, seed=21)
+    op.A[:, :K] = -128
+    op.A[1::3, :K] = 127
+    op.B[:, :48] = -128
+    op.B[5::7, :48] = -127   # every seventh row of B one step smaller
+    got = run_gpu(lib, op)
+    check(op, got)
+    assert oracle.gemm.last_overflow[1] > 0  # raw sums left int32 on the oracle's side too
+
+
 # ------------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
