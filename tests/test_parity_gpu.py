@@ -302,6 +302,26 @@ def test_int8_accumulator_wraps_modulo_2_32(lib, K):
     assert oracle.gemm.last_overflow[1] > 0  # raw sums left int32 on the oracle's side too
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_subnormal_inputs_and_results_are_kept(lib, dtype):
+    """Subnormal operands (and, for fp32 and bf16, subnormal fp32 results)
+    are not flushed to zero: powers of two whose sums are exact, so the GPU
+    must equal the oracle exactly."""
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    sub, big = {"f16": (2.0 ** -20, 2.0 ** 10), "bf16": (2.0 ** -130, 2.0 ** 20), "f32": (2.0 ** -140, 2.0 ** 30)}[dtype]
+    M, N, K = 64, 80, 256
+    for aval, bval in ((sub, big), (big, sub), (sub, 1.0)):
+        say("subnormal", dtype, aval, bval)
+        op = inputs.make_operands(dtype, M, N, K, seed=3)
+        op.A[:, :K] = torch.tensor(aval, dtype=tdt)
+        op.B[:, :N] = torch.tensor(bval, dtype=tdt)
+        assert float(op.A[0, 0]) == aval and float(op.B[0, 0]) == bval  # representable as given
+        got = run_gpu(lib, op)
+        ref = reference(op)
+        assert ref[0, 0] != 0.0
+        assert np.array_equal(got[:, :N].double().numpy(), ref), (aval, bval)
+
+
 # ------------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
