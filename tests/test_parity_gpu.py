@@ -322,6 +322,34 @@ def test_subnormal_inputs_and_results_are_kept(lib, dtype):
         assert np.array_equal(got[:, :N].double().numpy(), ref), (aval, bval)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_nan_and_inf_in_operands_propagate(lib, dtype):
+    """IEEE propagation through the pipeline: a NaN in row 3 of A makes row 3
+    of C NaN, a +Inf in row 7 (against a positive B) makes row 7 +Inf, a NaN
+    in column 11 of B makes column 11 NaN; every other output is finite and
+    within tolerance.  Padding past K stays NaN in the caller's memory and
+    must not leak in (the tile's zeros there keep every other output finite)."""
+    M, N, K = 130, 140, 300
+    say("nan/inf", dtype)
+    op = inputs.make_operands(dtype, M, N, K, seed=31, lda=K + 8, ldb=N + 8)
+    op.B[:, :N] = op.B[:, :N].abs() + 0.5
+    op.A[3, 17] = float("nan")
+    op.A[7, 250] = float("inf")
+    op.B[120, 11] = float("nan")
+    got = run_gpu(lib, op)
+    ref = reference(op)
+    g = got[:, :N].double().numpy()
+    assert np.all(np.isnan(g[3])) and np.all(np.isnan(g[:, 11]))
+    assert np.all(np.isposinf(np.delete(g[7], 11)))
+    assert np.array_equal(np.isnan(g), np.isnan(ref)) and np.array_equal(np.isinf(g), np.isinf(ref))
+    rest = np.ones((M, N), bool)
+    rest[[3, 7], :] = False
+    rest[:, 11] = False
+    err = np.max(np.abs(g[rest] - ref[rest]))
+    bound = TOL[dtype] * math.sqrt(K) * np.max(np.abs(ref[rest]))
+    assert err <= bound, (err, bound)
+
+
 # ------------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
