@@ -350,6 +350,41 @@ def test_nan_and_inf_in_operands_propagate(lib, dtype):
     assert err <= bound, (err, bound)
 
 
+def test_calls_on_a_side_stream_follow_stream_order(lib):
+    """Page "Software pipelines and asynchronous copies", section "Common
+    errors": issuing is not completing.  On a side stream (default priority),
+    a torch kernel writes A, a first GEMM reads it into C1, a second GEMM reads
+    C1 as its A; only the side stream is synchronised at the end.  Each GEMM
+    must see its predecessor's finished output: the second result equals the
+    oracle applied to the first GPU result."""
+    M = N = K = 1536
+    say("side stream chain", (M, N, K))
+    op1 = inputs.make_operands("f32", M, N, K, seed=41)
+    op2 = inputs.make_operands("f32", M, N, N, seed=43)
+    dev = torch.device("cuda:0")
+    A_half = (op1.A * 0.5).to(dev)
+    B1, B2 = op1.B.to(dev), op2.B.to(dev)
+    C1 = torch.full((M, N), float("nan"), device=dev)
+    C2 = torch.full((M, N), float("nan"), device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        A = A_half * 2.0                       # written on the side stream
+        for _ in range(3):                     # and again, so the first GEMM would race a late write
+            A.mul_(1.0)
+        assert lib.pgemm_gemm(M, N, K, 1.0, A, K, B1, N, 0.0, C1, N, "f32", 0, side) == 0
+        assert lib.pgemm_gemm(M, N, N, 1.0, C1, N, B2, N, 0.0, C2, N, "f32", 0, side) == 0
+    side.synchronize()
+    c1 = C1.cpu()
+    a, b1, _ = op1.numpy_views()
+    ref1 = oracle.gemm("f32", M, N, K, 1.0, a, b1)
+    assert np.max(np.abs(c1.double().numpy() - ref1)) <= TOL["f32"] * math.sqrt(K) * np.max(np.abs(ref1))
+    _, b2, _ = op2.numpy_views()
+    ref2 = oracle.gemm("f32", M, N, N, 1.0, c1.numpy(), b2)
+    g2 = C2.cpu().double().numpy()
+    assert np.max(np.abs(g2 - ref2)) <= TOL["f32"] * math.sqrt(N) * np.max(np.abs(ref2))
+
+
 # ------------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
