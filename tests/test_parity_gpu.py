@@ -385,6 +385,32 @@ def test_calls_on_a_side_stream_follow_stream_order(lib):
     assert np.max(np.abs(g2 - ref2)) <= TOL["f32"] * math.sqrt(N) * np.max(np.abs(ref2))
 
 
+def test_concurrent_calls_on_two_streams(lib):
+    """The library keeps no state between calls: GEMMs of different dtypes
+    and plans issued alternately on two streams (default priority) that run
+    concurrently each match the oracle."""
+    say("two streams")
+    dev = torch.device("cuda:0")
+    cases = [("bf16", 1024, 768, 1024), ("i8", 768, 1024, 512), ("f32", 512, 640, 384), ("f16", 640, 512, 700)]
+    ops = [inputs.make_operands(dt, M, N, K, seed=50 + i, alpha=(2 if dt == "i8" else 1.5),
+                                beta=(1 if dt == "i8" else 0.5)) for i, (dt, M, N, K) in enumerate(cases)]
+    bufs = [(o.A.to(dev), o.B.to(dev), o.C.to(dev)) for o in ops]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        for i, (o, (A, B, C)) in enumerate(zip(ops, bufs)):
+            s = streams[i % 2]
+            with torch.cuda.stream(s):
+                C.copy_(o.C.to(dev))  # the same C0 for every repetition, in stream order
+                r = lib.pgemm_gemm(o.M, o.N, o.K, o.alpha, A, o.lda, B, o.ldb, o.beta, C, o.ldc, o.dtype, 0, s)
+                assert r == 0, lib.pgemm_strerror(r)
+        for s in streams:
+            s.synchronize()
+        for o, (A, B, C) in zip(ops, bufs):
+            check(o, C.cpu())
+
+
 # ------------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
