@@ -411,6 +411,37 @@ def test_concurrent_calls_on_two_streams(lib):
             check(o, C.cpu())
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_k_around_whole_rings_of_k_tiles(lib, dtype):
+    """Prologue and drain at every compiled DIRECT tile class and ring depth
+    S: K = nK * BK - 1, nK * BK and nK * BK + 1 for nK in {1, S - 1, S, S + 1}
+    (page "Software pipelines and asynchronous copies", section "Prologue,
+    steady state, and epilogue": fewer K tiles than stages; page "GPU-Kernel
+    pipelinen", pitfalls: a forgotten epilogue tile and K tails).  One
+    workgroup's tile is cut in M and N as well (150 x 144 outputs)."""
+    classes = {}
+    for i in range(lib.pgemm_num_variants()):
+        v = lib.pgemm_variant_info(i)
+        if v["dtype"] == dtype and v["producer"] == "direct":
+            classes.setdefault((v["tile_m"], v["tile_n"], v["tile_k"]), []).append(v["stages"])
+    M, N = 150, 144
+    ran = 0
+    for tile, depths in sorted(classes.items()):
+        bk = tile[2]
+        for S in sorted(depths):
+            for nk in sorted({max(1, S - 1), S, S + 1, 1}):
+                for delta in (-1, 0, 1):
+                    K = nk * bk + delta
+                    if K < 1:
+                        continue
+                    say("ring edges", dtype, tile, "S", S, "K", K)
+                    op = inputs.make_operands(dtype, M, N, K, seed=7000 + K, alpha=1.0, beta=0.0)
+                    got = run_gpu(lib, op, stages=S, producer="direct", tile=tile)
+                    check(op, got)
+                    ran += 1
+    assert ran >= 60
+
+
 # ------------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
