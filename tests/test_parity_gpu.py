@@ -263,12 +263,24 @@ def test_k_slice_fingerprint_int8(lib, stages):
         check(op, got)
 
 
-def test_alpha_scaling_is_exact(lib):
-    op = inputs.make_operands("bf16", 256, 256, 512, seed=8, alpha=1.0, beta=0.0)
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_alpha_and_beta_scaling_are_exact(lib, dtype):
+    """Exact identities of the fused epilogue, on a shape that cuts tiles:
+    alpha = 2 gives twice the alpha = 1 output (a power of two scales
+    exactly), and C = A*B + 1*C1 with C1 = A*B gives 2*C1 (x + x = 2x
+    exactly), which also pins where old C is read from."""
+    say("alpha/beta identities", dtype)
+    op = inputs.make_operands(dtype, 300, 272, 520, seed=8, alpha=1.0, beta=0.0, ldc=280)
     c1 = run_gpu(lib, op, stages=2)
     op.alpha = 2.0
     c2 = run_gpu(lib, op, stages=2)
-    assert torch.equal(c2, 2.0 * c1)
+    assert torch.equal(c2[:, :272], c1[:, :272] * 2)
+    op.alpha, op.beta = 1.0, 1.0
+    op.C = c1.clone()
+    c3 = run_gpu(lib, op, stages=2)
+    assert torch.equal(c3[:, :272], c1[:, :272] * 2)
+    assert torch.equal(c3[:, 272:], c1[:, 272:]) if dtype == "i8" else torch.equal(
+        torch.isnan(c3[:, 272:]), torch.isnan(c1[:, 272:]))
 
 
 @pytest.mark.parametrize("alpha,beta", [(-2 ** 31, 2 ** 31 - 1), (2 ** 31 - 1, -2 ** 31), (-3, -2 ** 31)])
