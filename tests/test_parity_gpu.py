@@ -283,6 +283,35 @@ def test_alpha_and_beta_scaling_are_exact(lib, dtype):
         torch.isnan(c3[:, 272:]), torch.isnan(c1[:, 272:]))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_closed_forms_without_the_oracle(lib, dtype):
+    """Closed forms checked on the GPU directly: all-ones A and B give
+    C = alpha*K + beta*C0 rounded once to fp32 (alpha*K and the sums over K
+    are exact for these K); int8 A = B = -128 gives
+    16384*K and A = 1, B = -1 gives -K.  Shapes cut the output tiles and K
+    tiles; every ring depth of the planner's tile."""
+    M, N = 270, 260
+    for K in (1, 77, 640, 1029):
+        for stages in (1, 2, 3, 4):
+            say("closed form", dtype, K, "stages", stages)
+            alpha, beta = (3, -2) if dtype == "i8" else (0.5, 2.0)
+            op = inputs.make_operands(dtype, M, N, K, seed=K + stages, alpha=alpha, beta=beta)
+            op.A[:, :K] = 1
+            op.B[:, :N] = 1
+            got = run_gpu(lib, op, stages=stages)
+            # alpha*K and beta*C0 are exact, so is their sum in fp64; rounding it once to
+            # the output type is the fused epilogue's result
+            want = (alpha * K + beta * op.C[:, :N].to(torch.float64)).to(got.dtype)
+            assert torch.equal(got[:, :N], want), (K, stages)
+            if dtype == "i8":
+                for a, b, per_k in ((-128, -128, 16384), (1, -1, -1)):
+                    op = inputs.make_operands("i8", M, N, K, seed=K, alpha=1, beta=0)
+                    op.A[:, :K] = a
+                    op.B[:, :N] = b
+                    got = run_gpu(lib, op, stages=stages)
+                    assert bool((got[:, :N] == per_k * K).all()), (a, b, K, stages)
+
+
 @pytest.mark.parametrize("alpha,beta", [(-2 ** 31, 2 ** 31 - 1), (2 ** 31 - 1, -2 ** 31), (-3, -2 ** 31)])
 def test_int8_scalars_at_the_ends_of_int32(lib, alpha, beta):
     """alpha and beta anywhere in int32: alpha*acc + beta*C0 wraps modulo
