@@ -425,7 +425,7 @@ def main():
                     help="untimed calls before the warm-up, for this long, so the clock has settled (0 = off)")
     ap.add_argument("--retune", action="store_true",
                     help="re-run the tile/depth search and write the planner's tables (--retune-out)")
-    ap.add_argument("--retune-out", default=os.path.join(ROOT, "gpurun_out", "planner_tables.json"))
+    ap.add_argument("--retune-out", default=os.path.join(os.getcwd(), "planner_tables.retuned.json"))
     ap.add_argument("--planner-check", action="store_true",
                     help="time every tile class on the check shapes against the planner's pick")
     ap.add_argument("--copy-calibration", action="store_true",
