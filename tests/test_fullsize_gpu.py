@@ -91,3 +91,34 @@ def test_every_timed_launch_matches_the_oracle_at_full_size(lib, name):
             assert pad_same, "%s: columns past N were written" % p["key"]
     del A, B, C, C0, ref_d
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,M,N,K", [
+    ("bf16", 8192, 8192, 1024),   # 1024 tiles of 256 x 256: four workgroups in turn on every CU
+    ("i8", 8192, 8192, 1024),
+    ("f32", 8192, 8192, 64),      # short K, the planner's co-resident small tiles
+    ("f16", 1024, 8192, 4096),    # a wide, short output
+])
+def test_planner_check_shapes_beyond_the_workloads(lib, dtype, M, N, K):
+    """Shapes of the planner check that are larger than the benchmark's
+    workloads (several rounds of workgroups per CU), with the planner's own
+    plan, against the oracle over all M x N outputs."""
+    from software_pipelined_tiled_loop_amd import inputs
+    say("beyond", dtype, (M, N, K))
+    op = inputs.make_operands(dtype, M, N, K, seed=inputs.seed_for("bf16_k_sweep", 60 + K % 37))
+    ref = oracle_result(op)
+    dev = torch.device("cuda:0")
+    A, B, C = op.A.to(dev), op.B.to(dev), op.C.to(dev)
+    r = lib.pgemm_gemm(M, N, K, op.alpha, A, op.lda, B, op.ldb, op.beta, C, op.ldc, dtype, 0)
+    assert r == 0, lib.pgemm_strerror(r)
+    torch.cuda.synchronize()
+    ref_d = torch.from_numpy(ref).to(dev)
+    if dtype == "i8":
+        assert int((C != ref_d).sum().item()) == 0
+    else:
+        assert bool(torch.isfinite(C).all().item())
+        err = float((C.double() - ref_d).abs().max().item())
+        bound = TOL[dtype] * math.sqrt(K) * float(np.max(np.abs(ref)))
+        assert err <= bound, (err, bound)
+    del A, B, C, ref_d
+    torch.cuda.empty_cache()
